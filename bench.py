@@ -1,0 +1,300 @@
+"""Benchmark of the FP8 (E4M3) 128x128 block-scaled decode GEMM on one MI355X.
+
+One step = one fused-cast GEMM Y = X . W^T (bf16 X cast per row per 128
+columns inside the kernel, E4M3 weights with fp32 128x128 block scales,
+bf16 Y) on device-resident inputs. The default workload is the square
+projection M=8, K=N=5120. Weight quantization is a one-off per weight and
+is not part of a step.
+
+Every timed GEMM reads weights that are not in any cache: the steps cycle
+through a pool of distinct quantized weights of at least --pool-gib GiB,
+larger than the 256 MB Infinity Cache. The steps are captured once in a HIP
+graph and the graph is replayed (the decode-step launch pattern); the eager
+per-call time is reported beside it.
+
+Prints one JSON line (see the fields at the end of main()).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "µs/GEMM and achieved HBM GB/s (% of 8 TB/s) at M=8, K=5120 FP8 block-scaled"
+HBM_PEAK_GBPS = 8000.0
+FP8_DENSE_PEAK_TFLOPS = 5000.0
+
+WORKLOAD_DESCR = {
+    "square": "square projection, K=N=5120, e4m3 weights with 128x128 fp32 block scales, "
+              "bf16 activations cast per row per 128 columns inside the GEMM",
+    "mlp_up": "MLP up/gate projection, K=5120, N=34816",
+    "mlp_down": "MLP down projection, K=17408, N=5120",
+    "vocab": "vocabulary output layer, K=5120, N=248320",
+    "tiny": "tiny reference, K=1024, N=512",
+}
+
+
+def kernel_source_hash() -> str:
+    """Hash of the HIP sources, to tell whether stored counter results still
+    describe the current kernels."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "fp8_block_scaled_fp8bs_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".h", ".hip")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode())
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str, m: int) -> dict | None:
+    """HBM traffic per launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"gemm_{workload}_m{m}_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    try:
+        return {"bytes_per_launch": float(vals["hbm_bytes_per_launch"]),
+                "fetch_bytes": float(vals["fetch_bytes_per_launch"]),
+                "write_bytes": float(vals["write_bytes_per_launch"])}
+    except KeyError:
+        return None
+
+
+def cpu_baseline(workload, m: int, budget_s: float) -> dict:
+    """Time the CPU oracle (cast + fp64 GEMM) on the same workload."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    w_bits = workload.weight()
+    x_bits = workload.act(m)
+    wq, ws = oracle.quantize_weight_ref(w_bits)     # one-off, not timed (as on the GPU)
+    oracle.gemm_fused_ref(x_bits, wq, ws)           # warm-up
+    times = []
+    t_end = time.perf_counter() + budget_s
+    while len(times) < 3 or (time.perf_counter() < t_end and len(times) < 1000):
+        t0 = time.perf_counter()
+        oracle.gemm_fused_ref(x_bits, wq, ws)
+        times.append(time.perf_counter() - t0)
+    med = float(np.median(times))
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {
+        "value": workload.algorithmic_bytes(m) / med / 1e9,
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{len(times)} full oracle GEMMs (per-row cast + fp64 block GEMM) of the "
+                  f"timed workload, median {med * 1e3:.1f} ms each; host {platform.processor() or platform.machine()}, "
+                  f"{len(os.sched_getaffinity(0))} cores visible",
+        "us_per_gemm": med * 1e6,
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--workload", default="square", choices=sorted(WORKLOAD_DESCR))
+    ap.add_argument("--m", type=int, default=8)
+    ap.add_argument("--pool-gib", type=float, default=1.0)
+    ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--eager-only", action="store_true", help="time stream launches only")
+    ap.add_argument("--diag-copy-mib", type=int, default=0,
+                    help="run only the plain copy kernel over this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import fp8_block_scaled_fp8bs_amd as fp8bs
+    from workloads import WORKLOADS
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    fp8bs.load()
+
+    if args.diag_copy_mib:
+        nbytes = args.diag_copy_mib << 20
+        src = torch.randint(0, 255, (nbytes,), dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            fp8bs.diag_copy(src, dst)
+        torch.cuda.synchronize()
+        assert torch.equal(src, dst)
+        print(json.dumps({"diag_copy_bytes": nbytes, "launches": 5}))
+        return 0
+
+    wl = WORKLOADS[args.workload]
+    m, n, k = args.m, wl.n, wl.k
+    if m not in range(1, 33):
+        print("--m must be in 1..32", file=sys.stderr)
+        return 2
+    alg_bytes = wl.algorithmic_bytes(m)
+    floor_us = alg_bytes / (HBM_PEAK_GBPS * 1e3)
+    print(f"# workload {args.workload} m={m} n={n} k={k}: {alg_bytes} algorithmic bytes, "
+          f"floor {floor_us:.2f} us at 8 TB/s, 80% target {floor_us / 0.8:.2f} us", file=sys.stderr, flush=True)
+
+    # --- inputs, resident on the device before timing ---------------------
+    w_bits, x_bits = wl.weight(), wl.act(m)
+    w0 = torch.from_numpy(w_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    x = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    code_bytes = n * k
+    pool_n = max(1, math.ceil(args.pool_gib * (1 << 30) / code_bytes))
+    pool = [fp8bs.quantize_weight(w0)]
+    del w0
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1400)
+    for _ in range(pool_n - 1):
+        wi = (torch.randn((n, k), generator=gen, device=dev, dtype=torch.float32) * 0.02).to(torch.bfloat16)
+        pool.append(fp8bs.quantize_weight(wi))
+        del wi
+    torch.cuda.synchronize()
+    cfg = fp8bs.select_config(m, n, k)
+    ws_bytes = fp8bs.workspace_bytes(m, n, k)
+    workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    print(f"# pool {pool_n} weights ({pool_n * code_bytes / 2**30:.2f} GiB), config {cfg}",
+          file=sys.stderr, flush=True)
+
+    def step(i):
+        wq, wsc = pool[i % pool_n]
+        fp8bs.gemm(x, wq, wsc, out=y, workspace=workspace)
+
+    launches0 = fp8bs.launch_count("gemm_mfma") + fp8bs.launch_count("gemm_dot")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # --- eager: stream launches --------------------------------------------
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    eager_ms = e0.elapsed_time(e1) / args.steps
+
+    # --- graph: the same K steps captured once and replayed ------------------
+    graph_ms = None
+    if not args.eager_only:
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                for i in range(args.steps):
+                    step(i)
+        stream.wait_stream(cap)
+        g.replay()  # warm replay
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        g.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = g0.elapsed_time(g1) / args.steps
+
+    launches = fp8bs.launch_count("gemm_mfma") + fp8bs.launch_count("gemm_dot") - launches0
+    expected = args.warmup + args.steps * (1 if args.eager_only else 2)
+    if launches != expected:
+        print(f"kernel launch count {launches} != expected {expected}", file=sys.stderr)
+        return 1
+    maps = fp8bs.hip_runtime_mappings()
+    if len(maps["libamdhip64"]) != 1 or len(maps["libfp8bs"]) != 1:
+        print(f"unexpected runtime mappings: {maps}", file=sys.stderr)
+        return 1
+
+    # --- streaming-read ceiling over the same byte count ---------------------
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    for i in range(min(pool_n, 8)):
+        fp8bs.diag_read(pool[i][0], sink)
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    r0.record(stream)
+    reps = max(args.steps // 2, 1)
+    for i in range(reps):
+        fp8bs.diag_read(pool[i % pool_n][0], sink)
+    r1.record(stream)
+    torch.cuda.synchronize()
+    read_us = r0.elapsed_time(r1) * 1e3 / reps
+    read_gbps = code_bytes / (read_us * 1e3)
+
+    step_ms = graph_ms if graph_ms is not None else eager_ms
+    us = step_ms * 1e3
+    gbps = alg_bytes / (us * 1e3)
+    traffic = stored_traffic(args.workload, m)
+    roofline = {
+        "bound": "hbm",
+        "achieved": round(gbps, 1),
+        "peak": HBM_PEAK_GBPS,
+        "unit": "GB/s",
+        "frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "traffic": round(traffic["bytes_per_launch"]) if traffic else None,
+    }
+    cpu = None if args.no_cpu else cpu_baseline(wl, m, args.cpu_budget_s)
+    out = {
+        "metric": METRIC,
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{args.workload}: {WORKLOAD_DESCR[args.workload]}; M={m}",
+            "m": m, "n": n, "k": k,
+            "algorithmic_bytes": alg_bytes,
+            "weight_pool": pool_n,
+            "kernel": {"path": "mfma" if cfg.path == 1 else "dot", "tiles_n": cfg.tiles_n,
+                       "waves_n": cfg.waves_n, "waves_k": cfg.waves_k, "depth": cfg.depth,
+                       "split_k": cfg.split_k},
+            "timing": "hip graph of the steps, replayed" if graph_ms is not None else "stream launches",
+        },
+        "us_per_gemm": round(us, 3),
+        "pct_of_8TBps": round(100 * gbps / HBM_PEAK_GBPS, 2),
+        "eager_us_per_gemm": round(eager_ms * 1e3, 3),
+        "stream_read_ceiling_GBps": round(read_gbps, 1),
+        "mfma_flops_frac": round(2 * m * n * k / (us * 1e-6) / (FP8_DENSE_PEAK_TFLOPS * 1e12), 6),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,275 @@
+"""Python binding of libfp8bs: the FP8 (E4M3) 128x128 block-scaled decode GEMM
+for MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libfp8bs.so, reached through its C ABI (include/fp8bs.h) with
+ctypes. PyTorch provides device memory and the stream. If the library is not
+built, or a call returns a non-OK status, a Python exception is raised;
+there is no other implementation to fall back to.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch  # loaded first so that libfp8bs binds to the HIP runtime torch uses
+
+__all__ = [
+    "Fp8bsError", "GemmConfig", "load", "library_path",
+    "quantize_weight", "quantize_act", "gemm", "gemm_q", "gemm_ex",
+    "workspace_bytes", "config_workspace_bytes", "select_config",
+    "encode_e4m3", "launch_count", "build_info", "diag_read", "diag_copy",
+    "hip_runtime_mappings", "PATH_MFMA", "PATH_DOT", "REDUCE_KERNEL",
+    "REDUCE_LAST_ARRIVER", "COUNTER",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libfp8bs.so")
+_LIB = None
+
+PATH_AUTO, PATH_MFMA, PATH_DOT = 0, 1, 2
+REDUCE_KERNEL, REDUCE_LAST_ARRIVER = 0, 1
+COUNTER = {"quant_weight": 0, "quant_act": 1, "gemm_mfma": 2, "gemm_dot": 3,
+           "split_reduce": 4, "encode": 5, "diag": 6}
+
+
+class Fp8bsError(RuntimeError):
+    """A libfp8bs call returned a non-OK status."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+class _Config(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int32) for name in
+                ("path", "tiles_n", "waves_n", "waves_k", "depth", "split_k", "reduce",
+                 "reserved")]
+
+
+@dataclass(frozen=True)
+class GemmConfig:
+    """Mirror of fp8bs_gemm_config (see include/fp8bs.h)."""
+    path: int
+    tiles_n: int
+    waves_n: int
+    waves_k: int
+    depth: int
+    split_k: int = 1
+    reduce: int = REDUCE_KERNEL
+
+    def _c(self) -> _Config:
+        return _Config(self.path, self.tiles_n, self.waves_n, self.waves_k, self.depth,
+                       self.split_k, self.reduce, 0)
+
+    @staticmethod
+    def _from_c(c: _Config) -> "GemmConfig":
+        return GemmConfig(c.path, c.tiles_n, c.waves_n, c.waves_k, c.depth, c.split_k, c.reduce)
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load() -> ctypes.CDLL:
+    """Load libfp8bs.so (built in-tree); raises if it is missing."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is not built; run __graft_entry__.build() "
+                           "(hipcc for gfx950) first")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    sig = {
+        "fp8bs_quantize_weight": (i32, [vp, i64, i64, vp, vp, vp]),
+        "fp8bs_quantize_act": (i32, [vp, i64, i64, vp, vp, vp]),
+        "fp8bs_gemm": (i32, [vp, i64, vp, vp, i64, i64, vp, vp, sz, vp]),
+        "fp8bs_gemm_q": (i32, [vp, vp, i64, vp, vp, i64, i64, vp, vp, sz, vp]),
+        "fp8bs_gemm_workspace_bytes": (sz, [i64, i64, i64]),
+        "fp8bs_gemm_select_config": (i32, [i64, i64, i64, ctypes.POINTER(_Config)]),
+        "fp8bs_gemm_config_workspace_bytes": (sz, [ctypes.POINTER(_Config), i64, i64, i64]),
+        "fp8bs_gemm_ex": (i32, [vp, vp, vp, i64, vp, vp, i64, i64, vp, vp, sz,
+                                ctypes.POINTER(_Config), vp]),
+        "fp8bs_encode_e4m3": (i32, [vp, i64, vp, i32, vp]),
+        "fp8bs_status_string": (ctypes.c_char_p, [i32]),
+        "fp8bs_launch_count": (ctypes.c_uint64, [i32]),
+        "fp8bs_build_info": (ctypes.c_char_p, []),
+        "fp8bs_diag_read": (i32, [vp, sz, vp, vp]),
+        "fp8bs_diag_copy": (i32, [vp, vp, sz, vp]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _LIB = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        msg = load().fp8bs_status_string(status).decode()
+        raise Fp8bsError(status, msg)
+
+
+def _stream(stream=None) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _dev(t: torch.Tensor, dtype: torch.dtype, name: str, ndim: int) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if t.dim() != ndim or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {ndim}-d tensor")
+    return t.data_ptr()
+
+
+def quantize_weight(w: torch.Tensor, out=None, stream=None):
+    """bf16 W[n][k] -> (E4M3 codes uint8 [n][k], fp32 scales [n/128][k/128])."""
+    n, k = w.shape
+    q, s = out if out is not None else (
+        torch.empty((n, k), dtype=torch.uint8, device=w.device),
+        torch.empty((n // 128, k // 128), dtype=torch.float32, device=w.device))
+    _check(load().fp8bs_quantize_weight(_dev(w, torch.bfloat16, "w", 2), n, k,
+                                        _dev(q, torch.uint8, "w_fp8", 2),
+                                        _dev(s, torch.float32, "w_scale", 2), _stream(stream)))
+    return q, s
+
+
+def quantize_act(x: torch.Tensor, out=None, stream=None):
+    """bf16 X[m][k] -> (E4M3 codes uint8 [m][k], fp32 scales [m][k/128])."""
+    m, k = x.shape
+    q, s = out if out is not None else (
+        torch.empty((m, k), dtype=torch.uint8, device=x.device),
+        torch.empty((m, k // 128), dtype=torch.float32, device=x.device))
+    _check(load().fp8bs_quantize_act(_dev(x, torch.bfloat16, "x", 2), m, k,
+                                     _dev(q, torch.uint8, "x_fp8", 2),
+                                     _dev(s, torch.float32, "x_scale", 2), _stream(stream)))
+    return q, s
+
+
+def workspace_bytes(m: int, n: int, k: int) -> int:
+    return int(load().fp8bs_gemm_workspace_bytes(m, n, k))
+
+
+def config_workspace_bytes(cfg: GemmConfig, m: int, n: int, k: int) -> int:
+    c = cfg._c()
+    return int(load().fp8bs_gemm_config_workspace_bytes(ctypes.byref(c), m, n, k))
+
+
+def select_config(m: int, n: int, k: int) -> GemmConfig:
+    c = _Config()
+    _check(load().fp8bs_gemm_select_config(m, n, k, ctypes.byref(c)))
+    return GemmConfig._from_c(c)
+
+
+def _out_ws(m, n, device, out, workspace, need):
+    y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=device)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    return y, ws_ptr, ws_len
+
+
+def gemm(x: torch.Tensor, w_q: torch.Tensor, w_s: torch.Tensor, out=None, workspace=None,
+         stream=None) -> torch.Tensor:
+    """Y[m][n] (bf16) = X[m][k] . W^T with the per-row 1x128 FP8 cast fused in."""
+    m, k = x.shape
+    n = w_q.shape[0]
+    y, ws, wl = _out_ws(m, n, x.device, out, workspace, workspace_bytes(m, n, k))
+    _check(load().fp8bs_gemm(_dev(x, torch.bfloat16, "x", 2), m,
+                             _dev(w_q, torch.uint8, "w_fp8", 2), _dev(w_s, torch.float32, "w_scale", 2),
+                             n, k, _dev(y, torch.bfloat16, "y", 2), ws, wl, _stream(stream)))
+    return y
+
+
+def gemm_q(x_q: torch.Tensor, x_s: torch.Tensor, w_q: torch.Tensor, w_s: torch.Tensor,
+           out=None, workspace=None, stream=None) -> torch.Tensor:
+    """Same product from pre-quantized activations (codes and scales)."""
+    m, k = x_q.shape
+    n = w_q.shape[0]
+    y, ws, wl = _out_ws(m, n, x_q.device, out, workspace, workspace_bytes(m, n, k))
+    _check(load().fp8bs_gemm_q(_dev(x_q, torch.uint8, "x_fp8", 2), _dev(x_s, torch.float32, "x_scale", 2),
+                               m, _dev(w_q, torch.uint8, "w_fp8", 2),
+                               _dev(w_s, torch.float32, "w_scale", 2), n, k,
+                               _dev(y, torch.bfloat16, "y", 2), ws, wl, _stream(stream)))
+    return y
+
+
+def gemm_ex(cfg: GemmConfig, w_q: torch.Tensor, w_s: torch.Tensor, x: torch.Tensor | None = None,
+            x_q: torch.Tensor | None = None, x_s: torch.Tensor | None = None, out=None,
+            workspace=None, stream=None) -> torch.Tensor:
+    """GEMM with an explicit kernel configuration; x (bf16, fused cast) or
+    x_q/x_s (pre-quantized)."""
+    if x is not None:
+        m, k = x.shape
+        xp, xqp, xsp = _dev(x, torch.bfloat16, "x", 2), None, None
+        device = x.device
+    else:
+        m, k = x_q.shape
+        xp = None
+        xqp, xsp = _dev(x_q, torch.uint8, "x_fp8", 2), _dev(x_s, torch.float32, "x_scale", 2)
+        device = x_q.device
+    n = w_q.shape[0]
+    y, ws, wl = _out_ws(m, n, device, out, workspace, config_workspace_bytes(cfg, m, n, k))
+    c = cfg._c()
+    _check(load().fp8bs_gemm_ex(xp, xqp, xsp, m, _dev(w_q, torch.uint8, "w_fp8", 2),
+                                _dev(w_s, torch.float32, "w_scale", 2), n, k,
+                                _dev(y, torch.bfloat16, "y", 2), ws, wl, ctypes.byref(c),
+                                _stream(stream)))
+    return y
+
+
+def encode_e4m3(v: torch.Tensor, mode: int = 0, out=None, stream=None) -> torch.Tensor:
+    """fp32 values -> E4M3 codes (mode 0: quantizers' encoder, 1: hardware, 2: software)."""
+    v = v.reshape(-1)
+    o = out if out is not None else torch.empty(v.numel(), dtype=torch.uint8, device=v.device)
+    _check(load().fp8bs_encode_e4m3(_dev(v, torch.float32, "in", 1), v.numel(),
+                                    _dev(o, torch.uint8, "out", 1), mode, _stream(stream)))
+    return o
+
+
+def launch_count(which: str | int) -> int:
+    idx = COUNTER[which] if isinstance(which, str) else int(which)
+    return int(load().fp8bs_launch_count(idx))
+
+
+def build_info() -> str:
+    return load().fp8bs_build_info().decode()
+
+
+def diag_read(t: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    nbytes = t.numel() * t.element_size()
+    _check(load().fp8bs_diag_read(t.data_ptr(), nbytes, sink.data_ptr(), _stream(stream)))
+
+
+def diag_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("dst too small")
+    _check(load().fp8bs_diag_copy(src.data_ptr(), dst.data_ptr(), nbytes, _stream(stream)))
+
+
+def hip_runtime_mappings() -> dict:
+    """Which HIP runtime files and which libfp8bs are mapped into this process
+    (read from /proc/self/maps): a check that exactly one runtime is in use."""
+    hip, ours = set(), set()
+    with open("/proc/self/maps") as f:
+        for line in f:
+            parts = line.split()
+            if len(parts) >= 6:
+                path = parts[5]
+                base = os.path.basename(path)
+                if base.startswith("libamdhip64"):
+                    hip.add(os.path.realpath(path))
+                elif base == "libfp8bs.so":
+                    ours.add(os.path.realpath(path))
+    return {"libamdhip64": sorted(hip), "libfp8bs": sorted(ours)}

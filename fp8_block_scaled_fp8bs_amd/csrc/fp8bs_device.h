@@ -1,0 +1,188 @@
+// Device helpers shared by every kernel of the library (gfx950 only).
+//
+// The quantization rule implemented here: per block, scale = fl32(amax/448)
+// and code = RNE_e4m3(fl32(x/scale)), with the E4M3 variant whose largest
+// finite value is 448 ("Kernel-Level Optimisations for LLM Inference and
+// Training", section "Quantisation kernels"), one scale per 128x128 weight
+// block ("The profiler said the kernel ran zero times", section "The output
+// layer, which did run") and one per row per 128 columns for activations.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8bs {
+
+constexpr int BLK = 128;          // block edge along K (and along N for weights)
+constexpr int ACT_STRIDE = 144;   // LDS bytes per staged activation block row (128 + 16 pad)
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- bf16 ---
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16, round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return bf16_rne(a) | (bf16_rne(b) << 16);
+}
+
+// ---------------------------------------------------------------- E4M3 ---
+
+// Integer software encoder: nearest E4M3 value, ties to even mantissa,
+// magnitudes >= 448 saturate, the sign bit is copied.
+__device__ __forceinline__ uint32_t e4m3_encode_sw(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  if (a >= 0x43E00000u) return sign | 0x7Eu;              // |v| >= 448
+  if (a >= 0x3C800000u) {                                 // |v| >= 2^-6: normal E4M3
+    // round the fp32 pattern to 3 fraction bits (bit 20 is the kept LSB)
+    const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
+    const uint32_t code = ((r >> 23) - 120u) << 3 | ((r >> 20) & 7u);
+    return sign | (code > 0x7Eu ? 0x7Eu : code);
+  }
+  // subnormal E4M3 grid: multiples of 2^-9; |v| * 512 is exact and < 8
+  const float t = __builtin_rintf(__uint_as_float(a) * 512.0f);
+  return sign | (uint32_t)t;                              // t == 8 gives 0x08 = 2^-6
+}
+
+// Hardware conversion (v_cvt_pk_fp8_f32, OCP E4M3 on gfx950) of four values.
+__device__ __forceinline__ uint32_t e4m3x4_hw(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
+__device__ __forceinline__ uint32_t e4m3x4_sw(float a, float b, float c, float d) {
+  return e4m3_encode_sw(a) | e4m3_encode_sw(b) << 8 | e4m3_encode_sw(c) << 16 |
+         e4m3_encode_sw(d) << 24;
+}
+
+#ifndef FP8BS_ENCODER_SW
+#define FP8BS_ENCODER_SW 0
+#endif
+
+// The encoder every quantizer uses.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+#if FP8BS_ENCODER_SW
+  return e4m3x4_sw(a, b, c, d);
+#else
+  return e4m3x4_hw(a, b, c, d);
+#endif
+}
+
+// Decode the four codes of w (K order: byte 0 first) to fp32.
+__device__ __forceinline__ void e4m3x4_decode(uint32_t w, float* out) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  out[0] = lo.x;
+  out[1] = lo.y;
+  out[2] = hi.x;
+  out[3] = hi.y;
+}
+
+// ----------------------------------------------------------- quotients ---
+
+// Below this block amax the fast quotient's exactness argument (all
+// intermediates normal, remainder exact) is not made; use IEEE division.
+constexpr float FAST_QUOTIENT_MIN_AMAX = 0x1p-60f;
+
+// Replace x[i] by fl32(x[i] / s) for a block with largest magnitude `amax`
+// and scale s = fl32(amax / 448). For amax >= 2^-60 the quotient comes from
+// the correctly rounded reciprocal r = fl32(1/s): q0 = fl32(x r), then one
+// correction with the exact remainder e = x - s q0 (a fused multiply-add):
+// q = fl32(q0 + e r). For bf16 x and bf16 amax this equals the correctly
+// rounded quotient (checked exhaustively over all mantissa pairs and
+// exponent gaps; the result is scale invariant while every intermediate is
+// normal, which amax >= 2^-60 guarantees for every x whose code is not 0).
+// The sign is copied from x so that a zero keeps its sign. An all-zero block
+// (amax == 0) leaves x unchanged (signed zeros, codes 0x00 / 0x80).
+template <int N>
+__device__ __forceinline__ void block_quotients(float (&x)[N], float amax, float s) {
+  if (amax >= FAST_QUOTIENT_MIN_AMAX) {
+    const float r = 1.0f / s;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const float q0 = x[i] * r;
+      const float e = __builtin_fmaf(-s, q0, x[i]);
+      const float q = __builtin_fmaf(e, r, q0);
+      x[i] = __builtin_copysignf(q, x[i]);
+    }
+  } else if (amax > 0.0f) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] = x[i] / s;
+  }
+}
+
+// --------------------------------------------------------- lane shuffles ---
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int DPP_QUAD_XOR1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int DPP_QUAD_XOR2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;
+
+__device__ __forceinline__ float quad_max(float v) {
+  v = __builtin_fmaxf(v, dpp_f<DPP_QUAD_XOR1>(v));
+  v = __builtin_fmaxf(v, dpp_f<DPP_QUAD_XOR2>(v));
+  return v;
+}
+
+// Sum over the 8 lanes of each aligned group of 8; every lane gets the same
+// bits (each step adds a pair in an order-independent way).
+__device__ __forceinline__ float octet_sum(float v) {
+  v = v + dpp_f<DPP_QUAD_XOR1>(v);
+  v = v + dpp_f<DPP_QUAD_XOR2>(v);
+  v = v + dpp_f<DPP_ROW_HALF_MIRROR>(v);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = __builtin_fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// -------------------------------------------------- activation block cast ---
+
+// Cast one quarter (32 values) of a 1x128 activation block. The four
+// quarters of a block must sit in the four lanes of one DPP quad, quarter q
+// in lane q of the quad; the block amax is reduced across the quad.
+// xw: 16 dwords = 32 bf16 in K order. codes: 8 dwords = 32 codes in K order.
+// Returns the block scale fl32(amax / 448) (identical in the four lanes).
+__device__ __forceinline__ float cast_quarter(const uint4 (&xw)[4], uint32_t (&codes)[8]) {
+  float x[32];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w[4] = {xw[i].x, xw[i].y, xw[i].z, xw[i].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[8 * i + 2 * j] = bf16_lo(w[j]);
+      x[8 * i + 2 * j + 1] = bf16_hi(w[j]);
+    }
+  }
+  float am = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) am = __builtin_fmaxf(am, __builtin_fabsf(x[i]));
+  am = quad_max(am);
+  const float s = am / 448.0f;
+  block_quotients(x, am, s);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) codes[i] = e4m3x4(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
+  return s;
+}
+
+}  // namespace fp8bs

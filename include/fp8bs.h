@@ -1,0 +1,205 @@
+/*
+ * fp8bs.h -- C ABI of the FP8 (E4M3) 128x128 block-scaled decode GEMM for
+ * AMD MI355X (gfx950).
+ *
+ * The operation, as the pages state it:
+ *   - weights are converted once to FP8 E4M3 with one fp32 scale per
+ *     128 x 128 block ("The profiler said the kernel ran zero times",
+ *     section "The output layer, which did run"; "A 23% faster GPU kernel,
+ *     and a model that did not move", section "Why this shape is hard");
+ *   - the multiply's inputs are cast to FP8 on every call ("The profiler said
+ *     the kernel ran zero times", section "What the trace showed"); the
+ *     activation scale granularity is not given on the pages and is taken
+ *     here as one scale per row per 128 columns, aligned with the weight's
+ *     K blocks;
+ *   - the long K dimension is split across compute units and the partial
+ *     results are reduced in a fixed order ("A 23% faster GPU kernel...",
+ *     section "Why this shape is hard");
+ *   - the shapes are decode shapes: a handful of activation rows (about
+ *     eight), where the multiply is bound by reading the weights ("A 23%
+ *     faster GPU kernel...", section "Why this shape is hard";
+ *     "Kernel-Level Optimisations for LLM Inference and Training", section
+ *     "Start with the bound: memory or compute").
+ *
+ * FP8 format: E4M3 with largest finite value 448 (exponent bias 7,
+ * subnormals, no infinities, NaN only at 0x7F / 0xFF) -- "Kernel-Level
+ * Optimisations...", section "Quantisation kernels".
+ *
+ * Quantization rule (weights and activations alike): for each block,
+ *   amax  = max |x| over the block,
+ *   scale = fl32(amax / 448)                      (IEEE fp32 division),
+ *   code  = RNE_e4m3(fl32(x / scale))             (ties to even mantissa,
+ *           saturating at +-448, sign of zero kept);
+ * an all-zero block has scale 0 and codes 0x00 / 0x80 (sign of each zero).
+ * Dequantized value = decode(code) * scale.
+ *
+ * GEMM: Y[m][n] = sum over K blocks kb of
+ *         (sum_{k in kb} dec(xq[m][k]) * dec(wq[n][k])) * xs[m][kb] * ws[n/128][kb]
+ * accumulated in fp32 and rounded once to bf16 (round to nearest even).
+ *
+ * Conventions for every call:
+ *   - Tensor pointers are DEVICE pointers, row-major, owned by the caller.
+ *     The library never allocates, frees or synchronizes.
+ *   - `stream` is a hipStream_t (NULL = the null stream); calls are
+ *     asynchronous on it.
+ *   - Arguments are checked before anything is launched. On any non-OK
+ *     status nothing has been launched and no memory has been touched.
+ *     Checks, in order: NULL pointers, shapes, alignment, workspace size,
+ *     device (must be gfx950). A failed launch returns FP8BS_ERR_LAUNCH;
+ *     faults inside a kernel surface at the caller's next synchronization.
+ *   - There is no fallback: an unsupported shape is an error, never a
+ *     silently slower path.
+ *   - Determinism: the same inputs, shape, device and library build give
+ *     bit-identical outputs. The GEMM uses no floating-point atomics.
+ *   - Shapes: n and k must be multiples of 128 (whole blocks); m may be any
+ *     value >= 0 for the quantizers and 0..32 for the GEMM. A zero extent
+ *     is a no-op (k == 0 in the GEMM writes zeros: the empty sum).
+ *   - Alignment: bf16 and code pointers 16-byte aligned; scale pointers
+ *     4-byte aligned; workspace 16-byte aligned.
+ */
+#ifndef FP8BS_H
+#define FP8BS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FP8BS_OK = 0,
+  FP8BS_ERR_NULL = 1,      /* a required pointer is NULL */
+  FP8BS_ERR_SHAPE = 2,     /* n or k not a multiple of 128, m out of range, negative extent */
+  FP8BS_ERR_ALIGN = 3,     /* a pointer is not aligned as documented above */
+  FP8BS_ERR_WORKSPACE = 4, /* workspace smaller than fp8bs_gemm_workspace_bytes(...) */
+  FP8BS_ERR_DEVICE = 5,    /* no current HIP device, or it is not gfx950 */
+  FP8BS_ERR_LAUNCH = 6,    /* the kernel launch itself failed */
+  FP8BS_ERR_CONFIG = 7     /* an explicit kernel configuration is invalid for this shape */
+} fp8bs_status;
+
+/* Weight quantization, one scale per 128x128 block (done once per weight).
+ *   w_bf16  [n][k] bf16, in
+ *   w_fp8   [n][k] E4M3 codes, out
+ *   w_scale [n/128][k/128] fp32, out                                        */
+fp8bs_status fp8bs_quantize_weight(const void* w_bf16, int64_t n, int64_t k,
+                                   uint8_t* w_fp8, float* w_scale, void* stream);
+
+/* Activation quantization, one scale per row per 128 columns: the same rule
+ * the GEMM applies internally on every call (fp8bs_gemm fuses it).
+ *   x_bf16  [m][k] bf16, in
+ *   x_fp8   [m][k] E4M3 codes, out
+ *   x_scale [m][k/128] fp32, out                                            */
+fp8bs_status fp8bs_quantize_act(const void* x_bf16, int64_t m, int64_t k,
+                                uint8_t* x_fp8, float* x_scale, void* stream);
+
+/* Y = X . W^T with the activation cast fused in; 0 <= m <= 32.
+ *   x_bf16  [m][k] bf16; w_fp8 [n][k] codes; w_scale [n/128][k/128] fp32;
+ *   y_bf16  [m][n] bf16, out.
+ *   workspace: device scratch of at least fp8bs_gemm_workspace_bytes(m,n,k)
+ *   bytes (may be NULL when that is 0). Its contents need no initialization
+ *   and are garbage afterwards. Calls that share a workspace must be ordered
+ *   on one stream.                                                          */
+fp8bs_status fp8bs_gemm(const void* x_bf16, int64_t m,
+                        const uint8_t* w_fp8, const float* w_scale, int64_t n, int64_t k,
+                        void* y_bf16, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/* Same product from already-quantized activations (codes [m][k] and scales
+ * [m][k/128] as produced by fp8bs_quantize_act). With the same shape it runs
+ * the same kernel configuration as fp8bs_gemm, so
+ * fp8bs_gemm(x) == fp8bs_gemm_q(fp8bs_quantize_act(x)) bit for bit.        */
+fp8bs_status fp8bs_gemm_q(const uint8_t* x_fp8, const float* x_scale, int64_t m,
+                          const uint8_t* w_fp8, const float* w_scale, int64_t n, int64_t k,
+                          void* y_bf16, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* Workspace bytes the automatically selected configuration needs (0 when
+ * the K dimension is not split across workgroups). Returns 0 for shapes
+ * fp8bs_gemm would reject.                                                  */
+size_t fp8bs_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k);
+
+/* ---- explicit kernel configuration (tuning and tests) ------------------- */
+
+enum { FP8BS_PATH_AUTO = 0, FP8BS_PATH_MFMA = 1, FP8BS_PATH_DOT = 2 };
+enum { FP8BS_REDUCE_KERNEL = 0, FP8BS_REDUCE_LAST_ARRIVER = 1 };
+
+/* How one GEMM is laid out on the GPU.
+ *   path      MFMA (16x16x128 FP8 matrix instructions) or DOT (per-lane
+ *             fp32 dot products, for the smallest m)
+ *   tiles_n   MFMA: 16-row tiles per wave (1, 2, 4); DOT: 8-row groups per wave (1, 2, 4)
+ *   waves_n   waves side by side along N in one workgroup (1, 2, 4)
+ *   waves_k   waves splitting a workgroup's K range (1, 2, 4, 8); their
+ *             partials are summed in wave order inside the workgroup
+ *   depth     K blocks of weights each wave keeps in flight (1..8)
+ *   split_k   workgroups splitting K (1..64); their fp32 partials are summed
+ *             in split order, never with atomics on data
+ *   reduce    how split partials are combined when split_k > 1:
+ *             FP8BS_REDUCE_KERNEL = a second kernel sums them;
+ *             FP8BS_REDUCE_LAST_ARRIVER = the last workgroup of each output
+ *             tile to finish (found with one integer counter per tile) sums
+ *             them in split order in the same launch.                       */
+typedef struct {
+  int32_t path;
+  int32_t tiles_n;
+  int32_t waves_n;
+  int32_t waves_k;
+  int32_t depth;
+  int32_t split_k;
+  int32_t reduce;
+  int32_t reserved;
+} fp8bs_gemm_config;
+
+/* The configuration fp8bs_gemm uses for this shape (a fixed table: the same
+ * shape always gets the same configuration, hence the same bits).          */
+fp8bs_status fp8bs_gemm_select_config(int64_t m, int64_t n, int64_t k,
+                                      fp8bs_gemm_config* out);
+
+/* Workspace bytes a given configuration needs.                              */
+size_t fp8bs_gemm_config_workspace_bytes(const fp8bs_gemm_config* cfg,
+                                         int64_t m, int64_t n, int64_t k);
+
+/* fp8bs_gemm / fp8bs_gemm_q with an explicit configuration (cfg != NULL).
+ * x_bf16 != NULL selects the fused cast; otherwise x_fp8 and x_scale are
+ * used.                                                                     */
+fp8bs_status fp8bs_gemm_ex(const void* x_bf16, const uint8_t* x_fp8, const float* x_scale,
+                           int64_t m,
+                           const uint8_t* w_fp8, const float* w_scale, int64_t n, int64_t k,
+                           void* y_bf16, void* workspace, size_t workspace_bytes,
+                           const fp8bs_gemm_config* cfg, void* stream);
+
+/* ---- utilities ----------------------------------------------------------- */
+
+/* Encode fp32 values to E4M3 codes with the quantizers' rounding rule
+ * (nearest, ties to even mantissa, saturate at +-448, sign kept).
+ * mode 0 = the encoder the quantizers use; 1 = the hardware conversion
+ * instruction; 2 = the integer software encoder. in/out 4-byte aligned.     */
+fp8bs_status fp8bs_encode_e4m3(const float* in, int64_t count, uint8_t* out,
+                               int32_t mode, void* stream);
+
+/* Human-readable name of a status.                                          */
+const char* fp8bs_status_string(fp8bs_status s);
+
+/* Host-side count of launches of each kernel family since load: 0 = weight
+ * quantizer, 1 = activation quantizer, 2 = MFMA GEMM, 3 = DOT GEMM,
+ * 4 = split reduce, 5 = encoder utility, 6 = read/copy diagnostics.
+ * Lets a caller check that the kernels it benchmarks actually ran.          */
+uint64_t fp8bs_launch_count(int32_t which);
+
+/* Build identification string (compiler, target, flags).                    */
+const char* fp8bs_build_info(void);
+
+/* ---- diagnostics (bandwidth reference kernels) --------------------------- */
+
+/* Streaming read of `bytes` bytes (multiple of 16, 16-byte aligned) with a
+ * checksum written to sink[0..3] (uint32), so the reads are not elided.     */
+fp8bs_status fp8bs_diag_read(const void* src, size_t bytes, void* sink, void* stream);
+
+/* Plain copy of `bytes` bytes (multiple of 16, both 16-byte aligned).       */
+fp8bs_status fp8bs_diag_copy(const void* src, void* dst, size_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8BS_H */

@@ -1,0 +1,159 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/fp8bs.h declares, binds to the HIP runtime torch loaded, and rejects
+bad arguments before any HIP call (argument checks precede the device
+check, so on a machine without a GPU a valid call reports ERR_DEVICE)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8bs.h")
+
+OK, E_NULL, E_SHAPE, E_ALIGN, E_WS, E_DEV, E_LAUNCH, E_CFG = range(8)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import fp8_block_scaled_fp8bs_amd as fp8bs
+    if not os.path.exists(fp8bs.library_path()):
+        import __graft_entry__
+        __graft_entry__.build()
+    return fp8bs.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp8bs_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("fp8bs_quantize_weight", "fp8bs_quantize_act", "fp8bs_gemm"):
+        assert required in names
+
+
+def test_library_exports_every_declared_function(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", lib._name], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+
+
+def test_hip_imports_exist_in_torch_runtime(lib):
+    """Every HIP runtime symbol the library imports is exported by the
+    runtime copy that torch ships (the one it binds to at load time)."""
+    import torch
+    torch_hip = os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so")
+    if not os.path.exists(torch_hip):
+        pytest.skip("torch does not bundle its own HIP runtime")
+    need = subprocess.run(["nm", "-D", "--undefined-only", lib._name], capture_output=True,
+                          text=True, check=True).stdout
+    have = subprocess.run(["nm", "-D", "--defined-only", torch_hip], capture_output=True,
+                          text=True, check=True).stdout
+    have_names = {l.split()[-1].split("@")[0] for l in have.splitlines() if l.strip()}
+    need_names = [l.split()[-1].split("@")[0] for l in need.splitlines()
+                  if "hip" in l.lower() and l.strip()]
+    assert need_names and all(n in have_names for n in need_names), need_names
+
+
+def test_single_hip_runtime_mapped(lib):
+    import fp8_block_scaled_fp8bs_amd as fp8bs
+    maps = fp8bs.hip_runtime_mappings()
+    assert len(maps["libfp8bs"]) == 1
+    assert len(maps["libamdhip64"]) == 1, maps
+
+
+def test_status_strings(lib):
+    for s in range(8):
+        assert lib.fp8bs_status_string(s).decode().startswith("FP8BS_")
+    assert b"gfx950" in lib.fp8bs_build_info()
+
+
+P = 0x100000  # a fake, 256-byte aligned "device" pointer: never dereferenced
+
+
+def gemm(lib, x=P, m=8, w=P, ws=P, n=512, k=1024, y=P, work=None, wbytes=0):
+    return lib.fp8bs_gemm(x, m, w, ws, n, k, y, work, wbytes, None)
+
+
+def test_gemm_argument_errors_before_any_launch(lib):
+    assert gemm(lib, n=500) == E_SHAPE
+    assert gemm(lib, k=1000) == E_SHAPE
+    assert gemm(lib, m=33) == E_SHAPE
+    assert gemm(lib, m=-1) == E_SHAPE
+    assert gemm(lib, x=None) == E_NULL
+    assert gemm(lib, w=None) == E_NULL
+    assert gemm(lib, ws=None) == E_NULL
+    assert gemm(lib, y=None) == E_NULL
+    assert gemm(lib, x=P + 2) == E_ALIGN
+    assert gemm(lib, w=P + 8) == E_ALIGN
+    assert gemm(lib, ws=P + 2) == E_ALIGN
+    assert gemm(lib, y=P + 4) == E_ALIGN
+    # empty extents are no-ops and touch nothing
+    assert gemm(lib, m=0, x=None, y=None) == OK
+    assert gemm(lib, n=0, w=None, ws=None) == OK
+    # a valid call gets as far as the device check (no GPU here)
+    import torch
+    if not torch.cuda.is_available():
+        assert gemm(lib) == E_DEV
+
+
+def test_gemm_workspace_checked(lib):
+    import fp8_block_scaled_fp8bs_amd as fp8bs
+    cfg = fp8bs.select_config(8, 5120, 17408)
+    need = fp8bs.workspace_bytes(8, 5120, 17408)
+    assert cfg.split_k > 1 and need == cfg.split_k * 8 * 5120 * 4
+    assert gemm(lib, n=5120, k=17408) == E_WS
+    assert gemm(lib, n=5120, k=17408, work=P, wbytes=need - 16) == E_WS
+    assert gemm(lib, n=5120, k=17408, work=P + 4, wbytes=need) == E_ALIGN
+
+
+def test_quantizer_argument_errors(lib):
+    assert lib.fp8bs_quantize_weight(P, 100, 128, P, P, None) == E_SHAPE
+    assert lib.fp8bs_quantize_weight(P, 128, 130, P, P, None) == E_SHAPE
+    assert lib.fp8bs_quantize_weight(None, 128, 128, P, P, None) == E_NULL
+    assert lib.fp8bs_quantize_weight(P + 1, 128, 128, P, P, None) == E_ALIGN
+    assert lib.fp8bs_quantize_weight(None, 0, 128, None, None, None) == OK
+    assert lib.fp8bs_quantize_act(P, 3, 100, P, P, None) == E_SHAPE
+    assert lib.fp8bs_quantize_act(P, 3, 128, None, P, None) == E_NULL
+    assert lib.fp8bs_quantize_act(P, 3, 128, P, P + 1, None) == E_ALIGN
+    assert lib.fp8bs_quantize_act(None, 0, 128, None, None, None) == OK
+    assert lib.fp8bs_encode_e4m3(P, 4, P, 3, None) == E_SHAPE
+    assert lib.fp8bs_encode_e4m3(P, 0, P, 0, None) == OK
+
+
+def test_explicit_config_validation(lib):
+    import fp8_block_scaled_fp8bs_amd as fp8bs
+    from fp8_block_scaled_fp8bs_amd import GemmConfig
+    c = fp8bs._Config(1, 3, 1, 1, 4, 1, 0, 0)  # 3 tiles per wave is not compiled
+    r = lib.fp8bs_gemm_ex(P, None, None, 8, P, P, 512, 1024, P, None, 0, ctypes.byref(c), None)
+    assert r == E_CFG
+    c = GemmConfig(1, 1, 4, 1, 4, split_k=9)._c()  # more splits than K blocks (8)
+    r = lib.fp8bs_gemm_ex(P, None, None, 8, P, P, 512, 1024, P, P, 1 << 20, ctypes.byref(c), None)
+    assert r == E_CFG
+    c = GemmConfig(2, 2, 1, 8, 5)._c()  # DOT path takes at most 4 rows
+    r = lib.fp8bs_gemm_ex(P, None, None, 8, P, P, 512, 1024, P, None, 0, ctypes.byref(c), None)
+    assert r == E_CFG
+    assert lib.fp8bs_gemm_ex(P, None, None, 8, P, P, 512, 1024, P, None, 0, None, None) == E_NULL
+
+
+def test_config_table_is_a_pure_function_of_shape(lib):
+    import fp8_block_scaled_fp8bs_amd as fp8bs
+    shapes = [(m, n, k) for m in (1, 2, 3, 8, 16, 17, 32)
+              for (n, k) in ((512, 1024), (5120, 5120), (34816, 5120), (5120, 17408),
+                             (248320, 5120), (128, 128))]
+    for s in shapes:
+        a, b = fp8bs.select_config(*s), fp8bs.select_config(*s)
+        assert a == b
+        assert 1 <= a.split_k <= s[2] // 128
+        rows = (8 if a.path == fp8bs.PATH_DOT else 16) * a.tiles_n * a.waves_n
+        assert s[1] % rows == 0
+        if a.path == fp8bs.PATH_DOT:
+            assert s[0] <= 4
+    with pytest.raises(fp8bs.Fp8bsError):
+        fp8bs.select_config(8, 100, 128)
