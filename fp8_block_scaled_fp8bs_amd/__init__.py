@@ -96,7 +96,7 @@ def load() -> ctypes.CDLL:
         "fp8bs_status_string": (ctypes.c_char_p, [i32]),
         "fp8bs_launch_count": (ctypes.c_uint64, [i32]),
         "fp8bs_build_info": (ctypes.c_char_p, []),
-        "fp8bs_diag_read": (i32, [vp, sz, vp, vp]),
+        "fp8bs_diag_read": (i32, [vp, sz, vp, i32, vp]),
         "fp8bs_diag_copy": (i32, [vp, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
@@ -246,9 +246,9 @@ def build_info() -> str:
     return load().fp8bs_build_info().decode()
 
 
-def diag_read(t: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+def diag_read(t: torch.Tensor, sink: torch.Tensor, blocks: int = 0, stream=None) -> None:
     nbytes = t.numel() * t.element_size()
-    _check(load().fp8bs_diag_read(t.data_ptr(), nbytes, sink.data_ptr(), _stream(stream)))
+    _check(load().fp8bs_diag_read(t.data_ptr(), nbytes, sink.data_ptr(), blocks, _stream(stream)))
 
 
 def diag_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:

@@ -411,8 +411,9 @@ const char* fp8bs_build_info(void) {
   return "fp8bs gfx950; encoder=" FP8BS_ENC_NAME "; flags=" FP8BS_BUILD_FLAGS;
 }
 
-fp8bs_status fp8bs_diag_read(const void* src, size_t bytes, void* sink, void* stream) {
-  if (bytes % 16) return FP8BS_ERR_SHAPE;
+fp8bs_status fp8bs_diag_read(const void* src, size_t bytes, void* sink, int32_t blocks,
+                             void* stream) {
+  if (bytes % 16 || blocks < 0) return FP8BS_ERR_SHAPE;
   if (bytes == 0) return FP8BS_OK;
   if (!src || !sink) return FP8BS_ERR_NULL;
   if (!aligned(src, 16) || !aligned(sink, 16)) return FP8BS_ERR_ALIGN;
@@ -426,6 +427,7 @@ fp8bs_status fp8bs_diag_read(const void* src, size_t bytes, void* sink, void* st
   const int64_t cap = (int64_t)dev.num_cu * 16;
   if (want > cap) want = cap;
   if (want < 1) want = 1;
+  if (blocks > 0) want = blocks;
   void* args[] = {&s, &n16, &sk};
   g_counts[CNT_DIAG]++;
   return launch(reinterpret_cast<const void*>(diag_read_kernel), dim3((unsigned)want), dim3(256),

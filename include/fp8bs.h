@@ -191,9 +191,12 @@ const char* fp8bs_build_info(void);
 
 /* ---- diagnostics (bandwidth reference kernels) --------------------------- */
 
-/* Streaming read of `bytes` bytes (multiple of 16, 16-byte aligned) with a
- * checksum written to sink[0..3] (uint32), so the reads are not elided.     */
-fp8bs_status fp8bs_diag_read(const void* src, size_t bytes, void* sink, void* stream);
+/* Streaming read of `bytes` bytes (multiple of 16, 16-byte aligned); sink
+ * is a 16-byte device buffer written only on an impossible checksum, so the
+ * reads cannot be elided. blocks = workgroups of 256 threads (0 = about
+ * four 16-byte loads per lane, at most 16 per CU).                          */
+fp8bs_status fp8bs_diag_read(const void* src, size_t bytes, void* sink, int32_t blocks,
+                             void* stream);
 
 /* Plain copy of `bytes` bytes (multiple of 16, both 16-byte aligned).       */
 fp8bs_status fp8bs_diag_copy(const void* src, void* dst, size_t bytes, void* stream);
