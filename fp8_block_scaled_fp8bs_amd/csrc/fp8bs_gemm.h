@@ -14,15 +14,20 @@
 //   grid.x = row group (ROWS consecutive output columns n), grid.y = K split s.
 //   A workgroup stages the activations of its K range in LDS once (casting
 //   bf16 to E4M3 when fused), then its waves stream weight tiles from HBM
-//   with 16-byte loads, several K blocks in flight per wave. waves_k waves
-//   share a row range and interleave its K blocks; their fp32 partials are
-//   summed in LDS in wave order. With split_k > 1 each workgroup writes an
-//   fp32 partial tile that is summed over s in order by a second kernel.
+//   with 16-byte loads that cover whole 128-byte lines, several K blocks in
+//   flight per wave. waves_k waves share a row range and interleave its K
+//   blocks; their fp32 partials are summed in LDS in wave order. With
+//   split_k > 1 each workgroup writes an fp32 partial tile; the partials of a
+//   row group are summed over s in order, either by a second kernel or, in
+//   the same launch, by the workgroup of the row group that finishes last.
 #pragma once
 
 #include "fp8bs_device.h"
 
 namespace fp8bs {
+
+// Output handling of a kernel instance.
+enum { OUT_DIRECT = 0, OUT_PARTIAL = 1, OUT_LAST_ARRIVER = 2 };
 
 struct GemmParams {
   const uint16_t* x;    // bf16 [m][k] (fused cast) or nullptr
@@ -32,8 +37,12 @@ struct GemmParams {
   const float* ws;      // fp32 [n/128][k/128]
   uint16_t* y;          // bf16 [m][n]
   float* part;          // fp32 [split][m][n] when split > 1
+  uint64_t* counters;   // [row groups] arrival counters (last-arriver reduce)
+  uint64_t epoch;       // nonzero tag of this launch (last-arriver reduce)
   int m, n, k, kbn;     // kbn = k / 128
   int split;
+  int out;              // OUT_DIRECT, OUT_PARTIAL or OUT_LAST_ARRIVER
+  int rows_per_wg;      // row-range kernel: output columns per workgroup (multiple of 4)
 };
 
 // LDS layout of a workgroup:
@@ -44,46 +53,44 @@ __host__ __device__ inline int lds_act_bytes(int nblk, int m) {
   return ((nblk * m * (ACT_STRIDE + 4)) + 15) & ~15;
 }
 
-// Number of K blocks of split s (balanced: sizes differ by at most one).
+// K blocks [kb0, kb1) of split s (balanced: sizes differ by at most one).
 __device__ __forceinline__ void split_range(int s, int split, int kbn, int& kb0, int& kb1) {
   kb0 = (int)((int64_t)s * kbn / split);
   kb1 = (int)((int64_t)(s + 1) * kbn / split);
 }
 
-// Stage the activations of blocks [kb0, kb0+nblk) into LDS. Fused: each
-// thread casts CR quarter-blocks whose bf16 were loaded (before the weight
-// prefetch) into xr; any remainder is loaded and cast afterwards.
-// Pre-quantized: codes and scales are copied.
+// ---------------------------------------------------- activation staging ---
+
+// Quarter-block g of the workgroup's activation range: block bm = g / 4
+// (bm = kbl * m + row), columns 32 * (g % 4) .. +31 of that block.
 template <int NT, int CR>
-__device__ __forceinline__ void load_act_quarters(const GemmParams& p, int kb0, int nblk, int tid,
+__device__ __forceinline__ void load_act_quarters(const GemmParams& p, int kb0, int G, int tid,
                                                   int base, uint4 (&xr)[CR][4]) {
-  const int G = nblk * p.m * 4;
 #pragma unroll
   for (int i = 0; i < CR; ++i) {
-    int g = base + tid + i * NT;
-    g = g < G ? g : G - 1;
-    const int qq = g & 3, bm = g >> 2;
-    const int kbl = bm / p.m, m = bm - kbl * p.m;
-    const uint4* src = reinterpret_cast<const uint4*>(
-        p.x + (size_t)m * (size_t)p.k + (size_t)(kb0 + kbl) * BLK + qq * 32);
+    const int g = base + tid + i * NT;
+    if (g < G) {
+      const int qq = g & 3, bm = g >> 2;
+      const int kbl = bm / p.m, m = bm - kbl * p.m;
+      const uint4* src = reinterpret_cast<const uint4*>(
+          p.x + (size_t)m * (size_t)p.k + (size_t)(kb0 + kbl) * BLK + qq * 32);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) xr[i][j] = src[j];
+      for (int j = 0; j < 4; ++j) xr[i][j] = src[j];
+    }
   }
 }
 
 template <int NT, int CR>
-__device__ __forceinline__ void cast_act_quarters(const GemmParams& p, int nblk, int tid, int base,
+__device__ __forceinline__ void cast_act_quarters(int G, int tid, int base,
                                                   const uint4 (&xr)[CR][4], uint8_t* act,
                                                   float* act_s) {
-  const int G = nblk * p.m * 4;
 #pragma unroll
   for (int i = 0; i < CR; ++i) {
-    const int gi = base + tid + i * NT;
-    const int g = gi < G ? gi : G - 1;
-    const int qq = g & 3, bm = g >> 2;  // bm = kbl * m + row
-    uint32_t codes[8];
-    const float s = cast_quarter(xr[i], codes);
-    if (gi < G) {
+    const int g = base + tid + i * NT;
+    if (g < G) {  // G is a multiple of 4: the four lanes of a quad agree
+      const int qq = g & 3, bm = g >> 2;
+      uint32_t codes[8];
+      const float s = cast_quarter(xr[i], codes);
       uint4* d = reinterpret_cast<uint4*>(act + bm * ACT_STRIDE + qq * 32);
       d[0] = make_uint4(codes[0], codes[1], codes[2], codes[3]);
       d[1] = make_uint4(codes[4], codes[5], codes[6], codes[7]);
@@ -109,38 +116,122 @@ __device__ __forceinline__ void copy_act(const GemmParams& p, int kb0, int nblk,
   }
 }
 
-// Cast (or copy) the activations of this workgroup's K range into LDS.
-// The first CR quarters per thread were loaded into xr earlier.
+// Cast the activation quarters beyond the first CR * NT (needed only when a
+// workgroup's K range holds more than CR * NT quarter blocks). Runs before
+// the weight prefetch is issued, so its waits cover activation loads only.
+template <int NT, int CR, bool FUSED>
+__device__ __forceinline__ void stage_act_tail(const GemmParams& p, int kb0, int nblk, int tid,
+                                               uint8_t* act, float* act_s) {
+  if constexpr (FUSED) {
+    const int G = nblk * p.m * 4;
+    for (int base = CR * NT; base < G; base += CR * NT) {
+      uint4 xr2[CR][4];
+      load_act_quarters<NT, CR>(p, kb0, G, tid, base, xr2);
+      cast_act_quarters<NT, CR>(G, tid, base, xr2, act, act_s);
+    }
+  }
+}
+
+// Cast the first CR * NT activation quarters (loaded into xr before the
+// weight prefetch), or copy pre-quantized codes and scales into LDS.
 template <int NT, int CR, bool FUSED>
 __device__ __forceinline__ void stage_act(const GemmParams& p, int kb0, int nblk, int tid,
                                           const uint4 (&xr)[CR][4], uint8_t* act, float* act_s) {
   if constexpr (FUSED) {
-    cast_act_quarters<NT, CR>(p, nblk, tid, 0, xr, act, act_s);
-    const int G = nblk * p.m * 4;
-    for (int base = CR * NT; base < G; base += CR * NT) {
-      uint4 xr2[CR][4];
-      load_act_quarters<NT, CR>(p, kb0, nblk, tid, base, xr2);
-      cast_act_quarters<NT, CR>(p, nblk, tid, base, xr2, act, act_s);
-    }
+    cast_act_quarters<NT, CR>(nblk * p.m * 4, tid, 0, xr, act, act_s);
   } else {
     copy_act<NT>(p, kb0, nblk, tid, act, act_s);
+  }
+}
+
+// ------------------------------------------------------ split-K epilogue ---
+
+// Called by every thread of a workgroup after it stored its fp32 partial
+// tile part[s][m][n0 .. n0+ROWS). One 64-bit counter per row group holds
+// (launch epoch << 8) | arrivals. An arrival that finds another epoch in the
+// counter (a previous launch, or whatever the memory held) starts this
+// launch's count at 1; the arrival that brings the count to `split` is the
+// last one and sums the split partials in order s = 0, 1, ..., split-1, then
+// clears the counter. The epoch is unique per host-side launch call, so no
+// initialization of the counters is ever needed; a replayed graph reuses
+// its epoch, which the clearing makes safe.
+template <int NT, int ROWS>
+__device__ __forceinline__ void last_arriver_reduce(const GemmParams& p, int n0, int tid) {
+  __shared__ int s_last;
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) {
+    uint64_t* c = p.counters + blockIdx.x;
+    uint64_t old = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint64_t nv;
+    for (;;) {
+      nv = ((old >> 8) == p.epoch) ? old + 1 : ((p.epoch << 8) | 1u);
+      const uint64_t prev = atomicCAS(reinterpret_cast<unsigned long long*>(c),
+                                      (unsigned long long)old, (unsigned long long)nv);
+      if (prev == old) break;
+      old = prev;
+    }
+    s_last = (int)(nv & 0xFFu) == p.split;
+    if (s_last) __hip_atomic_store(c, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  const int M = p.m;
+  const size_t mn = (size_t)M * (size_t)p.n;
+  for (int i = tid; i < M * (ROWS / 4); i += NT) {
+    const int m = i / (ROWS / 4), r4 = i - m * (ROWS / 4);
+    const size_t off = (size_t)m * (size_t)p.n + n0 + 4 * r4;
+    float4 a = *reinterpret_cast<const float4*>(p.part + off);
+    for (int s = 1; s < p.split; ++s) {
+      const float4 b = *reinterpret_cast<const float4*>(p.part + (size_t)s * mn + off);
+      a.x += b.x;
+      a.y += b.y;
+      a.z += b.z;
+      a.w += b.w;
+    }
+    *reinterpret_cast<uint2*>(p.y + off) =
+        make_uint2(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w));
   }
 }
 
 // ====================================================================
 // MFMA path: v_mfma_f32_16x16x128_f8f6f4, A = 16 weight rows x 128 K,
 // B = 128 K x 16 activation rows (zero beyond m). Lane l holds A row l%16
-// and B column l%16, 32 bytes each, at K offsets 16*(l/16) .. +15 and
-// 64 + 16*(l/16) .. +15 of the block (the same K positions for A and B, so
-// the dot product is the block's). The result D[n][m] sits in lane l as
-// rows 4*(l/16) + i, column l%16.
+// and B column l%16: the 32 K positions 32*(l/16) .. +31 of the block, in
+// order (the same K positions in A and B, so the product is the block's
+// dot product). The result D[n][m] sits in lane l as rows 4*(l/16) + i,
+// column l%16.
+//
+// Weight loads cover whole 128-byte rows: load P takes rows 0-7 of the
+// tile, load Q rows 8-15; lane l reads 16 bytes of row (l&7) (P) or
+// 8+(l&7) (Q). A per-lane select and a rotate by 8 lanes within each row of
+// 16 lanes then give every lane the two 16-byte pieces of its own row.
 // ====================================================================
 
-template <int MT, int TN, int WN, int WK, int D, bool FUSED, bool SPLIT>
+struct TileLoad {
+  uint4 p, q;
+};
+
+__device__ __forceinline__ i32x8 tile_operand(const TileLoad& t, bool lo8) {
+  const uint32_t pp[4] = {t.p.x, t.p.y, t.p.z, t.p.w};
+  const uint32_t qq[4] = {t.q.x, t.q.y, t.q.z, t.q.w};
+  i32x8 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t xv = lo8 ? pp[i] : qq[i];
+    const uint32_t zv = lo8 ? qq[i] : pp[i];
+    r[i] = (int)xv;
+    r[4 + i] = __builtin_amdgcn_mov_dpp((int)zv, DPP_ROW_ROR8, 0xF, 0xF, false);
+  }
+  return r;
+}
+
+template <int MT, int TN, int WN, int WK, int D, bool FUSED>
 __global__ __launch_bounds__(64 * WN * WK) void gemm_mfma_kernel(GemmParams p) {
   constexpr int NT = 64 * WN * WK;
   constexpr int ROWS = 16 * TN * WN;
-  constexpr int CR = FUSED ? 4 : 1;
+  constexpr int CR = FUSED ? 2 : 1;
   extern __shared__ __align__(16) uint8_t lds[];
 
   const int tid = threadIdx.x;
@@ -157,37 +248,43 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_mfma_kernel(GemmParams p) {
   float* act_s = reinterpret_cast<float*>(lds + nblk * M * ACT_STRIDE);
   f32x4* red = reinterpret_cast<f32x4*>(lds + lds_act_bytes(nblk, M));
 
-  const int row0 = blockIdx.x * ROWS + wn * 16 * TN;
+  const int n0 = blockIdx.x * ROWS;
+  const int row0 = n0 + wn * 16 * TN;
   const int l16 = lane & 15, g16 = lane >> 4;
-  const uint8_t* wrow = p.wq + (size_t)(row0 + l16) * (size_t)p.k + 16 * g16;
+  const int l7 = lane & 7, hb = (lane >> 3) & 1;
+  const bool lo8 = hb == 0;
+  const uint8_t* wp = p.wq + (size_t)(row0 + l7) * (size_t)p.k + 16 * (2 * g16 + hb);
+  const uint8_t* wqp = p.wq + (size_t)(row0 + 8 + l7) * (size_t)p.k + 16 * (2 * g16 + 1 - hb);
   const int nj = nblk > wk ? (nblk - wk + WK - 1) / WK : 0;  // this wave's K blocks
 
-  // 1. activation bf16 loads first (so their wait does not wait on weights)
+  // 1. activation bf16 loads first (so waiting for them does not wait on weights)
+  stage_act_tail<NT, CR, FUSED>(p, kb0, nblk, tid, act, act_s);
   uint4 xr[CR][4];
-  if constexpr (FUSED) load_act_quarters<NT, CR>(p, kb0, nblk, tid, 0, xr);
+  if constexpr (FUSED) load_act_quarters<NT, CR>(p, kb0, nblk * M * 4, tid, 0, xr);
 
   // 2. weight prefetch: D blocks per wave in flight
-  i32x8 wb[D][TN];
+  TileLoad wb[D][TN];
   auto load_block = [&](int d, int j) {
     const int jc = j < nj ? j : (nj > 0 ? nj - 1 : 0);
     int kb = kb0 + wk + jc * WK;
     kb = kb < p.kbn ? kb : p.kbn - 1;
-    const uint8_t* src = wrow + (size_t)kb * BLK;
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
-      const uint4* st = reinterpret_cast<const uint4*>(src + (size_t)t * 16 * (size_t)p.k);
-      const uint4 lo = st[0];
-      const uint4 hi = st[4];
-      wb[d][t] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
-                       (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      const size_t off = (size_t)t * 16 * (size_t)p.k + (size_t)kb * BLK;
+      wb[d][t].p = load_stream16(wp + off);
+      wb[d][t].q = load_stream16(wqp + off);
     }
   };
+  // At most two blocks are issued before the cast (see gemm_rows_kernel).
+  constexpr int PRE = D < 2 ? D : 2;
 #pragma unroll
-  for (int d = 0; d < D; ++d) load_block(d, d);
+  for (int d = 0; d < PRE; ++d) load_block(d, d);
 
   // 3. stage activations in LDS
   stage_act<NT, CR, FUSED>(p, kb0, nblk, tid, xr, act, act_s);
-  __syncthreads();
+#pragma unroll
+  for (int d = PRE; d < D; ++d) load_block(d, d);
+  lds_barrier();
 
   // 4. stream K blocks
   f32x4 acc[TN][MT];
@@ -205,9 +302,9 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_mfma_kernel(GemmParams p) {
     for (int mt = 0; mt < MT; ++mt) {
       const int m = l16 + 16 * mt;
       if (m < M) {
-        const uint8_t* a = act + (kbl * M + m) * ACT_STRIDE + 16 * g16;
+        const uint8_t* a = act + (kbl * M + m) * ACT_STRIDE + 32 * g16;
         const uint4 lo = *reinterpret_cast<const uint4*>(a);
-        const uint4 hi = *reinterpret_cast<const uint4*>(a + 64);
+        const uint4 hi = *reinterpret_cast<const uint4*>(a + 16);
         bop[mt] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
                         (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         sa[mt] = act_s[kbl * M + m];
@@ -219,12 +316,13 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_mfma_kernel(GemmParams p) {
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
       const int nb = (row0 + 16 * t) / BLK;
-      const float sw = p.ws[(size_t)nb * (size_t)p.kbn + kb];
+      const float sw = load_invariant(p.ws, (size_t)nb * (size_t)p.kbn + kb);
+      const i32x8 aop = tile_operand(wb[d][t], lo8);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
         const f32x4 pb =
-            __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wb[d][t], bop[mt], z, 0, 0, 0, 0, 0, 0);
+            __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop[mt], z, 0, 0, 0, 0, 0, 0);
         const float sc = sa[mt] * sw;
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[t][mt][i] = __builtin_fmaf(pb[i], sc, acc[t][mt][i]);
@@ -277,16 +375,169 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_mfma_kernel(GemmParams p) {
         const int m = l16 + 16 * mt;
         if (m < M) {
           const int n = row0 + 16 * t + 4 * g16;
-          if constexpr (SPLIT) {
-            float4* dst = reinterpret_cast<float4*>(p.part + ((size_t)s * M + m) * (size_t)p.n + n);
-            *dst = make_float4(acc[t][mt][0], acc[t][mt][1], acc[t][mt][2], acc[t][mt][3]);
-          } else {
+          if (p.out == OUT_DIRECT) {
             uint2* dst = reinterpret_cast<uint2*>(p.y + (size_t)m * (size_t)p.n + n);
             *dst = make_uint2(pack_bf16x2(acc[t][mt][0], acc[t][mt][1]),
                               pack_bf16x2(acc[t][mt][2], acc[t][mt][3]));
+          } else {
+            float4* dst = reinterpret_cast<float4*>(p.part + ((size_t)s * M + m) * (size_t)p.n + n);
+            *dst = make_float4(acc[t][mt][0], acc[t][mt][1], acc[t][mt][2], acc[t][mt][3]);
           }
         }
       }
+  }
+  if (p.out == OUT_LAST_ARRIVER) last_arriver_reduce<NT, ROWS>(p, n0, tid);
+}
+
+// ====================================================================
+// MFMA row-range kernel: one workgroup per compute unit. Workgroup g owns
+// the output columns [g*R, g*R + R) (R = rows_per_wg, the last 16-row tile
+// partly masked) over the whole K range, so no partial sums leave the
+// workgroup and the activations are cast once per workgroup. Its WK waves
+// interleave the K blocks of each 16-row weight tile (wave w takes blocks
+// w, w+WK, ...), so at any time the workgroup reads one contiguous stretch of
+// weight rows. Each wave streams the sequence (tile, block) with D tiles in
+// flight across tile boundaries; at the end of a tile the waves' partial
+// sums are added in wave order through LDS (two alternating LDS areas, one
+// barrier per tile) and wave 0 writes the tile's outputs.
+// ====================================================================
+
+template <int MT, int WK, int D, int PRE, bool FUSED>
+__global__ __launch_bounds__(64 * WK) void gemm_rows_kernel(GemmParams p) {
+  constexpr int NT = 64 * WK;
+  constexpr int CR = FUSED ? 3 : 1;
+  extern __shared__ __align__(16) uint8_t lds[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wk = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int M = p.m;
+  const int kbn = p.kbn;
+  const int r0 = blockIdx.x * p.rows_per_wg;
+  const int r1 = r0 + p.rows_per_wg < p.n ? r0 + p.rows_per_wg : p.n;
+  const int nrows = r1 - r0;
+  const int ntile = (nrows + 15) >> 4;
+  const int njw = (kbn + WK - 1) / WK;  // blocks per tile per wave (same for every wave)
+  const int nitem = ntile * njw;
+
+  uint8_t* act = lds;
+  float* act_s = reinterpret_cast<float*>(lds + kbn * M * ACT_STRIDE);
+  f32x4* red = reinterpret_cast<f32x4*>(lds + lds_act_bytes(kbn, M));
+
+  const int l16 = lane & 15, g16 = lane >> 4;
+  const int l7 = lane & 7, hb = (lane >> 3) & 1;
+  const bool lo8 = hb == 0;
+
+  // 1. activations: any quarters beyond CR * NT first, then the first CR * NT
+  stage_act_tail<NT, CR, FUSED>(p, 0, kbn, tid, act, act_s);
+  uint4 xr[CR][4];
+  if constexpr (FUSED) load_act_quarters<NT, CR>(p, 0, kbn * M * 4, tid, 0, xr);
+
+  // 2. weight prefetch. Item i = (tile i / njw, block wk + (i % njw) * WK).
+  //    Rows past the range and blocks past K are clamped to valid addresses
+  //    (their products are discarded).
+  TileLoad wb[D];
+  auto load_item = [&](int d, int i) {
+    i = i < nitem ? i : nitem - 1;
+    const int t = i / njw, j = i - t * njw;
+    int kb = wk + j * WK;
+    kb = kb < kbn ? kb : kbn - 1;
+    int ra = 16 * t + l7, rb = 16 * t + 8 + l7;
+    ra = ra < nrows ? ra : nrows - 1;
+    rb = rb < nrows ? rb : nrows - 1;
+    const uint8_t* base = p.wq + (size_t)kb * BLK;
+    wb[d].p = load_stream16(base + (size_t)(r0 + ra) * (size_t)p.k + 16 * (2 * g16 + hb));
+    wb[d].q = load_stream16(base + (size_t)(r0 + rb) * (size_t)p.k + 16 * (2 * g16 + 1 - hb));
+  };
+  // Only PRE items are issued before the cast: a wave stalls at issue once
+  // the memory queue is full, and the cast must not wait behind the whole
+  // prefetch. The other D - PRE items follow the cast.
+#pragma unroll
+  for (int d = 0; d < PRE; ++d) load_item(d, d);
+
+  // 3. stage activations in LDS
+  stage_act<NT, CR, FUSED>(p, 0, kbn, tid, xr, act, act_s);
+#pragma unroll
+  for (int d = PRE; d < D; ++d) load_item(d, d);
+  lds_barrier();
+
+  f32x4 acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int d, int i) {
+    const int t = i / njw, j = i - t * njw;
+    const int kb = wk + j * WK;
+    if (kb < kbn) {
+      // A 16-row tile may straddle two 128-row scale blocks (row ranges are
+      // multiples of 4, not of 16); each lane's four output rows lie in one.
+      const int row = r0 + 16 * t;
+      const int nb_lo = row / BLK, nb_hi = (row + 15) / BLK;
+      const float sw_lo = load_invariant(p.ws, (size_t)nb_lo * (size_t)kbn + kb);
+      const float sw_hi = load_invariant(p.ws, (size_t)nb_hi * (size_t)kbn + kb);
+      const float sw = (row + 4 * g16) / BLK == nb_lo ? sw_lo : sw_hi;
+      const i32x8 aop = tile_operand(wb[d], lo8);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int m = l16 + 16 * mt;
+        i32x8 bop = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+        float sa = 0.0f;
+        if (m < M) {
+          const uint8_t* a = act + (kb * M + m) * ACT_STRIDE + 32 * g16;
+          const uint4 lo = *reinterpret_cast<const uint4*>(a);
+          const uint4 hi = *reinterpret_cast<const uint4*>(a + 16);
+          bop = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                      (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+          sa = act_s[kb * M + m];
+        }
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        const f32x4 pb =
+            __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop, z, 0, 0, 0, 0, 0, 0);
+        const float sc = sa * sw;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[mt][q] = __builtin_fmaf(pb[q], sc, acc[mt][q]);
+      }
+    }
+    if (j == njw - 1) {
+      // end of tile t: partial sums of waves 1..WK-1 through LDS, summed in wave order
+      f32x4* rt = red + (t & 1) * (WK - 1) * MT * 64;
+      if (wk > 0) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) rt[((wk - 1) * MT + mt) * 64 + lane] = acc[mt];
+      }
+      lds_barrier();
+      if (wk == 0) {
+        for (int w = 1; w < WK; ++w)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) acc[mt] += rt[((w - 1) * MT + mt) * 64 + lane];
+        const int rl = 16 * t + 4 * g16;  // first of this lane's four rows
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const int m = l16 + 16 * mt;
+          if (m < M && rl < nrows) {
+            uint2* dst = reinterpret_cast<uint2*>(p.y + (size_t)m * (size_t)p.n + r0 + rl);
+            *dst = make_uint2(pack_bf16x2(acc[mt][0], acc[mt][1]),
+                              pack_bf16x2(acc[mt][2], acc[mt][3]));
+          }
+        }
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+
+  const int ngrp = (nitem + D - 1) / D;
+  for (int g = 0; g + 1 < ngrp; ++g) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      compute(d, g * D + d);
+      load_item(d, (g + 1) * D + d);
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    const int i = (ngrp - 1) * D + d;
+    if (i < nitem) compute(d, i);
   }
 }
 
@@ -298,11 +549,11 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_mfma_kernel(GemmParams p) {
 // xs * ws; the 8 lanes of a row are summed once at the end.
 // ====================================================================
 
-template <int MD, int RT, int WN, int WK, int D, bool FUSED, bool SPLIT>
+template <int MD, int RT, int WN, int WK, int D, bool FUSED>
 __global__ __launch_bounds__(64 * WN * WK) void gemm_dot_kernel(GemmParams p) {
   constexpr int NT = 64 * WN * WK;
   constexpr int ROWS = 8 * RT * WN;
-  constexpr int CR = FUSED ? 4 : 1;
+  constexpr int CR = FUSED ? 2 : 1;
   extern __shared__ __align__(16) uint8_t lds[];
 
   const int tid = threadIdx.x;
@@ -319,13 +570,15 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_dot_kernel(GemmParams p) {
   float* act_s = reinterpret_cast<float*>(lds + nblk * M * ACT_STRIDE);
   float* red = reinterpret_cast<float*>(lds + lds_act_bytes(nblk, M));
 
-  const int row0 = blockIdx.x * ROWS + wn * 8 * RT;
+  const int n0 = blockIdx.x * ROWS;
+  const int row0 = n0 + wn * 8 * RT;
   const int r8 = lane >> 3, seg = lane & 7;
   const uint8_t* wrow = p.wq + (size_t)(row0 + r8) * (size_t)p.k + 16 * seg;
   const int nj = nblk > wk ? (nblk - wk + WK - 1) / WK : 0;
 
+  stage_act_tail<NT, CR, FUSED>(p, kb0, nblk, tid, act, act_s);
   uint4 xr[CR][4];
-  if constexpr (FUSED) load_act_quarters<NT, CR>(p, kb0, nblk, tid, 0, xr);
+  if constexpr (FUSED) load_act_quarters<NT, CR>(p, kb0, nblk * M * 4, tid, 0, xr);
 
   uint4 wb[D][RT];
   auto load_block = [&](int d, int j) {
@@ -335,13 +588,16 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_dot_kernel(GemmParams p) {
     const uint8_t* src = wrow + (size_t)kb * BLK;
 #pragma unroll
     for (int t = 0; t < RT; ++t)
-      wb[d][t] = *reinterpret_cast<const uint4*>(src + (size_t)t * 8 * (size_t)p.k);
+      wb[d][t] = load_stream16(src + (size_t)t * 8 * (size_t)p.k);
   };
+  constexpr int PRE = D < 2 ? D : 2;
 #pragma unroll
-  for (int d = 0; d < D; ++d) load_block(d, d);
+  for (int d = 0; d < PRE; ++d) load_block(d, d);
 
   stage_act<NT, CR, FUSED>(p, kb0, nblk, tid, xr, act, act_s);
-  __syncthreads();
+#pragma unroll
+  for (int d = PRE; d < D; ++d) load_block(d, d);
+  lds_barrier();
 
   float acc[RT][MD];
 #pragma unroll
@@ -369,7 +625,7 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_dot_kernel(GemmParams p) {
       }
     }
     const int nb = row0 / BLK;
-    const float sw = p.ws[(size_t)nb * (size_t)p.kbn + kb];
+    const float sw = load_invariant(p.ws, (size_t)nb * (size_t)p.kbn + kb);
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       const uint32_t ww[4] = {wb[d][t].x, wb[d][t].y, wb[d][t].z, wb[d][t].w};
@@ -434,14 +690,15 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_dot_kernel(GemmParams p) {
 #pragma unroll
       for (int m = 0; m < MD; ++m) {
         if (m < M) {
-          if constexpr (SPLIT)
-            p.part[((size_t)s * M + m) * (size_t)p.n + n] = acc[t][m];
-          else
+          if (p.out == OUT_DIRECT)
             p.y[(size_t)m * (size_t)p.n + n] = (uint16_t)bf16_rne(acc[t][m]);
+          else
+            p.part[((size_t)s * M + m) * (size_t)p.n + n] = acc[t][m];
         }
       }
     }
   }
+  if (p.out == OUT_LAST_ARRIVER) last_arriver_reduce<NT, ROWS>(p, n0, tid);
 }
 
 }  // namespace fp8bs

@@ -1,40 +1,50 @@
-// Table of the compiled GEMM kernel variants, shared by the translation
-// units that instantiate them and the host code that picks one.
+// Table of the compiled GEMM kernel variants. Each instantiation unit adds
+// its kernels at load time; the host code looks a configuration up here.
 #pragma once
+
+#include <vector>
 
 #include "fp8bs_gemm.h"
 
 namespace fp8bs {
 
 struct KernelEntry {
-  int path;    // 1 = MFMA, 2 = DOT
+  int path;    // 1 = MFMA grid, 2 = DOT grid, 3 = MFMA row range (one workgroup per CU)
   int mt;      // MFMA: 16-row activation tiles (1: m <= 16, 2: m <= 32); DOT: max m
   int tn;      // MFMA: 16-row weight tiles per wave; DOT: 8-row groups per wave
   int wn, wk, d;
-  int fused, split;
+  int fused;   // activations cast in the kernel (1) or given as codes and scales (0)
   void (*fn)(GemmParams);
 };
 
-extern const KernelEntry g_mfma_entries[];
-extern const int g_mfma_count;
-extern const KernelEntry g_dot_entries[];
-extern const int g_dot_count;
+std::vector<KernelEntry>& kernel_registry();
+
+struct KernelRegistrar {
+  KernelRegistrar(std::initializer_list<KernelEntry> l) {
+    for (const KernelEntry& e : l) kernel_registry().push_back(e);
+  }
+};
 
 }  // namespace fp8bs
 
-// (tiles_n, waves_n, waves_k, depth) shapes compiled for the MFMA path.
-#define FP8BS_MFMA_SHAPES(X) \
-  X(1, 1, 8, 5)              \
-  X(1, 1, 4, 5)              \
-  X(1, 2, 4, 5)              \
-  X(1, 4, 1, 4)              \
-  X(1, 4, 2, 4)              \
-  X(2, 2, 2, 4)              \
-  X(2, 4, 1, 4)              \
-  X(2, 2, 1, 8)
+#define FP8BS_MFMA_ENTRY(TN, WN, WK, D)                                   \
+  {1, 1, TN, WN, WK, D, 1, gemm_mfma_kernel<1, TN, WN, WK, D, true>},     \
+  {1, 2, TN, WN, WK, D, 1, gemm_mfma_kernel<2, TN, WN, WK, D, true>},     \
+  {1, 1, TN, WN, WK, D, 0, gemm_mfma_kernel<1, TN, WN, WK, D, false>},    \
+  {1, 2, TN, WN, WK, D, 0, gemm_mfma_kernel<2, TN, WN, WK, D, false>},
 
-// (groups_n, waves_n, waves_k, depth) shapes compiled for the DOT path.
-#define FP8BS_DOT_SHAPES(X) \
-  X(2, 1, 8, 5)             \
-  X(2, 4, 1, 4)             \
-  X(4, 2, 2, 4)
+#define FP8BS_DOT_ENTRY(RT, WN, WK, D)                                    \
+  {2, 1, RT, WN, WK, D, 1, gemm_dot_kernel<1, RT, WN, WK, D, true>},      \
+  {2, 2, RT, WN, WK, D, 1, gemm_dot_kernel<2, RT, WN, WK, D, true>},      \
+  {2, 4, RT, WN, WK, D, 1, gemm_dot_kernel<4, RT, WN, WK, D, true>},      \
+  {2, 1, RT, WN, WK, D, 0, gemm_dot_kernel<1, RT, WN, WK, D, false>},     \
+  {2, 2, RT, WN, WK, D, 0, gemm_dot_kernel<2, RT, WN, WK, D, false>},     \
+  {2, 4, RT, WN, WK, D, 0, gemm_dot_kernel<4, RT, WN, WK, D, false>},
+
+// Row-range kernel: (waves along K, tiles in flight, of which issued before
+// the activation cast). The config's tiles_n field selects the pre-cast count.
+#define FP8BS_ROWS_ENTRY(WK, D, PRE)                                         \
+  {3, 1, PRE, 1, WK, D, 1, gemm_rows_kernel<1, WK, D, PRE, true>},           \
+  {3, 2, PRE, 1, WK, D, 1, gemm_rows_kernel<2, WK, D, PRE, true>},           \
+  {3, 1, PRE, 1, WK, D, 0, gemm_rows_kernel<1, WK, D, PRE, false>},          \
+  {3, 2, PRE, 1, WK, D, 0, gemm_rows_kernel<2, WK, D, PRE, false>},

@@ -121,12 +121,17 @@ size_t fp8bs_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k);
 
 /* ---- explicit kernel configuration (tuning and tests) ------------------- */
 
-enum { FP8BS_PATH_AUTO = 0, FP8BS_PATH_MFMA = 1, FP8BS_PATH_DOT = 2 };
+enum { FP8BS_PATH_AUTO = 0, FP8BS_PATH_MFMA = 1, FP8BS_PATH_DOT = 2, FP8BS_PATH_MFMA_ROWS = 3 };
 enum { FP8BS_REDUCE_KERNEL = 0, FP8BS_REDUCE_LAST_ARRIVER = 1 };
 
 /* How one GEMM is laid out on the GPU.
- *   path      MFMA (16x16x128 FP8 matrix instructions) or DOT (per-lane
- *             fp32 dot products, for the smallest m)
+ *   path      MFMA (16x16x128 FP8 matrix instructions, a grid of row
+ *             groups x K splits), DOT (per-lane fp32 dot products, for the
+ *             smallest m), or MFMA_ROWS (one workgroup per compute unit, each
+ *             owning a contiguous range of output columns over the whole K
+ *             range; waves_k and depth apply, tiles_n gives how many of
+ *             the depth tiles are requested before the activation cast,
+ *             waves_n and split_k must be 1)
  *   tiles_n   MFMA: 16-row tiles per wave (1, 2, 4); DOT: 8-row groups per wave (1, 2, 4)
  *   waves_n   waves side by side along N in one workgroup (1, 2, 4)
  *   waves_k   waves splitting a workgroup's K range (1, 2, 4, 8); their
@@ -136,9 +141,13 @@ enum { FP8BS_REDUCE_KERNEL = 0, FP8BS_REDUCE_LAST_ARRIVER = 1 };
  *             in split order, never with atomics on data
  *   reduce    how split partials are combined when split_k > 1:
  *             FP8BS_REDUCE_KERNEL = a second kernel sums them;
- *             FP8BS_REDUCE_LAST_ARRIVER = the last workgroup of each output
- *             tile to finish (found with one integer counter per tile) sums
- *             them in split order in the same launch.                       */
+ *             FP8BS_REDUCE_LAST_ARRIVER = in the same launch, the last
+ *             workgroup of each output tile to finish sums them in split
+ *             order. It is found with one 64-bit integer arrival counter per
+ *             tile, kept in the workspace and tagged with a per-launch epoch,
+ *             so the workspace still needs no initialization. The integer
+ *             counter is the only atomic; the partials are plain loads and
+ *             stores summed in a fixed order.                              */
 typedef struct {
   int32_t path;
   int32_t tiles_n;

@@ -14,9 +14,20 @@ pytestmark = pytest.mark.gpu
 
 TOL = dict(rel=2.0 ** -7, abs_rms=1e-3)
 
-MFMA_SHAPES = [(1, 1, 8, 5), (1, 1, 4, 5), (1, 2, 4, 5), (1, 4, 1, 4), (1, 4, 2, 4),
-               (2, 2, 2, 4), (2, 4, 1, 4), (2, 2, 1, 8)]
-DOT_SHAPES = [(2, 1, 8, 5), (2, 4, 1, 4), (4, 2, 2, 4)]
+# (tiles or row groups per wave, waves along N, waves along K, blocks in flight):
+# every shape compiled into the library.
+MFMA_SHAPES = [(1, 1, 8, 5), (1, 1, 8, 2), (1, 1, 8, 4), (1, 1, 4, 5), (1, 1, 4, 8), (1, 2, 4, 5),
+               (1, 2, 4, 2), (2, 1, 8, 2), (2, 1, 4, 4), (4, 1, 8, 1), (4, 1, 4, 2), (2, 1, 8, 4),
+               (1, 4, 1, 5), (1, 4, 2, 5), (1, 4, 4, 2), (1, 5, 1, 5), (1, 5, 2, 5), (1, 5, 2, 2),
+               (1, 8, 1, 5), (1, 8, 2, 2), (2, 4, 1, 5), (2, 2, 2, 4), (2, 2, 4, 2), (1, 2, 8, 2)]
+DOT_SHAPES = [(2, 1, 8, 5), (2, 4, 1, 5), (4, 2, 2, 4), (1, 1, 8, 5), (2, 1, 8, 2), (4, 1, 8, 2),
+              (2, 2, 4, 4)]
+# (waves along K, tiles in flight, tiles issued before the cast) of the
+# row-range kernel
+ROWS_SHAPES = [(8, 4, 2), (8, 4, 4), (8, 2, 2), (8, 3, 1), (8, 6, 2), (16, 2, 1), (16, 3, 1),
+               (4, 8, 2)]
+# (split_k, reduce): no split, second-kernel reduce, last-arriver reduce
+SPLITS = [(1, 0), (3, 0), (4, 1), (5, 1)]
 
 
 @pytest.fixture(scope="module")
@@ -112,19 +123,23 @@ def _configs():
     out = []
     for (tn, wn, wk, d) in MFMA_SHAPES:
         for m in (1, 5, 8, 16, 17, 32):
-            for split in (1, 3):
-                out.append(("mfma", (1, tn, wn, wk, d, split), m))
+            for split, red in SPLITS:
+                out.append(("mfma", (1, tn, wn, wk, d, split, red), m))
     for (rt, wn, wk, d) in DOT_SHAPES:
         for m in (1, 2, 3, 4):
-            for split in (1, 3):
-                out.append(("dot", (2, rt, wn, wk, d, split), m))
+            for split, red in SPLITS:
+                out.append(("dot", (2, rt, wn, wk, d, split, red), m))
+    for (wk, d, pre) in ROWS_SHAPES:
+        for m in (1, 5, 8, 16, 17, 32):
+            out.append(("rows", (3, pre, 1, wk, d, 1, 0), m))
     return out
 
 
 @pytest.fixture(scope="module")
 def ragged_problem(fp8bs):
-    # K = 13 blocks: not a multiple of any waves_k, depth or split count used
-    return _random_problem(fp8bs, 32, 512, 13 * 128, 77)
+    # K = 13 blocks: not a multiple of any waves_k, depth or split count used;
+    # N = 1280 is a multiple of every row count (16 .. 128, and 80)
+    return _random_problem(fp8bs, 32, 1280, 13 * 128, 77)
 
 
 @pytest.mark.parametrize("path,cfg,m", _configs())
@@ -139,6 +154,41 @@ def test_every_compiled_config(fp8bs, ragged_problem, path, cfg, m):
     _assert_close(host_bits(y), ref, f"{path} {cfg} m={m}")
     # the pre-quantized route through the same configuration gives the same bits
     xq, xs = fp8bs.quantize_act(x)
+    y2 = fp8bs.gemm_ex(c, pr.wq, pr.ws, x_q=xq, x_s=xs)
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+
+
+def test_last_arriver_workspace_reuse(fp8bs):
+    """Calls with different splits (power of two or not) and shapes share one
+    workspace whose counters start as arbitrary bytes, in any order, and
+    every result is the one a fresh workspace gives."""
+    from fp8_block_scaled_fp8bs_amd import GemmConfig
+    pr = _random_problem(fp8bs, 8, 1280, 16 * 128, 91)
+    ws = torch.empty(1 << 22, dtype=torch.uint8, device="cuda")
+    ws.fill_(0xA5)  # arbitrary initial counter values
+    seq = [(2, (1, 1, 1, 8, 5)), (4, (1, 1, 4, 1, 5)), (8, (1, 1, 5, 2, 5)), (16, (1, 1, 1, 4, 5)),
+           (3, (1, 1, 4, 1, 5)), (5, (1, 1, 1, 8, 5)), (8, (1, 1, 8, 1, 5)), (7, (1, 2, 2, 2, 4))] * 3
+    for split, shape in seq:
+        c = GemmConfig(*shape, split_k=split, reduce=1)
+        y = fp8bs.gemm_ex(c, pr.wq, pr.ws, x=pr.x, workspace=ws)
+        y_fresh = fp8bs.gemm_ex(c, pr.wq, pr.ws, x=pr.x)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), y_fresh.view(torch.int16)), (split, shape)
+        _assert_close(host_bits(y), pr.ref, f"reuse {split} {shape}")
+
+
+@pytest.mark.parametrize("m,n,k", [(8, 384, 640), (3, 1152, 1920), (16, 2048, 5120), (32, 640, 1024)])
+@pytest.mark.parametrize("wk,d,pre", ROWS_SHAPES)
+def test_row_range_kernel_uneven_ranges(fp8bs, m, n, k, wk, d, pre):
+    """Row ranges that leave the last workgroup short, 4-row ranges and
+    partial 16-row tiles; pre-quantized route gives the same bits."""
+    from fp8_block_scaled_fp8bs_amd import GemmConfig
+    pr = _random_problem(fp8bs, m, n, k, 7 * m + n + k + wk + d)
+    c = GemmConfig(3, pre, 1, wk, d)
+    y = fp8bs.gemm_ex(c, pr.wq, pr.ws, x=pr.x)
+    torch.cuda.synchronize()
+    _assert_close(host_bits(y), pr.ref, f"rows {wk},{d} m={m} n={n} k={k}")
+    xq, xs = fp8bs.quantize_act(pr.x)
     y2 = fp8bs.gemm_ex(c, pr.wq, pr.ws, x_q=xq, x_s=xs)
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
 
