@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "µs/GEMM and achieved HBM GB/s (% of 8 TB/s) at M=8, K=5120 FP8 block-scaled"
 HBM_PEAK_GBPS = 8000.0
+PATH_NAMES = {1: "mfma", 2: "dot", 3: "mfma_rows", 4: "mfma_stream"}
 FP8_DENSE_PEAK_TFLOPS = 5000.0
 
 WORKLOAD_DESCR = {
@@ -279,9 +280,10 @@ def main() -> int:
             "m": m, "n": n, "k": k,
             "algorithmic_bytes": alg_bytes,
             "weight_pool": pool_n,
-            "kernel": {"path": "mfma" if cfg.path == 1 else "dot", "tiles_n": cfg.tiles_n,
+            "kernel": {"path": PATH_NAMES.get(cfg.path, str(cfg.path)), "tiles_n": cfg.tiles_n,
                        "waves_n": cfg.waves_n, "waves_k": cfg.waves_k, "depth": cfg.depth,
-                       "split_k": cfg.split_k},
+                       "split_k": cfg.split_k,
+                       "launches_per_gemm": 2 if cfg.split_k > 1 and cfg.reduce == 0 else 1},
             "timing": "hip graph of the steps, replayed" if graph_ms is not None else "stream launches",
         },
         "us_per_gemm": round(us, 3),

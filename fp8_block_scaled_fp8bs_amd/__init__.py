@@ -28,7 +28,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "libfp8bs.so")
 _LIB = None
 
-PATH_AUTO, PATH_MFMA, PATH_DOT = 0, 1, 2
+PATH_AUTO, PATH_MFMA, PATH_DOT, PATH_MFMA_ROWS, PATH_MFMA_STREAM = 0, 1, 2, 3, 4
 REDUCE_KERNEL, REDUCE_LAST_ARRIVER = 0, 1
 COUNTER = {"quant_weight": 0, "quant_act": 1, "gemm_mfma": 2, "gemm_dot": 3,
            "split_reduce": 4, "encode": 5, "diag": 6}

@@ -85,17 +85,30 @@ std::vector<KernelEntry>& kernel_registry() {
 
 namespace {
 
+// Row-range paths: one workgroup per compute unit, n split over them.
+inline bool is_row_range(int path) {
+  return path == FP8BS_PATH_MFMA_ROWS || path == FP8BS_PATH_MFMA_STREAM;
+}
+
+// The streaming kernel addresses activations with 32-bit buffer offsets
+// and marks unused fetches with offset 2^31: every byte offset of the bf16
+// activations must stay below that.
+inline bool stream_offsets_fit(int64_t m, int64_t k) { return m * k * 2 < ((int64_t)1 << 31); }
+
 const KernelEntry* find_kernel(const fp8bs_gemm_config& c, int m, bool fused) {
   int mt;
   if (c.path == FP8BS_PATH_MFMA || c.path == FP8BS_PATH_MFMA_ROWS) {
     mt = m <= 16 ? 1 : 2;
+  } else if (c.path == FP8BS_PATH_MFMA_STREAM) {
+    if (c.tiles_n != 1) return nullptr;
+    mt = m <= 8 ? 1 : (m <= 16 ? 2 : 4);  // staging passes
   } else if (c.path == FP8BS_PATH_DOT) {
     if (m > 4) return nullptr;
     mt = m <= 1 ? 1 : (m <= 2 ? 2 : 4);
   } else {
     return nullptr;
   }
-  const bool rows = c.path == FP8BS_PATH_MFMA_ROWS;
+  const bool rows = is_row_range(c.path);
   for (const KernelEntry& e : kernel_registry())
     if (e.path == c.path && e.mt == mt && e.tn == c.tiles_n && (rows || e.wn == c.waves_n) &&
         e.wk == c.waves_k && e.d == c.depth && e.fused == (int)fused)
@@ -106,7 +119,7 @@ const KernelEntry* find_kernel(const fp8bs_gemm_config& c, int m, bool fused) {
 // Output columns per workgroup of a grid configuration (the row-range
 // path divides n by the compute-unit count at launch instead).
 int config_rows(const fp8bs_gemm_config& c) {
-  if (c.path == FP8BS_PATH_MFMA_ROWS) return 4;
+  if (is_row_range(c.path)) return 4;
   return (c.path == FP8BS_PATH_DOT ? 8 : 16) * c.tiles_n * c.waves_n;
 }
 
@@ -119,6 +132,8 @@ int rows_per_workgroup(int64_t n, int num_cu) {
 }
 
 size_t config_lds_bytes(const fp8bs_gemm_config& c, int m, int kbn) {
+  if (c.path == FP8BS_PATH_MFMA_STREAM)
+    return (size_t)lds_stream_bytes(kbn, m, c.waves_k, m <= 16 ? 1 : 2);
   if (c.path == FP8BS_PATH_MFMA_ROWS) {
     const int mt = m <= 16 ? 1 : 2;
     return (size_t)lds_act_bytes(kbn, m) + (size_t)2 * (c.waves_k - 1) * mt * 64 * 16;
@@ -162,6 +177,7 @@ constexpr int RK = FP8BS_REDUCE_KERNEL;
 constexpr int MF = FP8BS_PATH_MFMA;
 constexpr int DT = FP8BS_PATH_DOT;
 constexpr int RW = FP8BS_PATH_MFMA_ROWS;
+constexpr int ST = FP8BS_PATH_MFMA_STREAM;
 
 bool candidate_fits(const Candidate& cd, int64_t m, int64_t n, int kbn, fp8bs_gemm_config* out) {
   fp8bs_gemm_config c = make_cfg(cd.path, cd.tn, cd.wn, cd.wk, cd.d, cd.split);
@@ -169,7 +185,8 @@ bool candidate_fits(const Candidate& cd, int64_t m, int64_t n, int kbn, fp8bs_ge
   if (n % config_rows(c) != 0) return false;
   if (cd.path == DT && m > 4) return false;
   if (c.split_k > kbn) return false;
-  const size_t lds_limit = cd.path == RW ? kRowsLdsLimit : kAutoLdsLimit;
+  const size_t lds_limit = is_row_range(cd.path) ? kRowsLdsLimit : kAutoLdsLimit;
+  if (cd.path == ST && !stream_offsets_fit(m, (int64_t)kbn * BLK)) return false;
   if (kbn > 0 && config_lds_bytes(c, (int)m, kbn) > lds_limit) return false;
   *out = c;
   return true;
@@ -185,11 +202,14 @@ bool select_config(int64_t m, int64_t n, int64_t k, fp8bs_gemm_config* out) {
   const int kbn = (int)(k / BLK);
   const int64_t nbn = n / BLK;
   static const Candidate small_m_wide[] = {{DT, 2, 4, 1, 5, 1, RK}, {DT, 2, 1, 8, 5, 1, RK}};
-  static const Candidate small_m[] = {{DT, 2, 1, 8, 5, 1, RK}, {DT, 1, 1, 8, 5, 1, RK}};
-  static const Candidate vocab[] = {{RW, 2, 1, 8, 4, 1, RK}, {MF, 1, 1, 8, 5, 1, RK}};
-  static const Candidate wide[] = {{RW, 2, 1, 8, 4, 1, RK}, {MF, 1, 1, 4, 5, 4, RK}};
-  static const Candidate square[] = {{RW, 2, 1, 8, 4, 1, RK}, {MF, 1, 5, 1, 5, 4, RK},
-                                     {MF, 1, 2, 4, 5, 1, RK}};
+  static const Candidate small_m[] = {{DT, 2, 2, 4, 4, 1, RK}, {DT, 2, 1, 8, 5, 1, RK},
+                                      {DT, 1, 1, 8, 5, 1, RK}};
+  static const Candidate vocab[] = {{ST, 1, 1, 8, 6, 1, RK}, {RW, 2, 1, 8, 6, 1, RK},
+                                    {MF, 1, 1, 8, 5, 1, RK}, {MF, 1, 1, 8, 5, 2, RK}};
+  static const Candidate wide[] = {{RW, 2, 1, 8, 6, 1, RK}, {RW, 1, 1, 16, 3, 1, RK},
+                                   {MF, 1, 1, 4, 5, 4, RK}};
+  static const Candidate square[] = {{MF, 1, 2, 4, 5, 1, RK}, {MF, 1, 5, 1, 5, 4, RK},
+                                     {RW, 1, 1, 16, 2, 1, RK}};
   static const Candidate deep[] = {{MF, 1, 5, 2, 2, 4, RK}, {MF, 1, 5, 2, 5, 4, RK},
                                    {MF, 1, 4, 2, 5, 8, RK}};
   static const Candidate fallback[] = {{MF, 1, 1, 4, 5, 1, RK}, {MF, 1, 1, 4, 5, 2, RK},
@@ -286,7 +306,8 @@ fp8bs_status gemm_impl(const void* x_bf16, const uint8_t* x_fp8, const float* x_
     return FP8BS_ERR_SHAPE;
   }
   if (c.split_k < 1 || c.split_k > 64 || c.split_k > kbn) return FP8BS_ERR_CONFIG;
-  if (c.path == FP8BS_PATH_MFMA_ROWS && c.split_k != 1) return FP8BS_ERR_CONFIG;
+  if (is_row_range(c.path) && (c.split_k != 1 || c.waves_n != 1)) return FP8BS_ERR_CONFIG;
+  if (c.path == FP8BS_PATH_MFMA_STREAM && !stream_offsets_fit(m, k)) return FP8BS_ERR_CONFIG;
   if (c.reduce != FP8BS_REDUCE_KERNEL && c.reduce != FP8BS_REDUCE_LAST_ARRIVER)
     return FP8BS_ERR_CONFIG;
   const bool split = c.split_k > 1;
@@ -335,11 +356,11 @@ fp8bs_status gemm_impl(const void* x_bf16, const uint8_t* x_fp8, const float* x_
   p.out = !split ? OUT_DIRECT : (last_arriver ? OUT_LAST_ARRIVER : OUT_PARTIAL);
   void* args[] = {&p};
   dim3 grid((unsigned)(n / rows), (unsigned)c.split_k);
-  if (c.path == FP8BS_PATH_MFMA_ROWS) {
+  if (is_row_range(c.path)) {
     p.rows_per_wg = rows_per_workgroup(n, dev.num_cu);
     grid = dim3((unsigned)((n + p.rows_per_wg - 1) / p.rows_per_wg), 1);
   }
-  const dim3 block(64 * (c.path == FP8BS_PATH_MFMA_ROWS ? 1 : c.waves_n) * c.waves_k);
+  const dim3 block(64 * (is_row_range(c.path) ? 1 : c.waves_n) * c.waves_k);
   g_counts[c.path == FP8BS_PATH_DOT ? CNT_DOT : CNT_MFMA]++;
   fp8bs_status ls = launch(reinterpret_cast<const void*>(ke->fn), grid, block, lds, stream, args);
   if (ls != FP8BS_OK || !split || last_arriver) return ls;

@@ -146,19 +146,47 @@ __device__ __forceinline__ void stage_act(const GemmParams& p, int kb0, int nblk
 
 // ------------------------------------------------------ split-K epilogue ---
 
-// Called by every thread of a workgroup after it stored its fp32 partial
-// tile part[s][m][n0 .. n0+ROWS). One 64-bit counter per row group holds
-// (launch epoch << 8) | arrivals. An arrival that finds another epoch in the
-// counter (a previous launch, or whatever the memory held) starts this
-// launch's count at 1; the arrival that brings the count to `split` is the
-// last one and sums the split partials in order s = 0, 1, ..., split-1, then
-// clears the counter. The epoch is unique per host-side launch call, so no
-// initialization of the counters is ever needed; a replayed graph reuses
-// its epoch, which the clearing makes safe.
+// Partials that another workgroup sums in the same launch (last-arriver
+// reduce) are written and read with device-scope coherent accesses: the
+// stores write through this XCD's L2 and the loads do not hit stale lines
+// of another XCD's L2. No cache-wide writeback or invalidate is needed.
+__device__ __forceinline__ void store_coherent(float* dst, float v) {
+  __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* src) {
+  return __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Store an fp32 partial of 4 consecutive outputs: plain vector store when a
+// second kernel sums the partials, coherent stores for the last-arriver
+// reduce.
+__device__ __forceinline__ void store_partial4(const GemmParams& p, float* dst, float a, float b,
+                                               float c, float d) {
+  if (p.out == OUT_LAST_ARRIVER) {
+    store_coherent(dst, a);
+    store_coherent(dst + 1, b);
+    store_coherent(dst + 2, c);
+    store_coherent(dst + 3, d);
+  } else {
+    *reinterpret_cast<float4*>(dst) = make_float4(a, b, c, d);
+  }
+}
+
+// Called by every thread of a workgroup after it stored (coherently) its fp32
+// partial tile part[s][m][n0 .. n0+ROWS). Each thread first waits until its
+// own stores are performed at device scope; after the barrier the whole
+// tile is visible to every workgroup. One 64-bit counter per row group
+// holds (launch epoch << 8) | arrivals. An arrival that finds another epoch
+// in the counter (a previous launch, or whatever the memory held) starts
+// this launch's count at 1; the arrival that brings the count to `split` is
+// the last one and sums the split partials in order s = 0, 1, ..., split-1
+// (coherent loads), then clears the counter. The epoch is unique per
+// host-side launch call, so no initialization of the counters is ever
+// needed; a replayed graph reuses its epoch, which the clearing makes safe.
 template <int NT, int ROWS>
 __device__ __forceinline__ void last_arriver_reduce(const GemmParams& p, int n0, int tid) {
   __shared__ int s_last;
-  __threadfence();
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (tid == 0) {
     uint64_t* c = p.counters + blockIdx.x;
@@ -166,32 +194,29 @@ __device__ __forceinline__ void last_arriver_reduce(const GemmParams& p, int n0,
     uint64_t nv;
     for (;;) {
       nv = ((old >> 8) == p.epoch) ? old + 1 : ((p.epoch << 8) | 1u);
-      const uint64_t prev = atomicCAS(reinterpret_cast<unsigned long long*>(c),
-                                      (unsigned long long)old, (unsigned long long)nv);
-      if (prev == old) break;
-      old = prev;
+      if (__hip_atomic_compare_exchange_strong(c, &old, nv, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT))
+        break;
     }
     s_last = (int)(nv & 0xFFu) == p.split;
     if (s_last) __hip_atomic_store(c, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
   const int M = p.m;
   const size_t mn = (size_t)M * (size_t)p.n;
   for (int i = tid; i < M * (ROWS / 4); i += NT) {
     const int m = i / (ROWS / 4), r4 = i - m * (ROWS / 4);
     const size_t off = (size_t)m * (size_t)p.n + n0 + 4 * r4;
-    float4 a = *reinterpret_cast<const float4*>(p.part + off);
+    float a[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) a[q] = load_coherent(p.part + off + q);
     for (int s = 1; s < p.split; ++s) {
-      const float4 b = *reinterpret_cast<const float4*>(p.part + (size_t)s * mn + off);
-      a.x += b.x;
-      a.y += b.y;
-      a.z += b.z;
-      a.w += b.w;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) a[q] += load_coherent(p.part + (size_t)s * mn + off + q);
     }
     *reinterpret_cast<uint2*>(p.y + off) =
-        make_uint2(pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w));
+        make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
   }
 }
 
@@ -380,8 +405,8 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_mfma_kernel(GemmParams p) {
             *dst = make_uint2(pack_bf16x2(acc[t][mt][0], acc[t][mt][1]),
                               pack_bf16x2(acc[t][mt][2], acc[t][mt][3]));
           } else {
-            float4* dst = reinterpret_cast<float4*>(p.part + ((size_t)s * M + m) * (size_t)p.n + n);
-            *dst = make_float4(acc[t][mt][0], acc[t][mt][1], acc[t][mt][2], acc[t][mt][3]);
+            store_partial4(p, p.part + ((size_t)s * M + m) * (size_t)p.n + n, acc[t][mt][0],
+                           acc[t][mt][1], acc[t][mt][2], acc[t][mt][3]);
           }
         }
       }
@@ -451,14 +476,27 @@ __global__ __launch_bounds__(64 * WK) void gemm_rows_kernel(GemmParams p) {
   };
   // Only PRE items are issued before the cast: a wave stalls at issue once
   // the memory queue is full, and the cast must not wait behind the whole
-  // prefetch. The other D - PRE items follow the cast.
+  // prefetch. The other items are issued one after each cast quarter, so the
+  // weight stream keeps flowing while the VALU casts.
 #pragma unroll
   for (int d = 0; d < PRE; ++d) load_item(d, d);
 
-  // 3. stage activations in LDS
-  stage_act<NT, CR, FUSED>(p, 0, kbn, tid, xr, act, act_s);
+  // 3. stage activations in LDS, interleaved with the rest of the prefetch
+  if constexpr (FUSED) {
+    const int G = kbn * M * 4;
 #pragma unroll
-  for (int d = PRE; d < D; ++d) load_item(d, d);
+    for (int c = 0; c < CR; ++c) {
+      cast_act_quarters<NT, 1>(G, tid, c * NT, reinterpret_cast<const uint4(&)[1][4]>(xr[c]),
+                               act, act_s);
+      if (PRE + c < D) load_item(PRE + c, PRE + c);
+    }
+#pragma unroll
+    for (int d = PRE + CR; d < D; ++d) load_item(d, d);
+  } else {
+    copy_act<NT>(p, 0, kbn, tid, act, act_s);
+#pragma unroll
+    for (int d = PRE; d < D; ++d) load_item(d, d);
+  }
   lds_barrier();
 
   f32x4 acc[MT];
@@ -472,7 +510,8 @@ __global__ __launch_bounds__(64 * WK) void gemm_rows_kernel(GemmParams p) {
       // A 16-row tile may straddle two 128-row scale blocks (row ranges are
       // multiples of 4, not of 16); each lane's four output rows lie in one.
       const int row = r0 + 16 * t;
-      const int nb_lo = row / BLK, nb_hi = (row + 15) / BLK;
+      const int row_last = row + 15 < r1 ? row + 15 : r1 - 1;  // last valid row of the tile
+      const int nb_lo = row / BLK, nb_hi = row_last / BLK;
       const float sw_lo = load_invariant(p.ws, (size_t)nb_lo * (size_t)kbn + kb);
       const float sw_hi = load_invariant(p.ws, (size_t)nb_hi * (size_t)kbn + kb);
       const float sw = (row + 4 * g16) / BLK == nb_lo ? sw_lo : sw_hi;
@@ -511,6 +550,254 @@ __global__ __launch_bounds__(64 * WK) void gemm_rows_kernel(GemmParams p) {
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) acc[mt] += rt[((w - 1) * MT + mt) * 64 + lane];
         const int rl = 16 * t + 4 * g16;  // first of this lane's four rows
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const int m = l16 + 16 * mt;
+          if (m < M && rl < nrows) {
+            uint2* dst = reinterpret_cast<uint2*>(p.y + (size_t)m * (size_t)p.n + r0 + rl);
+            *dst = make_uint2(pack_bf16x2(acc[mt][0], acc[mt][1]),
+                              pack_bf16x2(acc[mt][2], acc[mt][3]));
+          }
+        }
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+
+  const int ngrp = (nitem + D - 1) / D;
+  for (int g = 0; g + 1 < ngrp; ++g) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      compute(d, g * D + d);
+      load_item(d, (g + 1) * D + d);
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    const int i = (ngrp - 1) * D + d;
+    if (i < nitem) compute(d, i);
+  }
+}
+
+// ====================================================================
+// MFMA streaming row-range kernel: the work split of gemm_rows_kernel (one
+// workgroup per compute unit, a contiguous range of output columns over the
+// whole K range, waves interleaving the K blocks of each 16-row tile), but
+// without a staging phase. Wave w is the only reader of the activation
+// blocks kb = w, w + WK, ..., so it stages exactly those itself, each one
+// when the first tile reaches it: the bf16 block (or its codes and scales)
+// is fetched together with the weight tile of that item, cast in registers,
+// and kept in LDS for the later tiles. The cast of the whole activation is
+// thereby spread over the weight stream instead of delaying its start, and
+// each workgroup still casts every activation element once.
+//
+// Staging layout: a K block of m activation rows is 8m segments of 16
+// values; segment task = 8 * row + seg is handled by lane task % 64 of pass
+// task / 64, so the 8 segments of one row sit in 8 adjacent lanes and the
+// block amax is an 8-lane reduction. Codes go to LDS as 16-byte chunks
+// [kb][seg][row], which the MFMA B operand reads back without bank
+// conflicts (lane = row, two consecutive segments).
+//
+// Activation fetches go through a buffer resource: items of later tiles
+// issue the same load instructions with an out-of-range offset, which
+// return zeros without touching memory, so every item issues the same
+// number of loads and the wait counts stay exact.
+// ====================================================================
+
+// LDS bytes of the streaming kernel: codes [kbn][8][m] x 16, scales
+// [kbn][m] fp32 (padded to 16), tile-sum exchange [2][WK-1][MT][64] x 16.
+__host__ __device__ inline int lds_stream_bytes(int kbn, int m, int wk, int mt) {
+  return kbn * m * BLK + ((kbn * m * 4 + 15) & ~15) + 2 * (wk - 1) * mt * 64 * 16;
+}
+
+constexpr uint32_t BUF_OOB = 0x80000000u;  // an offset past every staged tensor
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ float octet_max(float v) {
+  v = __builtin_fmaxf(v, dpp_f<DPP_QUAD_XOR1>(v));
+  v = __builtin_fmaxf(v, dpp_f<DPP_QUAD_XOR2>(v));
+  v = __builtin_fmaxf(v, dpp_f<DPP_ROW_HALF_MIRROR>(v));
+  return v;
+}
+
+// One K block of activations as fetched by one wave: per pass, 16 bf16
+// values (two 16-byte loads) or 16 codes plus the row's scale.
+template <int XP>
+struct ActFetch {
+  uint4 a[XP];
+  uint4 b[XP];  // fused: values 8..15; pre-quantized: .x holds the scale bits
+};
+
+// XP = staging passes (1, 2, 4): 8 * XP >= m activation rows.
+template <int XP, int WK, int D, bool FUSED>
+__global__ __launch_bounds__(64 * WK) void gemm_stream_kernel(GemmParams p) {
+  constexpr int MT = XP > 2 ? 2 : 1;  // 16-row activation tiles of the MFMA B operand
+  extern __shared__ __align__(16) uint8_t lds[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wk = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int M = p.m;
+  const int kbn = p.kbn;
+  const int r0 = blockIdx.x * p.rows_per_wg;
+  const int r1 = r0 + p.rows_per_wg < p.n ? r0 + p.rows_per_wg : p.n;
+  const int nrows = r1 - r0;
+  const int ntile = (nrows + 15) >> 4;
+  const int njw = (kbn + WK - 1) / WK;  // blocks per tile per wave (same for every wave)
+  const int nitem = ntile * njw;
+
+  uint4* act = reinterpret_cast<uint4*>(lds);                     // [kbn][8][M] chunks
+  float* act_s = reinterpret_cast<float*>(lds + kbn * M * BLK);    // [kbn][M]
+  f32x4* red = reinterpret_cast<f32x4*>(lds + kbn * M * BLK + ((kbn * M * 4 + 15) & ~15));
+
+  const int l16 = lane & 15, g16 = lane >> 4;
+  const int l7 = lane & 7, hb = (lane >> 3) & 1;
+  const bool lo8 = hb == 0;
+
+  // activation sources (byte offsets < 2^31 are guaranteed by the host)
+  const __amdgpu_buffer_rsrc_t xr =
+      FUSED ? buffer_rsrc(p.x, (uint32_t)M * (uint32_t)p.k * 2u)
+            : buffer_rsrc(p.xq, (uint32_t)M * (uint32_t)p.k);
+  const __amdgpu_buffer_rsrc_t sr = buffer_rsrc(p.xs, FUSED ? 0u : (uint32_t)M * (uint32_t)kbn * 4u);
+
+  TileLoad wb[D];
+  ActFetch<XP> xb[D];
+  auto load_item = [&](int d, int i) {
+    i = i < nitem ? i : nitem - 1;
+    const int t = i / njw, j = i - t * njw;
+    int kb = wk + j * WK;
+    const bool stage = t == 0 && kb < kbn;
+    kb = kb < kbn ? kb : kbn - 1;
+    int ra = 16 * t + l7, rb = 16 * t + 8 + l7;
+    ra = ra < nrows ? ra : nrows - 1;
+    rb = rb < nrows ? rb : nrows - 1;
+    const uint8_t* base = p.wq + (size_t)kb * BLK;
+    wb[d].p = load_stream16(base + (size_t)(r0 + ra) * (size_t)p.k + 16 * (2 * g16 + hb));
+    wb[d].q = load_stream16(base + (size_t)(r0 + rb) * (size_t)p.k + 16 * (2 * g16 + 1 - hb));
+#pragma unroll
+    for (int c = 0; c < XP; ++c) {
+      const int task = 64 * c + lane;
+      const int m = task >> 3, seg = task & 7;
+      const bool live = stage && m < M;
+      if constexpr (FUSED) {
+        const uint32_t off = live ? ((uint32_t)m * (uint32_t)p.k + (uint32_t)kb * BLK + 16u * seg) * 2u
+                                  : BUF_OOB;
+        xb[d].a[c] = buffer_load16(xr, off);
+        xb[d].b[c] = buffer_load16(xr, off + 16u);
+      } else {
+        const uint32_t off = live ? (uint32_t)m * (uint32_t)p.k + (uint32_t)kb * BLK + 16u * seg
+                                  : BUF_OOB;
+        const uint32_t soff = live ? ((uint32_t)m * (uint32_t)kbn + (uint32_t)kb) * 4u : BUF_OOB;
+        xb[d].a[c] = buffer_load16(xr, off);
+        xb[d].b[c].x = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(sr, soff, 0, 0);
+      }
+    }
+  };
+
+  // Stage K block kb (first tile only): cast or copy into LDS.
+  auto stage_block = [&](int d, int kb) {
+#pragma unroll
+    for (int c = 0; c < XP; ++c) {
+      const int task = 64 * c + lane;
+      const int m = task >> 3, seg = task & 7;
+      if (c > 0 && 64 * c >= 8 * M) break;  // no rows left in this pass (uniform)
+      uint4 codes;
+      float s;
+      if constexpr (FUSED) {
+        const uint32_t w[8] = {xb[d].a[c].x, xb[d].a[c].y, xb[d].a[c].z, xb[d].a[c].w,
+                               xb[d].b[c].x, xb[d].b[c].y, xb[d].b[c].z, xb[d].b[c].w};
+        float x[16];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          x[2 * e] = bf16_lo(w[e]);
+          x[2 * e + 1] = bf16_hi(w[e]);
+        }
+        float am = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) am = __builtin_fmaxf(am, __builtin_fabsf(x[e]));
+        am = octet_max(am);
+        s = am / 448.0f;
+        block_quotients(x, am, s);
+        codes = make_uint4(e4m3x4(x[0], x[1], x[2], x[3]), e4m3x4(x[4], x[5], x[6], x[7]),
+                           e4m3x4(x[8], x[9], x[10], x[11]), e4m3x4(x[12], x[13], x[14], x[15]));
+      } else {
+        codes = xb[d].a[c];
+        s = __uint_as_float(xb[d].b[c].x);
+      }
+      if (m < M) {
+        act[(kb * 8 + seg) * M + m] = codes;
+        if (seg == 0) act_s[kb * M + m] = s;
+      }
+    }
+  };
+
+  // Issue order must match the loop's (item by item) for the wait counts
+  // of the loop to be tight: keep the scheduler from interleaving items.
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    load_item(d, d);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  f32x4 acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int d, int i) {
+    const int t = i / njw, j = i - t * njw;
+    const int kb = wk + j * WK;
+    if (kb < kbn) {
+      if (t == 0) stage_block(d, kb);
+      const int row = r0 + 16 * t;
+      const int row_last = row + 15 < r1 ? row + 15 : r1 - 1;  // last valid row of the tile
+      const int nb_lo = row / BLK, nb_hi = row_last / BLK;
+      const float sw_lo = load_invariant(p.ws, (size_t)nb_lo * (size_t)kbn + kb);
+      const float sw_hi = load_invariant(p.ws, (size_t)nb_hi * (size_t)kbn + kb);
+      const float sw = (row + 4 * g16) / BLK == nb_lo ? sw_lo : sw_hi;
+      const i32x8 aop = tile_operand(wb[d], lo8);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int m = l16 + 16 * mt;
+        i32x8 bop = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+        float sa = 0.0f;
+        if (m < M) {
+          const uint4 lo = act[(kb * 8 + 2 * g16) * M + m];
+          const uint4 hi = act[(kb * 8 + 2 * g16 + 1) * M + m];
+          bop = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                      (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+          sa = act_s[kb * M + m];
+        }
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        const f32x4 pb =
+            __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop, z, 0, 0, 0, 0, 0, 0);
+        const float sc = sa * sw;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[mt][q] = __builtin_fmaf(pb[q], sc, acc[mt][q]);
+      }
+    }
+    if (j == njw - 1) {
+      f32x4* rt = red + (t & 1) * (WK - 1) * MT * 64;
+      if (wk > 0) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) rt[((wk - 1) * MT + mt) * 64 + lane] = acc[mt];
+      }
+      lds_barrier();
+      if (wk == 0) {
+        for (int w = 1; w < WK; ++w)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) acc[mt] += rt[((w - 1) * MT + mt) * 64 + lane];
+        const int rl = 16 * t + 4 * g16;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           const int m = l16 + 16 * mt;
@@ -692,6 +979,8 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_dot_kernel(GemmParams p) {
         if (m < M) {
           if (p.out == OUT_DIRECT)
             p.y[(size_t)m * (size_t)p.n + n] = (uint16_t)bf16_rne(acc[t][m]);
+          else if (p.out == OUT_LAST_ARRIVER)
+            store_coherent(p.part + ((size_t)s * M + m) * (size_t)p.n + n, acc[t][m]);
           else
             p.part[((size_t)s * M + m) * (size_t)p.n + n] = acc[t][m];
         }

@@ -9,7 +9,8 @@
 namespace fp8bs {
 
 struct KernelEntry {
-  int path;    // 1 = MFMA grid, 2 = DOT grid, 3 = MFMA row range (one workgroup per CU)
+  int path;    // 1 = MFMA grid, 2 = DOT grid, 3 = MFMA row range (one workgroup per CU),
+               // 4 = MFMA streaming row range
   int mt;      // MFMA: 16-row activation tiles (1: m <= 16, 2: m <= 32); DOT: max m
   int tn;      // MFMA: 16-row weight tiles per wave; DOT: 8-row groups per wave
   int wn, wk, d;
@@ -48,3 +49,13 @@ struct KernelRegistrar {
   {3, 2, PRE, 1, WK, D, 1, gemm_rows_kernel<2, WK, D, PRE, true>},           \
   {3, 1, PRE, 1, WK, D, 0, gemm_rows_kernel<1, WK, D, PRE, false>},          \
   {3, 2, PRE, 1, WK, D, 0, gemm_rows_kernel<2, WK, D, PRE, false>},
+
+// Streaming row-range kernel: (waves along K, tiles in flight); the entry's
+// mt field holds the staging passes (1: m <= 8, 2: m <= 16, 4: m <= 32).
+#define FP8BS_STREAM_ENTRY(WK, D)                                             \
+  {4, 1, 1, 1, WK, D, 1, gemm_stream_kernel<1, WK, D, true>},                \
+  {4, 2, 1, 1, WK, D, 1, gemm_stream_kernel<2, WK, D, true>},                \
+  {4, 4, 1, 1, WK, D, 1, gemm_stream_kernel<4, WK, D, true>},                \
+  {4, 1, 1, 1, WK, D, 0, gemm_stream_kernel<1, WK, D, false>},               \
+  {4, 2, 1, 1, WK, D, 0, gemm_stream_kernel<2, WK, D, false>},               \
+  {4, 4, 1, 1, WK, D, 0, gemm_stream_kernel<4, WK, D, false>},

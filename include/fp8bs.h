@@ -121,7 +121,13 @@ size_t fp8bs_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k);
 
 /* ---- explicit kernel configuration (tuning and tests) ------------------- */
 
-enum { FP8BS_PATH_AUTO = 0, FP8BS_PATH_MFMA = 1, FP8BS_PATH_DOT = 2, FP8BS_PATH_MFMA_ROWS = 3 };
+enum {
+  FP8BS_PATH_AUTO = 0,
+  FP8BS_PATH_MFMA = 1,
+  FP8BS_PATH_DOT = 2,
+  FP8BS_PATH_MFMA_ROWS = 3,
+  FP8BS_PATH_MFMA_STREAM = 4
+};
 enum { FP8BS_REDUCE_KERNEL = 0, FP8BS_REDUCE_LAST_ARRIVER = 1 };
 
 /* How one GEMM is laid out on the GPU.
@@ -131,7 +137,10 @@ enum { FP8BS_REDUCE_KERNEL = 0, FP8BS_REDUCE_LAST_ARRIVER = 1 };
  *             owning a contiguous range of output columns over the whole K
  *             range; waves_k and depth apply, tiles_n gives how many of
  *             the depth tiles are requested before the activation cast,
- *             waves_n and split_k must be 1)
+ *             waves_n and split_k must be 1), or MFMA_STREAM (the work split
+ *             of MFMA_ROWS without a staging phase: each wave casts the
+ *             activation blocks it uses as the first tile reaches them;
+ *             tiles_n, waves_n and split_k must be 1; needs m*k*2 < 2^31)
  *   tiles_n   MFMA: 16-row tiles per wave (1, 2, 4); DOT: 8-row groups per wave (1, 2, 4)
  *   waves_n   waves side by side along N in one workgroup (1, 2, 4)
  *   waves_k   waves splitting a workgroup's K range (1, 2, 4, 8); their

@@ -19,13 +19,16 @@ TOL = dict(rel=2.0 ** -7, abs_rms=1e-3)
 MFMA_SHAPES = [(1, 1, 8, 5), (1, 1, 8, 2), (1, 1, 8, 4), (1, 1, 4, 5), (1, 1, 4, 8), (1, 2, 4, 5),
                (1, 2, 4, 2), (2, 1, 8, 2), (2, 1, 4, 4), (4, 1, 8, 1), (4, 1, 4, 2), (2, 1, 8, 4),
                (1, 4, 1, 5), (1, 4, 2, 5), (1, 4, 4, 2), (1, 5, 1, 5), (1, 5, 2, 5), (1, 5, 2, 2),
-               (1, 8, 1, 5), (1, 8, 2, 2), (2, 4, 1, 5), (2, 2, 2, 4), (2, 2, 4, 2), (1, 2, 8, 2)]
+               (1, 8, 1, 5), (1, 8, 2, 2), (2, 4, 1, 5), (2, 2, 2, 4), (2, 2, 4, 2), (1, 2, 8, 2),
+               (1, 5, 1, 10), (2, 5, 1, 5), (1, 4, 1, 10)]
 DOT_SHAPES = [(2, 1, 8, 5), (2, 4, 1, 5), (4, 2, 2, 4), (1, 1, 8, 5), (2, 1, 8, 2), (4, 1, 8, 2),
               (2, 2, 4, 4)]
 # (waves along K, tiles in flight, tiles issued before the cast) of the
 # row-range kernel
 ROWS_SHAPES = [(8, 4, 2), (8, 4, 4), (8, 2, 2), (8, 3, 1), (8, 6, 2), (16, 2, 1), (16, 3, 1),
                (4, 8, 2)]
+# (waves along K, tiles in flight) of the streaming row-range kernel
+STREAM_SHAPES = [(8, 4), (8, 2), (8, 6), (16, 2), (16, 3), (4, 8), (16, 5), (8, 8)]
 # (split_k, reduce): no split, second-kernel reduce, last-arriver reduce
 SPLITS = [(1, 0), (3, 0), (4, 1), (5, 1)]
 
@@ -132,6 +135,9 @@ def _configs():
     for (wk, d, pre) in ROWS_SHAPES:
         for m in (1, 5, 8, 16, 17, 32):
             out.append(("rows", (3, pre, 1, wk, d, 1, 0), m))
+    for (wk, d) in STREAM_SHAPES:
+        for m in (1, 5, 8, 9, 16, 17, 32):
+            out.append(("stream", (4, 1, 1, wk, d, 1, 0), m))
     return out
 
 
@@ -188,6 +194,25 @@ def test_row_range_kernel_uneven_ranges(fp8bs, m, n, k, wk, d, pre):
     y = fp8bs.gemm_ex(c, pr.wq, pr.ws, x=pr.x)
     torch.cuda.synchronize()
     _assert_close(host_bits(y), pr.ref, f"rows {wk},{d} m={m} n={n} k={k}")
+    xq, xs = fp8bs.quantize_act(pr.x)
+    y2 = fp8bs.gemm_ex(c, pr.wq, pr.ws, x_q=xq, x_s=xs)
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+
+
+@pytest.mark.parametrize("m,n,k", [(8, 384, 640), (3, 1152, 1920), (12, 2048, 5120),
+                                   (32, 640, 1024), (16, 5120, 2048)])
+@pytest.mark.parametrize("wk,d", STREAM_SHAPES)
+def test_stream_kernel_uneven_ranges(fp8bs, m, n, k, wk, d):
+    """Streaming row-range kernel: short last ranges, partial tiles, K
+    blocks not a multiple of the waves, every staging pass count; the
+    pre-quantized route gives the same bits."""
+    from fp8_block_scaled_fp8bs_amd import GemmConfig
+    pr = _random_problem(fp8bs, m, n, k, 11 * m + n + k + wk + d)
+    c = GemmConfig(4, 1, 1, wk, d)
+    announce("stream", wk, d, "m", m, "n", n, "k", k)
+    y = fp8bs.gemm_ex(c, pr.wq, pr.ws, x=pr.x)
+    torch.cuda.synchronize()
+    _assert_close(host_bits(y), pr.ref, f"stream {wk},{d} m={m} n={n} k={k}")
     xq, xs = fp8bs.quantize_act(pr.x)
     y2 = fp8bs.gemm_ex(c, pr.wq, pr.ws, x_q=xq, x_s=xs)
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
