@@ -108,7 +108,7 @@ const KernelEntry* find_kernel(const fp8bs_gemm_config& c, int m, bool fused) {
   } else {
     return nullptr;
   }
-  const bool rows = is_row_range(c.path);
+  const bool rows = is_row_range(c.path);  // waves_n unused
   for (const KernelEntry& e : kernel_registry())
     if (e.path == c.path && e.mt == mt && e.tn == c.tiles_n && (rows || e.wn == c.waves_n) &&
         e.wk == c.waves_k && e.d == c.depth && e.fused == (int)fused)
@@ -131,18 +131,19 @@ int rows_per_workgroup(int64_t n, int num_cu) {
   return (int)((r + 3) / 4 * 4);
 }
 
-size_t config_lds_bytes(const fp8bs_gemm_config& c, int m, int kbn) {
-  if (c.path == FP8BS_PATH_MFMA_STREAM)
-    return (size_t)lds_stream_bytes(kbn, m, c.waves_k, m <= 16 ? 1 : 2);
-  if (c.path == FP8BS_PATH_MFMA_ROWS) {
-    const int mt = m <= 16 ? 1 : 2;
-    return (size_t)lds_act_bytes(kbn, m) + (size_t)2 * (c.waves_k - 1) * mt * 64 * 16;
+size_t config_lds_bytes(const fp8bs_gemm_config& c, int m, int64_t n, int kbn, int num_cu) {
+  const int mt = m <= 16 ? 1 : 2;
+  if (is_row_range(c.path)) {
+    // weight scales of the row range first, then the kernel's own layout
+    const size_t ws = (size_t)lds_wscale_bytes(rows_per_workgroup(n, num_cu), kbn);
+    if (c.path == FP8BS_PATH_MFMA_STREAM)
+      return ws + (size_t)lds_stream_bytes(kbn, m, c.waves_k, mt);
+    return ws + (size_t)lds_act_bytes(kbn, m) + (size_t)2 * (c.waves_k - 1) * mt * 64 * 16;
   }
   const int nblk = (kbn + c.split_k - 1) / c.split_k;
   size_t red = 0;
   if (c.waves_k > 1) {
     if (c.path == FP8BS_PATH_MFMA) {
-      const int mt = m <= 16 ? 1 : 2;
       red = (size_t)(c.waves_k - 1) * c.waves_n * c.tiles_n * mt * 64 * 16;
     } else {
       const int md = m <= 1 ? 1 : (m <= 2 ? 2 : 4);
@@ -178,6 +179,7 @@ constexpr int MF = FP8BS_PATH_MFMA;
 constexpr int DT = FP8BS_PATH_DOT;
 constexpr int RW = FP8BS_PATH_MFMA_ROWS;
 constexpr int ST = FP8BS_PATH_MFMA_STREAM;
+constexpr int kTableCUs = 256;  // the configuration table assumes a full MI355X
 
 bool candidate_fits(const Candidate& cd, int64_t m, int64_t n, int kbn, fp8bs_gemm_config* out) {
   fp8bs_gemm_config c = make_cfg(cd.path, cd.tn, cd.wn, cd.wk, cd.d, cd.split);
@@ -187,7 +189,7 @@ bool candidate_fits(const Candidate& cd, int64_t m, int64_t n, int kbn, fp8bs_ge
   if (c.split_k > kbn) return false;
   const size_t lds_limit = is_row_range(cd.path) ? kRowsLdsLimit : kAutoLdsLimit;
   if (cd.path == ST && !stream_offsets_fit(m, (int64_t)kbn * BLK)) return false;
-  if (kbn > 0 && config_lds_bytes(c, (int)m, kbn) > lds_limit) return false;
+  if (kbn > 0 && config_lds_bytes(c, (int)m, n, kbn, kTableCUs) > lds_limit) return false;
   *out = c;
   return true;
 }
@@ -210,7 +212,7 @@ bool select_config(int64_t m, int64_t n, int64_t k, fp8bs_gemm_config* out) {
                                    {MF, 1, 1, 4, 5, 4, RK}};
   static const Candidate square[] = {{MF, 1, 2, 4, 5, 1, RK}, {MF, 1, 5, 1, 5, 4, RK},
                                      {RW, 1, 1, 16, 2, 1, RK}};
-  static const Candidate deep[] = {{MF, 1, 5, 2, 2, 4, RK}, {MF, 1, 5, 2, 5, 4, RK},
+  static const Candidate deep[] = {{MF, 1, 5, 2, 5, 4, RK}, {MF, 1, 5, 2, 2, 4, RK},
                                    {MF, 1, 4, 2, 5, 8, RK}};
   static const Candidate fallback[] = {{MF, 1, 1, 4, 5, 1, RK}, {MF, 1, 1, 4, 5, 2, RK},
                                        {MF, 1, 1, 4, 5, 4, RK}, {MF, 1, 1, 4, 5, 8, RK},
@@ -316,7 +318,6 @@ fp8bs_status gemm_impl(const void* x_bf16, const uint8_t* x_fp8, const float* x_
   if (!ke) return FP8BS_ERR_CONFIG;
   const int rows = config_rows(c);
   if (n % rows) return FP8BS_ERR_CONFIG;
-  const size_t lds = config_lds_bytes(c, (int)m, kbn);
   // workspace
   const size_t need = cfg_workspace(c, m, n);
   if (need > 0) {
@@ -327,6 +328,7 @@ fp8bs_status gemm_impl(const void* x_bf16, const uint8_t* x_fp8, const float* x_
   DeviceInfo dev;
   const fp8bs_status st = current_device(&dev);
   if (st != FP8BS_OK) return st;
+  const size_t lds = config_lds_bytes(c, (int)m, n, kbn, dev.num_cu);
   if (lds > (size_t)dev.max_lds) return FP8BS_ERR_CONFIG;
   if (lds > 64 * 1024) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(ke->fn),

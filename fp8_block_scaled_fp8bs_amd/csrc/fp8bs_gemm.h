@@ -59,24 +59,82 @@ __device__ __forceinline__ void split_range(int s, int split, int kbn, int& kb0,
   kb1 = (int)((int64_t)(s + 1) * kbn / split);
 }
 
+// ------------------------------------------------- weight-scale staging ---
+
+// The weight scales a workgroup needs are staged in LDS once, at the start,
+// instead of being read with a dependent scalar load per K block: block rows
+// nbf .. nbf + nbr - 1 (clamped to the matrix), K blocks kb0 .. kb0 + nblk - 1,
+// as wsl[(nb - nbf) * nblk + (kb - kb0)]. The area sits at the start of the
+// workgroup's LDS; its size covers any range of `rows` output columns.
+__host__ __device__ inline int lds_wscale_bytes(int rows, int nblk) {
+  return ((rows / BLK + 2) * nblk * 4 + 15) & ~15;
+}
+
+constexpr int SCALE_REGS = 4;  // scales fetched into registers per thread
+
+struct ScaleFetch {
+  float v[SCALE_REGS];
+};
+
+// Issue the scale loads (the first SCALE_REGS * NT of them into registers,
+// so they are in flight together with the other prologue loads).
+// (Unconditional loads with clamped indices, as for the activations.)
+template <int NT>
+__device__ __forceinline__ void load_wscales(const GemmParams& p, int nbf, int nbr, int kb0,
+                                             int nblk, int tid, ScaleFetch& f) {
+  const int total = nbr * nblk;
+  const int nbn = p.n / BLK;
+#pragma unroll
+  for (int i = 0; i < SCALE_REGS; ++i) {
+    int e = tid + i * NT;
+    e = e < total ? e : total - 1;
+    const int r = e / nblk, kb = e - r * nblk;
+    const int nb = nbf + r < nbn ? nbf + r : nbn - 1;
+    f.v[i] = p.ws[(size_t)nb * (size_t)p.kbn + kb0 + kb];
+  }
+}
+
+// Store the fetched scales to LDS (and fetch any beyond SCALE_REGS * NT
+// directly). The caller's next barrier makes them visible.
+template <int NT>
+__device__ __forceinline__ void store_wscales(const GemmParams& p, int nbf, int nbr, int kb0,
+                                              int nblk, int tid, const ScaleFetch& f, float* wsl) {
+  const int total = nbr * nblk;
+#pragma unroll
+  for (int i = 0; i < SCALE_REGS; ++i) {
+    const int e = tid + i * NT;
+    if (e < total) wsl[e] = f.v[i];
+  }
+  const int nbn = p.n / BLK;
+  for (int e = tid + SCALE_REGS * NT; e < total; e += NT) {
+    const int r = e / nblk, kb = e - r * nblk;
+    const int nb = nbf + r < nbn ? nbf + r : nbn - 1;
+    wsl[e] = p.ws[(size_t)nb * (size_t)p.kbn + kb0 + kb];
+  }
+}
+
 // ---------------------------------------------------- activation staging ---
 
 // Quarter-block g of the workgroup's activation range: block bm = g / 4
-// (bm = kbl * m + row), columns 32 * (g % 4) .. +31 of that block.
+// (bm = kbl * m + row), columns 32 * (g % 4) .. +31 of that block. Indices
+// past G load the last quarter again (unused): the loads are unconditional,
+// so the compiler's wait counts for them stay exact and later loads (the
+// weight prefetch) are never held back behind them. Kernels that serve
+// very different activation sizes pick CR per launch (see the grid kernels)
+// so that few of these loads are redundant.
 template <int NT, int CR>
 __device__ __forceinline__ void load_act_quarters(const GemmParams& p, int kb0, int G, int tid,
                                                   int base, uint4 (&xr)[CR][4]) {
 #pragma unroll
   for (int i = 0; i < CR; ++i) {
-    const int g = base + tid + i * NT;
-    if (g < G) {
-      const int qq = g & 3, bm = g >> 2;
-      const int kbl = bm / p.m, m = bm - kbl * p.m;
-      const uint4* src = reinterpret_cast<const uint4*>(
-          p.x + (size_t)m * (size_t)p.k + (size_t)(kb0 + kbl) * BLK + qq * 32);
+    int g = base + tid + i * NT;
+    g = g < G ? g : G - 1;
+    const int qq = g & 3, bm = g >> 2;
+    const int kbl = bm / p.m, m = bm - kbl * p.m;
+    const uint4* src = reinterpret_cast<const uint4*>(
+        p.x + (size_t)m * (size_t)p.k + (size_t)(kb0 + kbl) * BLK + qq * 32);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) xr[i][j] = src[j];
-    }
+    for (int j = 0; j < 4; ++j) xr[i][j] = src[j];
   }
 }
 
@@ -252,12 +310,11 @@ __device__ __forceinline__ i32x8 tile_operand(const TileLoad& t, bool lo8) {
   return r;
 }
 
-template <int MT, int TN, int WN, int WK, int D, bool FUSED>
-__global__ __launch_bounds__(64 * WN * WK) void gemm_mfma_kernel(GemmParams p) {
+// Body of the grid kernel for CR activation-load rounds per thread.
+template <int MT, int TN, int WN, int WK, int D, bool FUSED, int CR>
+__device__ __forceinline__ void gemm_mfma_body(const GemmParams& p, uint8_t* lds_all) {
   constexpr int NT = 64 * WN * WK;
   constexpr int ROWS = 16 * TN * WN;
-  constexpr int CR = FUSED ? 2 : 1;
-  extern __shared__ __align__(16) uint8_t lds[];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -269,12 +326,12 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_mfma_kernel(GemmParams p) {
   const int nblk = kb1 - kb0;
   const int M = p.m;
 
+  const int n0 = blockIdx.x * ROWS;
+  const int row0 = n0 + wn * 16 * TN;
+  uint8_t* lds = lds_all;
   uint8_t* act = lds;
   float* act_s = reinterpret_cast<float*>(lds + nblk * M * ACT_STRIDE);
   f32x4* red = reinterpret_cast<f32x4*>(lds + lds_act_bytes(nblk, M));
-
-  const int n0 = blockIdx.x * ROWS;
-  const int row0 = n0 + wn * 16 * TN;
   const int l16 = lane & 15, g16 = lane >> 4;
   const int l7 = lane & 7, hb = (lane >> 3) & 1;
   const bool lo8 = hb == 0;
@@ -283,9 +340,13 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_mfma_kernel(GemmParams p) {
   const int nj = nblk > wk ? (nblk - wk + WK - 1) / WK : 0;  // this wave's K blocks
 
   // 1. activation bf16 loads first (so waiting for them does not wait on weights)
+  //    The tail (a loop with its own waits) runs before any other load is
+  //    issued, so the compiler's wait counts for the straight-line loads
+  //    below are exact.
   stage_act_tail<NT, CR, FUSED>(p, kb0, nblk, tid, act, act_s);
   uint4 xr[CR][4];
   if constexpr (FUSED) load_act_quarters<NT, CR>(p, kb0, nblk * M * 4, tid, 0, xr);
+  __builtin_amdgcn_sched_barrier(0);  // activation loads stay ahead of the weight loads
 
   // 2. weight prefetch: D blocks per wave in flight
   TileLoad wb[D][TN];
@@ -305,7 +366,7 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_mfma_kernel(GemmParams p) {
 #pragma unroll
   for (int d = 0; d < PRE; ++d) load_block(d, d);
 
-  // 3. stage activations in LDS
+  // 3. stage activations and weight scales in LDS
   stage_act<NT, CR, FUSED>(p, kb0, nblk, tid, xr, act, act_s);
 #pragma unroll
   for (int d = PRE; d < D; ++d) load_block(d, d);
@@ -414,6 +475,34 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_mfma_kernel(GemmParams p) {
   if (p.out == OUT_LAST_ARRIVER) last_arriver_reduce<NT, ROWS>(p, n0, tid);
 }
 
+// Rounds of activation loads a workgroup needs for its G quarter blocks
+// (1 .. 3; beyond 3 * NT the rest is cast in a loop first). The choice is
+// made once at kernel entry, before any load, so each body is straight-line
+// code whose loads are all needed.
+__device__ __forceinline__ int act_rounds(int G, int NT) {
+  const int r = (G + NT - 1) / NT;
+  return r < 1 ? 1 : (r > 3 ? 3 : r);
+}
+
+template <int MT, int TN, int WN, int WK, int D, bool FUSED>
+__global__ __launch_bounds__(64 * WN * WK) void gemm_mfma_kernel(GemmParams p) {
+  constexpr int NT = 64 * WN * WK;
+  extern __shared__ __align__(16) uint8_t lds_all[];
+  if constexpr (FUSED) {
+    int kb0, kb1;
+    split_range(blockIdx.y, p.split, p.kbn, kb0, kb1);
+    const int rounds = act_rounds((kb1 - kb0) * p.m * 4, NT);
+    if (rounds == 1)
+      gemm_mfma_body<MT, TN, WN, WK, D, true, 1>(p, lds_all);
+    else if (rounds == 2)
+      gemm_mfma_body<MT, TN, WN, WK, D, true, 2>(p, lds_all);
+    else
+      gemm_mfma_body<MT, TN, WN, WK, D, true, 3>(p, lds_all);
+  } else {
+    gemm_mfma_body<MT, TN, WN, WK, D, false, 1>(p, lds_all);
+  }
+}
+
 // ====================================================================
 // MFMA row-range kernel: one workgroup per compute unit. Workgroup g owns
 // the output columns [g*R, g*R + R) (R = rows_per_wg, the last 16-row tile
@@ -431,7 +520,7 @@ template <int MT, int WK, int D, int PRE, bool FUSED>
 __global__ __launch_bounds__(64 * WK) void gemm_rows_kernel(GemmParams p) {
   constexpr int NT = 64 * WK;
   constexpr int CR = FUSED ? 3 : 1;
-  extern __shared__ __align__(16) uint8_t lds[];
+  extern __shared__ __align__(16) uint8_t lds_all[];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -445,6 +534,9 @@ __global__ __launch_bounds__(64 * WK) void gemm_rows_kernel(GemmParams p) {
   const int njw = (kbn + WK - 1) / WK;  // blocks per tile per wave (same for every wave)
   const int nitem = ntile * njw;
 
+  const int nbf = r0 / BLK, nbr = (r1 - 1) / BLK - nbf + 1;
+  float* wsl = reinterpret_cast<float*>(lds_all);
+  uint8_t* lds = lds_all + lds_wscale_bytes(p.rows_per_wg, kbn);
   uint8_t* act = lds;
   float* act_s = reinterpret_cast<float*>(lds + kbn * M * ACT_STRIDE);
   f32x4* red = reinterpret_cast<f32x4*>(lds + lds_act_bytes(kbn, M));
@@ -453,10 +545,15 @@ __global__ __launch_bounds__(64 * WK) void gemm_rows_kernel(GemmParams p) {
   const int l7 = lane & 7, hb = (lane >> 3) & 1;
   const bool lo8 = hb == 0;
 
-  // 1. activations: any quarters beyond CR * NT first, then the first CR * NT
+  // 1. activations beyond the first CR * NT quarters (a loop with its own
+  //    waits, before any other load), then the weight-scale loads and the
+  //    first CR * NT quarters' loads
   stage_act_tail<NT, CR, FUSED>(p, 0, kbn, tid, act, act_s);
+  ScaleFetch sf;
+  load_wscales<NT>(p, nbf, nbr, 0, kbn, tid, sf);
   uint4 xr[CR][4];
   if constexpr (FUSED) load_act_quarters<NT, CR>(p, 0, kbn * M * 4, tid, 0, xr);
+  __builtin_amdgcn_sched_barrier(0);  // activation loads stay ahead of the weight loads
 
   // 2. weight prefetch. Item i = (tile i / njw, block wk + (i % njw) * WK).
   //    Rows past the range and blocks past K are clamped to valid addresses
@@ -497,6 +594,7 @@ __global__ __launch_bounds__(64 * WK) void gemm_rows_kernel(GemmParams p) {
 #pragma unroll
     for (int d = PRE; d < D; ++d) load_item(d, d);
   }
+  store_wscales<NT>(p, nbf, nbr, 0, kbn, tid, sf, wsl);
   lds_barrier();
 
   f32x4 acc[MT];
@@ -509,12 +607,11 @@ __global__ __launch_bounds__(64 * WK) void gemm_rows_kernel(GemmParams p) {
     if (kb < kbn) {
       // A 16-row tile may straddle two 128-row scale blocks (row ranges are
       // multiples of 4, not of 16); each lane's four output rows lie in one.
-      const int row = r0 + 16 * t;
-      const int row_last = row + 15 < r1 ? row + 15 : r1 - 1;  // last valid row of the tile
-      const int nb_lo = row / BLK, nb_hi = row_last / BLK;
-      const float sw_lo = load_invariant(p.ws, (size_t)nb_lo * (size_t)kbn + kb);
-      const float sw_hi = load_invariant(p.ws, (size_t)nb_hi * (size_t)kbn + kb);
-      const float sw = (row + 4 * g16) / BLK == nb_lo ? sw_lo : sw_hi;
+      // this lane's four output rows lie in one 128-row scale block (row
+      // ranges are multiples of 4); lanes past the range read a valid entry
+      int nbl = (r0 + 16 * t + 4 * g16) / BLK - nbf;
+      nbl = nbl < nbr ? nbl : nbr - 1;
+      const float sw = wsl[nbl * kbn + kb];
       const i32x8 aop = tile_operand(wb[d], lo8);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
@@ -643,7 +740,7 @@ struct ActFetch {
 template <int XP, int WK, int D, bool FUSED>
 __global__ __launch_bounds__(64 * WK) void gemm_stream_kernel(GemmParams p) {
   constexpr int MT = XP > 2 ? 2 : 1;  // 16-row activation tiles of the MFMA B operand
-  extern __shared__ __align__(16) uint8_t lds[];
+  extern __shared__ __align__(16) uint8_t lds_all[];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -657,6 +754,9 @@ __global__ __launch_bounds__(64 * WK) void gemm_stream_kernel(GemmParams p) {
   const int njw = (kbn + WK - 1) / WK;  // blocks per tile per wave (same for every wave)
   const int nitem = ntile * njw;
 
+  const int nbf = r0 / BLK, nbr = (r1 - 1) / BLK - nbf + 1;
+  float* wsl = reinterpret_cast<float*>(lds_all);
+  uint8_t* lds = lds_all + lds_wscale_bytes(p.rows_per_wg, kbn);
   uint4* act = reinterpret_cast<uint4*>(lds);                     // [kbn][8][M] chunks
   float* act_s = reinterpret_cast<float*>(lds + kbn * M * BLK);    // [kbn][M]
   f32x4* red = reinterpret_cast<f32x4*>(lds + kbn * M * BLK + ((kbn * M * 4 + 15) & ~15));
@@ -742,6 +842,9 @@ __global__ __launch_bounds__(64 * WK) void gemm_stream_kernel(GemmParams p) {
     }
   };
 
+  ScaleFetch sf;
+  load_wscales<64 * WK>(p, nbf, nbr, 0, kbn, tid, sf);
+  __builtin_amdgcn_sched_barrier(0);
   // Issue order must match the loop's (item by item) for the wait counts
   // of the loop to be tight: keep the scheduler from interleaving items.
 #pragma unroll
@@ -749,6 +852,8 @@ __global__ __launch_bounds__(64 * WK) void gemm_stream_kernel(GemmParams p) {
     load_item(d, d);
     __builtin_amdgcn_sched_barrier(0);
   }
+  store_wscales<64 * WK>(p, nbf, nbr, 0, kbn, tid, sf, wsl);
+  lds_barrier();
 
   f32x4 acc[MT];
 #pragma unroll
@@ -759,12 +864,11 @@ __global__ __launch_bounds__(64 * WK) void gemm_stream_kernel(GemmParams p) {
     const int kb = wk + j * WK;
     if (kb < kbn) {
       if (t == 0) stage_block(d, kb);
-      const int row = r0 + 16 * t;
-      const int row_last = row + 15 < r1 ? row + 15 : r1 - 1;  // last valid row of the tile
-      const int nb_lo = row / BLK, nb_hi = row_last / BLK;
-      const float sw_lo = load_invariant(p.ws, (size_t)nb_lo * (size_t)kbn + kb);
-      const float sw_hi = load_invariant(p.ws, (size_t)nb_hi * (size_t)kbn + kb);
-      const float sw = (row + 4 * g16) / BLK == nb_lo ? sw_lo : sw_hi;
+      // this lane's four output rows lie in one 128-row scale block (row
+      // ranges are multiples of 4); lanes past the range read a valid entry
+      int nbl = (r0 + 16 * t + 4 * g16) / BLK - nbf;
+      nbl = nbl < nbr ? nbl : nbr - 1;
+      const float sw = wsl[nbl * kbn + kb];
       const i32x8 aop = tile_operand(wb[d], lo8);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
@@ -836,12 +940,11 @@ __global__ __launch_bounds__(64 * WK) void gemm_stream_kernel(GemmParams p) {
 // xs * ws; the 8 lanes of a row are summed once at the end.
 // ====================================================================
 
-template <int MD, int RT, int WN, int WK, int D, bool FUSED>
-__global__ __launch_bounds__(64 * WN * WK) void gemm_dot_kernel(GemmParams p) {
+// Body of the DOT kernel for CR activation-load rounds per thread.
+template <int MD, int RT, int WN, int WK, int D, bool FUSED, int CR>
+__device__ __forceinline__ void gemm_dot_body(const GemmParams& p, uint8_t* lds_all) {
   constexpr int NT = 64 * WN * WK;
   constexpr int ROWS = 8 * RT * WN;
-  constexpr int CR = FUSED ? 2 : 1;
-  extern __shared__ __align__(16) uint8_t lds[];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -853,11 +956,11 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_dot_kernel(GemmParams p) {
   const int nblk = kb1 - kb0;
   const int M = p.m;
 
+  const int n0 = blockIdx.x * ROWS;
+  uint8_t* lds = lds_all;
   uint8_t* act = lds;
   float* act_s = reinterpret_cast<float*>(lds + nblk * M * ACT_STRIDE);
   float* red = reinterpret_cast<float*>(lds + lds_act_bytes(nblk, M));
-
-  const int n0 = blockIdx.x * ROWS;
   const int row0 = n0 + wn * 8 * RT;
   const int r8 = lane >> 3, seg = lane & 7;
   const uint8_t* wrow = p.wq + (size_t)(row0 + r8) * (size_t)p.k + 16 * seg;
@@ -866,6 +969,7 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_dot_kernel(GemmParams p) {
   stage_act_tail<NT, CR, FUSED>(p, kb0, nblk, tid, act, act_s);
   uint4 xr[CR][4];
   if constexpr (FUSED) load_act_quarters<NT, CR>(p, kb0, nblk * M * 4, tid, 0, xr);
+  __builtin_amdgcn_sched_barrier(0);  // activation loads stay ahead of the weight loads
 
   uint4 wb[D][RT];
   auto load_block = [&](int d, int j) {
@@ -911,8 +1015,7 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_dot_kernel(GemmParams p) {
         sa[m] = 0.0f;
       }
     }
-    const int nb = row0 / BLK;
-    const float sw = load_invariant(p.ws, (size_t)nb * (size_t)p.kbn + kb);
+    const float sw = load_invariant(p.ws, (size_t)(row0 / BLK) * (size_t)p.kbn + kb);
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       const uint32_t ww[4] = {wb[d][t].x, wb[d][t].y, wb[d][t].z, wb[d][t].w};
@@ -988,6 +1091,25 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_dot_kernel(GemmParams p) {
     }
   }
   if (p.out == OUT_LAST_ARRIVER) last_arriver_reduce<NT, ROWS>(p, n0, tid);
+}
+
+template <int MD, int RT, int WN, int WK, int D, bool FUSED>
+__global__ __launch_bounds__(64 * WN * WK) void gemm_dot_kernel(GemmParams p) {
+  constexpr int NT = 64 * WN * WK;
+  extern __shared__ __align__(16) uint8_t lds_all[];
+  if constexpr (FUSED) {
+    int kb0, kb1;
+    split_range(blockIdx.y, p.split, p.kbn, kb0, kb1);
+    const int rounds = act_rounds((kb1 - kb0) * p.m * 4, NT);
+    if (rounds == 1)
+      gemm_dot_body<MD, RT, WN, WK, D, true, 1>(p, lds_all);
+    else if (rounds == 2)
+      gemm_dot_body<MD, RT, WN, WK, D, true, 2>(p, lds_all);
+    else
+      gemm_dot_body<MD, RT, WN, WK, D, true, 3>(p, lds_all);
+  } else {
+    gemm_dot_body<MD, RT, WN, WK, D, false, 1>(p, lds_all);
+  }
 }
 
 }  // namespace fp8bs

@@ -59,3 +59,4 @@ struct KernelRegistrar {
   {4, 1, 1, 1, WK, D, 0, gemm_stream_kernel<1, WK, D, false>},               \
   {4, 2, 1, 1, WK, D, 0, gemm_stream_kernel<2, WK, D, false>},               \
   {4, 4, 1, 1, WK, D, 0, gemm_stream_kernel<4, WK, D, false>},
+
