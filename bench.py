@@ -108,6 +108,82 @@ def cpu_baseline(workload, m: int, budget_s: float) -> dict:
     }
 
 
+def step_mix(args, fp8bs, dev) -> int:
+    """Decode-step mix: 256 GEMMs drawn from the square, MLP-up, MLP-down and
+    vocabulary shapes in a fixed seeded order, run back to back on one
+    stream as one captured HIP graph per M. Each shape cycles through its own
+    pool of distinct quantized weights (at least --pool-gib GiB, or one
+    weight when a single weight is larger), so no weight is served from the
+    Infinity Cache. Reports microseconds per step and aggregate algorithmic
+    GB/s, with per-shape subtotals of the bytes."""
+    import torch
+
+    from workloads import STEP_SHAPES, WORKLOADS, step_order
+
+    order = step_order(256, 0)
+    pools = {}
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1400)
+    for name in STEP_SHAPES:
+        wl = WORKLOADS[name]
+        count = max(1, math.ceil(args.pool_gib * (1 << 30) / (wl.n * wl.k)))
+        pool = []
+        for _ in range(count):
+            w = (torch.randn((wl.n, wl.k), generator=gen, device=dev, dtype=torch.float32) * 0.02).to(torch.bfloat16)
+            pool.append(fp8bs.quantize_weight(w))
+            del w
+        pools[name] = pool
+    torch.cuda.synchronize()
+    for m in [int(v) for v in args.step_m.split(",")]:
+        xs = {name: torch.randn((m, WORKLOADS[name].k), generator=gen, device=dev,
+                                dtype=torch.float32).to(torch.bfloat16) for name in STEP_SHAPES}
+        ys = {name: torch.empty((m, WORKLOADS[name].n), dtype=torch.bfloat16, device=dev)
+              for name in STEP_SHAPES}
+        ws_bytes = max(fp8bs.workspace_bytes(m, WORKLOADS[nm].n, WORKLOADS[nm].k) for nm in STEP_SHAPES)
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+        cursor = {name: 0 for name in STEP_SHAPES}
+
+        def one_step():
+            for name in order:
+                pool = pools[name]
+                wq, wsc = pool[cursor[name] % len(pool)]
+                cursor[name] += 1
+                fp8bs.gemm(xs[name], wq, wsc, out=ys[name], workspace=workspace)
+
+        for _ in range(2):
+            one_step()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                one_step()
+        stream.wait_stream(cap)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = max(1, args.steps // 40)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        by_shape = {name: order.count(name) * WORKLOADS[name].algorithmic_bytes(m) for name in STEP_SHAPES}
+        total = sum(by_shape.values())
+        print(json.dumps({
+            "mode": "step_mix", "m": m, "gemms_per_step": len(order),
+            "counts": {name: order.count(name) for name in STEP_SHAPES},
+            "us_per_step": round(us, 1), "algorithmic_bytes_per_step": total,
+            "GBps": round(total / (us * 1e3), 1), "pct_of_8TBps": round(100 * total / (us * 1e3) / HBM_PEAK_GBPS, 2),
+            "bytes_by_shape": by_shape, "replays": reps,
+            "timing": "one captured HIP graph of the 256-GEMM step, replayed"}), flush=True)
+        del xs, ys, workspace, g
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -121,6 +197,10 @@ def main() -> int:
     ap.add_argument("--eager-only", action="store_true", help="time stream launches only")
     ap.add_argument("--diag-copy-mib", type=int, default=0,
                     help="run only the plain copy kernel over this many MiB (counter calibration)")
+    ap.add_argument("--step-mix", action="store_true",
+                    help="decode-step mix: 256 GEMMs over the four shapes per step, at every M; "
+                         "prints one JSON line per M")
+    ap.add_argument("--step-m", default="1,2,4,8,16,32", help="M values of the step mix")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -140,6 +220,9 @@ def main() -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     fp8bs.load()
+
+    if args.step_mix:
+        return step_mix(args, fp8bs, dev)
 
     if args.diag_copy_mib:
         nbytes = args.diag_copy_mib << 20

@@ -153,8 +153,7 @@ size_t config_lds_bytes(const fp8bs_gemm_config& c, int m, int64_t n, int kbn, i
   return (size_t)lds_act_bytes(nblk, m) + red;
 }
 
-constexpr size_t kAutoLdsLimit = 96 * 1024;    // grid kernels: room for two workgroups per CU
-constexpr size_t kRowsLdsLimit = 160 * 1024;   // row-range kernel: one workgroup per CU
+constexpr size_t kLdsLimit = 160 * 1024;  // one workgroup per CU at most
 
 fp8bs_gemm_config make_cfg(int path, int tn, int wn, int wk, int d, int split) {
   fp8bs_gemm_config c;
@@ -187,65 +186,75 @@ bool candidate_fits(const Candidate& cd, int64_t m, int64_t n, int kbn, fp8bs_ge
   if (n % config_rows(c) != 0) return false;
   if (cd.path == DT && m > 4) return false;
   if (c.split_k > kbn) return false;
-  const size_t lds_limit = is_row_range(cd.path) ? kRowsLdsLimit : kAutoLdsLimit;
   if (cd.path == ST && !stream_offsets_fit(m, (int64_t)kbn * BLK)) return false;
-  if (kbn > 0 && config_lds_bytes(c, (int)m, n, kbn, kTableCUs) > lds_limit) return false;
+  if (kbn > 0 && config_lds_bytes(c, (int)m, n, kbn, kTableCUs) > kLdsLimit) return false;
   *out = c;
   return true;
 }
 
 // The fixed configuration table. A pure function of (m, n, k): no timing,
 // no device state, so a shape always runs the same kernel and gives the
-// same bits. Each regime lists candidates in order of preference; the first
-// one that fits the shape (rows dividing n, split not above the number of K
-// blocks, staged activations within the LDS budget) is used.
+// same bits. Shapes fall in four classes by their extents (square-like,
+// deep K, wide N, vocabulary-wide N) and six classes of m; each cell lists
+// candidates in order of preference, measured on MI355X with graph-replayed
+// launches over a rotating 1 GiB weight pool. The first candidate that fits
+// the shape (rows dividing n, split not above the number of K blocks,
+// staged activations within the LDS budget) is used; a fallback list with
+// growing split catches everything else.
 bool select_config(int64_t m, int64_t n, int64_t k, fp8bs_gemm_config* out) {
   if (m < 0 || m > 32 || n < 0 || k < 0 || n % BLK || k % BLK) return false;
   const int kbn = (int)(k / BLK);
   const int64_t nbn = n / BLK;
-  static const Candidate small_m_wide[] = {{DT, 2, 4, 1, 5, 1, RK}, {DT, 2, 1, 8, 5, 1, RK}};
-  static const Candidate small_m[] = {{DT, 2, 2, 4, 4, 1, RK}, {DT, 2, 1, 8, 5, 1, RK},
-                                      {DT, 1, 1, 8, 5, 1, RK}};
-  static const Candidate vocab[] = {{ST, 1, 1, 8, 6, 1, RK}, {RW, 2, 1, 8, 6, 1, RK},
-                                    {MF, 1, 1, 8, 5, 1, RK}, {MF, 1, 1, 8, 5, 2, RK}};
-  static const Candidate wide[] = {{RW, 2, 1, 8, 6, 1, RK}, {RW, 1, 1, 16, 3, 1, RK},
-                                   {MF, 1, 1, 4, 5, 4, RK}};
-  static const Candidate square[] = {{MF, 1, 2, 4, 5, 1, RK}, {MF, 1, 5, 1, 5, 4, RK},
-                                     {RW, 1, 1, 16, 2, 1, RK}};
-  static const Candidate deep[] = {{MF, 1, 5, 2, 5, 4, RK}, {MF, 1, 5, 2, 2, 4, RK},
-                                   {MF, 1, 4, 2, 5, 8, RK}};
-  static const Candidate fallback[] = {{MF, 1, 1, 4, 5, 1, RK}, {MF, 1, 1, 4, 5, 2, RK},
-                                       {MF, 1, 1, 4, 5, 4, RK}, {MF, 1, 1, 4, 5, 8, RK},
-                                       {MF, 1, 1, 4, 5, 16, RK}, {MF, 1, 1, 4, 5, 32, RK},
-                                       {MF, 1, 1, 4, 5, 64, RK}};
-  struct List {
-    const Candidate* c;
-    int n;
-  };
-  List lists[2];
-  int nl = 0;
-#define FP8BS_LIST(a) lists[nl++] = List{a, (int)(sizeof(a) / sizeof(a[0]))}
-  if (m <= 2 && nbn >= 256)
-    FP8BS_LIST(small_m_wide);
-  else if (m <= 2)
-    FP8BS_LIST(small_m);
-  else if (nbn >= 512)
-    FP8BS_LIST(vocab);
-  else if (nbn >= 200)
-    FP8BS_LIST(wide);
-  else if (kbn <= 48)
-    FP8BS_LIST(square);
-  else
-    FP8BS_LIST(deep);
-  FP8BS_LIST(fallback);
-#undef FP8BS_LIST
   if (m == 0 || n == 0 || kbn == 0) {
     *out = make_cfg(MF, 1, 1, 4, 5, 1);
     return true;
   }
-  for (int l = 0; l < nl; ++l)
-    for (int i = 0; i < lists[l].n; ++i)
-      if (candidate_fits(lists[l].c[i], m, n, kbn, out)) return true;
+  struct Cell {
+    Candidate c[3];
+    int n;
+  };
+  // [shape class][m class]: m = 1, 2, 3-4, 5-8, 9-16, 17-32; each candidate
+  // is {path, tiles_n, waves_n, waves_k, depth, split_k, reduce}
+  static const Cell table[4][6] = {
+      // square-like: n < 25600, k <= 6144
+      {{{{DT, 2, 2, 4, 4, 1, RK}, {MF, 1, 2, 4, 5, 1, RK}}, 2},
+       {{{MF, 1, 2, 4, 5, 1, RK}}, 1},
+       {{{MF, 1, 2, 4, 5, 1, RK}, {MF, 1, 5, 1, 5, 4, RK}}, 2},
+       {{{MF, 1, 2, 4, 5, 1, RK}, {MF, 1, 5, 1, 5, 4, RK}}, 2},
+       {{{MF, 1, 5, 1, 5, 4, RK}, {MF, 1, 5, 2, 5, 4, RK}}, 2},
+       {{{MF, 1, 5, 2, 5, 4, RK}, {MF, 1, 8, 1, 5, 4, RK}}, 2}},
+      // deep K: n < 25600, k > 6144
+      {{{{DT, 2, 2, 4, 4, 1, RK}, {MF, 1, 5, 2, 2, 4, RK}}, 2},
+       {{{MF, 1, 5, 1, 5, 4, RK}, {MF, 1, 5, 2, 2, 4, RK}}, 2},
+       {{{MF, 1, 5, 1, 5, 4, RK}, {MF, 1, 5, 2, 2, 4, RK}}, 2},
+       {{{MF, 1, 5, 2, 5, 4, RK}, {MF, 1, 5, 2, 2, 4, RK}}, 2},
+       {{{MF, 1, 5, 2, 5, 4, RK}, {MF, 2, 5, 1, 5, 8, RK}}, 2},
+       {{{MF, 2, 5, 1, 5, 8, RK}, {MF, 1, 5, 2, 5, 8, RK}}, 2}},
+      // wide N: 25600 <= n < 65536
+      {{{{MF, 1, 1, 4, 5, 1, RK}, {MF, 1, 1, 8, 5, 1, RK}}, 2},
+       {{{RW, 4, 1, 8, 4, 1, RK}, {RW, 1, 1, 8, 3, 1, RK}}, 2},
+       {{{RW, 1, 1, 8, 3, 1, RK}, {RW, 2, 1, 8, 6, 1, RK}}, 2},
+       {{{RW, 2, 1, 8, 6, 1, RK}, {RW, 1, 1, 8, 3, 1, RK}}, 2},
+       {{{RW, 4, 1, 8, 4, 1, RK}, {RW, 2, 1, 8, 6, 1, RK}}, 2},
+       {{{MF, 1, 8, 1, 5, 4, RK}, {MF, 1, 4, 1, 5, 4, RK}}, 2}},
+      // vocabulary-wide N: n >= 65536
+      {{{{MF, 1, 2, 4, 2, 1, RK}, {MF, 1, 2, 4, 5, 1, RK}}, 2},
+       {{{MF, 1, 2, 4, 5, 1, RK}, {MF, 1, 1, 8, 5, 1, RK}}, 2},
+       {{{MF, 4, 1, 4, 2, 1, RK}, {MF, 1, 8, 1, 5, 1, RK}}, 2},
+       {{{ST, 1, 1, 8, 6, 1, RK}, {RW, 2, 1, 8, 6, 1, RK}}, 2},
+       {{{RW, 1, 1, 8, 3, 1, RK}, {RW, 2, 1, 8, 6, 1, RK}}, 2},
+       {{{MF, 1, 8, 1, 5, 2, RK}, {MF, 1, 8, 2, 2, 2, RK}}, 2}}};
+  static const Candidate fallback[] = {{MF, 1, 1, 4, 5, 1, RK}, {MF, 1, 1, 4, 5, 2, RK},
+                                       {MF, 1, 1, 4, 5, 4, RK}, {MF, 1, 1, 4, 5, 8, RK},
+                                       {MF, 1, 1, 4, 5, 16, RK}, {MF, 1, 1, 4, 5, 32, RK},
+                                       {MF, 1, 1, 4, 5, 64, RK}};
+  const int shape = nbn >= 512 ? 3 : (nbn >= 200 ? 2 : (kbn > 48 ? 1 : 0));
+  const int mc = m == 1 ? 0 : (m == 2 ? 1 : (m <= 4 ? 2 : (m <= 8 ? 3 : (m <= 16 ? 4 : 5))));
+  const Cell& cell = table[shape][mc];
+  for (int i = 0; i < cell.n; ++i)
+    if (candidate_fits(cell.c[i], m, n, kbn, out)) return true;
+  for (const Candidate& cd : fallback)
+    if (candidate_fits(cd, m, n, kbn, out)) return true;
   return false;
 }
 
