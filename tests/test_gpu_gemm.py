@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 from gpu_util import announce, dev_bf16, dev_f32, dev_u8, host_bits, need_gpu, same_bits_f32, torch
-from workloads import WORKLOADS, bf16_from_f32, weight_rows_bf16
+from workloads import WORKLOADS, act_bf16, bf16_from_f32, weight_rows_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -76,15 +76,46 @@ def _random_problem(fp8bs, m, n, k, seed):
     return Problem(fp8bs, w, bf16_from_f32(x))
 
 
-@pytest.mark.parametrize("name,m", [("tiny", 8), ("square", 1), ("square", 8),
-                                    ("mlp_up", 8), ("mlp_down", 8)])
-def test_workload_parity_full_output(fp8bs, name, m):
-    wl = WORKLOADS[name]
-    announce("gemm parity", name, "m", m, "cfg", fp8bs.select_config(m, wl.n, wl.k))
-    pr = Problem(fp8bs, wl.weight(), wl.act(m))
+def test_tiny_workload_parity_full_output(fp8bs):
+    wl = WORKLOADS["tiny"]
+    announce("gemm parity tiny m 8 cfg", fp8bs.select_config(8, wl.n, wl.k))
+    pr = Problem(fp8bs, wl.weight(), wl.act(8))
     y = fp8bs.gemm(pr.x, pr.wq, pr.ws)
     torch.cuda.synchronize()
-    _assert_close(host_bits(y), pr.ref, f"{name} m={m}")
+    _assert_close(host_bits(y), pr.ref, "tiny m=8")
+
+
+@pytest.fixture(scope="module")
+def full_problems(fp8bs):
+    """Seeded full-size weights of the square and MLP shapes (quantized on
+    the GPU, bit-checked against the oracle once) and their activations at
+    the largest M of the step mix."""
+    out = {}
+    for name in ("square", "mlp_up", "mlp_down"):
+        wl = WORKLOADS[name]
+        announce("full-size weight", name, wl.n, wl.k)
+        w_bits = wl.weight()
+        x_bits = act_bf16(wl.x_seed, wl.col_seed, 32, wl.k, wl.n_outlier, wl.outlier_factor)
+        out[name] = Problem(fp8bs, w_bits, x_bits)
+        torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("name", ["square", "mlp_up", "mlp_down"])
+@pytest.mark.parametrize("m", [1, 2, 4, 8, 16, 32])
+def test_step_mix_shapes_every_m(fp8bs, full_problems, name, m):
+    """Every full-size GEMM shape of the decode-step mix (the square, MLP-up
+    and MLP-down workloads with their seeded weights and activations) at
+    every M it runs at, in the configuration the library picks for it (the
+    one the benches time): full output within tolerance of the oracle."""
+    pr = full_problems[name]
+    cfg = fp8bs.select_config(m, pr.w_bits.shape[0], pr.w_bits.shape[1])
+    announce("step-mix shape", name, "m", m, "cfg", cfg)
+    x = pr.x[:m].contiguous()
+    y = fp8bs.gemm(x, pr.wq, pr.ws)
+    torch.cuda.synchronize()
+    ref = oracle.gemm_ref(pr.xq_ref[:m], pr.xs_ref[:m], pr.wq_ref, pr.ws_ref)
+    _assert_close(host_bits(y), ref, f"{name} m={m} {cfg}")
 
 
 @pytest.fixture(scope="module")
@@ -98,7 +129,7 @@ def vocab_weight(fp8bs):
     return wq, ws
 
 
-@pytest.mark.parametrize("m", [1, 8, 16])
+@pytest.mark.parametrize("m", [1, 2, 4, 8, 16, 32])
 def test_vocab_parity_sampled_columns(fp8bs, vocab_weight, m):
     """The 248,320-wide output layer at its full size, in the launch
     configuration the library picks; sampled block rows of W are regenerated
@@ -107,7 +138,7 @@ def test_vocab_parity_sampled_columns(fp8bs, vocab_weight, m):
     wl = WORKLOADS["vocab"]
     announce("gemm vocab", "m", m, "cfg", fp8bs.select_config(m, wl.n, wl.k))
     wq, ws = vocab_weight
-    x_bits = wl.act(m)
+    x_bits = act_bf16(wl.x_seed, wl.col_seed, 32, wl.k, wl.n_outlier, wl.outlier_factor)[:m]
     y = host_bits(fp8bs.gemm(dev_bf16(x_bits), wq, ws))
     xq, xs = oracle.quantize_act_ref(x_bits)
     nbn = wl.n // 128
