@@ -34,6 +34,22 @@ What it computes, and where the pages say so:
   sum over blocks rounds.
 
 The reference result is kept in fp64 and never rounded to bf16.
+
+MLP epilogue (the step after the up/gate projection):
+
+* SwiGLU fused onto the multiply's output, and the 1 x 128 FP8 cast of its
+  result that feeds the down projection ("Kernel-Level Optimisations for LLM
+  Inference and Training", section "Scheduling decides the shapes your
+  kernels see", its paragraph on fusion; the cast's cost as in "The profiler
+  said the kernel ran zero times", section "What the trace showed"). The
+  pages name SwiGLU without defining it; the definition used is the
+  published gated unit (Shazeer, "GLU Variants Improve Transformer", 2020):
+  h = silu(gate) * up, silu(g) = g * sigmoid(g) = g / (1 + e^-g).
+* Readings the pages leave open: the fused up/gate output holds the gate in
+  its first n/2 columns and the up projection in the last n/2; gate and up
+  are the GEMM's bf16 outputs; h is rounded once to bf16 (the element type
+  an unfused SwiGLU step would hand on) and then cast with the activation
+  rule above. Here h is evaluated in fp64 and rounded to bf16 in one step.
 """
 from __future__ import annotations
 
@@ -54,6 +70,10 @@ __all__ = [
     "tolerance_report",
     "within_tolerance",
     "unquantized_gemm_ref",
+    "bf16_bits_from_f64",
+    "silu_ref",
+    "swiglu_ref",
+    "swiglu_quant_ref",
 ]
 
 E4M3_MAX = 448.0
@@ -254,3 +274,58 @@ def tolerance_report(y_bf16: np.ndarray, ref: np.ndarray,
 def within_tolerance(y_bf16: np.ndarray, ref: np.ndarray, **kw) -> bool:
     r = tolerance_report(y_bf16, ref, **kw)
     return r["finite"] and r["n_bad"] == 0
+
+
+# ---------------------------------------------------------------------------
+# MLP epilogue: SwiGLU and the re-quantization of its output
+# ---------------------------------------------------------------------------
+
+BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
+
+
+def bf16_bits_from_f64(v: np.ndarray) -> np.ndarray:
+    """Round fp64 values to bf16 in one step (nearest, ties to even mantissa);
+    returns uint16 bit patterns.
+
+    bf16 keeps 8 significant bits with fp32's exponent range: a value whose
+    leading bit has weight 2^e is rounded to a multiple of 2^(e-7), and values
+    below 2^-126 to multiples of 2^-133 (subnormals). Magnitudes that round
+    past the largest finite value become infinity; zero keeps its sign.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    _, e = np.frexp(a)                      # a = f * 2^e, 0.5 <= f < 1 (e = 0 for a = 0)
+    qexp = np.maximum(e.astype(np.int64) - 8, -133)
+    r = np.rint(np.ldexp(a, -qexp))         # exact scaling; rint rounds ties to even
+    mag = np.ldexp(r, qexp)
+    mag = np.where(mag > BF16_MAX, np.inf, mag)
+    out = np.copysign(mag, v).astype(np.float32)   # exact: bf16 values are fp32 values
+    return (out.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def silu_ref(g: np.ndarray) -> np.ndarray:
+    """silu(g) = g / (1 + e^-g) in fp64 (e^-g overflows to inf for very
+    negative g, giving a zero with the sign of g)."""
+    g = np.asarray(g, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g))
+
+
+def swiglu_ref(y_bf16: np.ndarray) -> np.ndarray:
+    """h[m][j] = silu(gate[m][j]) * up[m][j] in fp64, from the bf16 bits of
+    the up/gate output y[m][2I]: gate = y[:, :I], up = y[:, I:]."""
+    y = np.asarray(y_bf16, dtype=np.uint16)
+    m, n2 = y.shape
+    if n2 % 2:
+        raise ValueError("the up/gate output must have an even number of columns")
+    inter = n2 // 2
+    yf = bf16_bits_to_f32(y).astype(np.float64)
+    return silu_ref(yf[:, :inter]) * yf[:, inter:]
+
+
+def swiglu_quant_ref(y_bf16: np.ndarray):
+    """y[m][2I] bf16 bits -> (h bf16 bits [m][I], codes uint8 [m][I], scales
+    fp32 [m][I/128]): SwiGLU, one rounding to bf16, then the 1 x 128 cast."""
+    hb = bf16_bits_from_f64(swiglu_ref(y_bf16))
+    codes, scales = quantize_act_ref(hb)
+    return hb, codes, scales
