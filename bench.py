@@ -184,6 +184,96 @@ def step_mix(args, fp8bs, dev) -> int:
     return 0
 
 
+def mlp_swiglu(args, fp8bs, dev) -> int:
+    """MLP up/gate projection with the SwiGLU epilogue and the FP8 cast of its
+    output (one fp8bs_gemm_swiglu call), at every M of the step mix, on the
+    5120 -> 34816 shape (inter 17408) with a rotating weight pool of at least
+    --pool-gib GiB. Timed beside it, with the same launches in captured
+    graphs: the plain GEMM alone, the GEMM followed by the standalone
+    epilogue call, and the epilogue inside the GEMM launch. One JSON line per
+    M. Algorithmic bytes of the fused call: weight codes and scales, bf16 X,
+    bf16 y (gate and up), h codes and h scales."""
+    import dataclasses
+
+    import torch
+
+    from workloads import WORKLOADS
+
+    wl = WORKLOADS["mlp_up"]
+    n, k = wl.n, wl.k
+    inter = n // 2
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1500)
+    count = max(1, math.ceil(args.pool_gib * (1 << 30) / (n * k)))
+    pool = []
+    for _ in range(count):
+        w = (torch.randn((n, k), generator=gen, device=dev, dtype=torch.float32) * 0.02).to(torch.bfloat16)
+        pool.append(fp8bs.quantize_weight(w))
+        del w
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, steps):
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                for i in range(steps):
+                    fn(i)
+        stream.wait_stream(cap)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        best = float("inf")
+        for _ in range(3):
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) * 1e3 / steps)
+        return best
+
+    steps = max(10, min(100, args.steps // 4))
+    for m in [int(v) for v in args.step_m.split(",")]:
+        x = torch.randn((m, k), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        hq = torch.empty((m, inter), dtype=torch.uint8, device=dev)
+        hs = torch.empty((m, inter // 128), dtype=torch.float32, device=dev)
+        cfg = fp8bs.swiglu_select_config(m, n, k)
+        inside = dataclasses.replace(cfg, epilogue=fp8bs.EPILOGUE_IN_GEMM) if cfg.split_k == 1 else None
+        ws_bytes = max(fp8bs.swiglu_workspace_bytes(m, n, k, c) for c in (cfg, inside) if c)
+        work = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+        P = len(pool)
+        fused = timed(lambda i: fp8bs.gemm_swiglu(x, pool[i % P][0], pool[i % P][1], out=y,
+                                                  h=(hq, hs), workspace=work), steps)
+        plain = timed(lambda i: fp8bs.gemm(x, pool[i % P][0], pool[i % P][1], out=y,
+                                           workspace=work), steps)
+        two = timed(lambda i: (fp8bs.gemm(x, pool[i % P][0], pool[i % P][1], out=y, workspace=work),
+                               fp8bs.swiglu_quant(y, h=(hq, hs))), steps)
+        in_gemm = (timed(lambda i: fp8bs.gemm_swiglu_ex(inside, pool[i % P][0], pool[i % P][1], x=x,
+                                                        out=y, h=(hq, hs), workspace=work), steps)
+                   if inside is not None else None)
+        nbytes = (n * k + 4 * (n // 128) * (k // 128) + 2 * m * k + 2 * m * n + m * inter
+                  + 4 * m * (inter // 128))
+        print(json.dumps({
+            "mode": "mlp_swiglu", "m": m, "n": n, "k": k, "inter": inter,
+            "config": dataclasses.asdict(cfg),
+            "us_fused_call": round(fused, 3), "GBps": round(nbytes / (fused * 1e3), 1),
+            "pct_of_8TBps": round(100 * nbytes / (fused * 1e3) / HBM_PEAK_GBPS, 2),
+            "algorithmic_bytes": nbytes,
+            "us_plain_gemm": round(plain, 3),
+            "us_gemm_then_epilogue_call": round(two, 3),
+            "us_epilogue_in_gemm": round(in_gemm, 3) if in_gemm is not None else None,
+            "timing": f"captured graph of {steps} calls over a {P}-weight pool, best of 3 replays"}),
+            flush=True)
+        del x, y, hq, hs, work
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -201,6 +291,9 @@ def main() -> int:
                     help="decode-step mix: 256 GEMMs over the four shapes per step, at every M; "
                          "prints one JSON line per M")
     ap.add_argument("--step-m", default="1,2,4,8,16,32", help="M values of the step mix")
+    ap.add_argument("--mlp-swiglu", action="store_true",
+                    help="MLP up/gate projection with the SwiGLU epilogue at every M; "
+                         "prints one JSON line per M")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -223,6 +316,8 @@ def main() -> int:
 
     if args.step_mix:
         return step_mix(args, fp8bs, dev)
+    if args.mlp_swiglu:
+        return mlp_swiglu(args, fp8bs, dev)
 
     if args.diag_copy_mib:
         nbytes = args.diag_copy_mib << 20

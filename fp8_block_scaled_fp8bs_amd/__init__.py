@@ -19,9 +19,11 @@ __all__ = [
     "Fp8bsError", "GemmConfig", "load", "library_path",
     "quantize_weight", "quantize_act", "gemm", "gemm_q", "gemm_ex",
     "workspace_bytes", "config_workspace_bytes", "select_config",
+    "swiglu_quant", "gemm_swiglu", "gemm_swiglu_ex", "swiglu_select_config",
+    "swiglu_workspace_bytes",
     "encode_e4m3", "launch_count", "build_info", "diag_read", "diag_copy",
     "hip_runtime_mappings", "PATH_MFMA", "PATH_DOT", "REDUCE_KERNEL",
-    "REDUCE_LAST_ARRIVER", "COUNTER",
+    "REDUCE_LAST_ARRIVER", "EPILOGUE_SEPARATE", "EPILOGUE_IN_GEMM", "COUNTER",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -30,8 +32,9 @@ _LIB = None
 
 PATH_AUTO, PATH_MFMA, PATH_DOT, PATH_MFMA_ROWS, PATH_MFMA_STREAM = 0, 1, 2, 3, 4
 REDUCE_KERNEL, REDUCE_LAST_ARRIVER = 0, 1
+EPILOGUE_SEPARATE, EPILOGUE_IN_GEMM = 0, 1
 COUNTER = {"quant_weight": 0, "quant_act": 1, "gemm_mfma": 2, "gemm_dot": 3,
-           "split_reduce": 4, "encode": 5, "diag": 6}
+           "split_reduce": 4, "encode": 5, "diag": 6, "swiglu": 7}
 
 
 class Fp8bsError(RuntimeError):
@@ -45,7 +48,7 @@ class Fp8bsError(RuntimeError):
 class _Config(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int32) for name in
                 ("path", "tiles_n", "waves_n", "waves_k", "depth", "split_k", "reduce",
-                 "reserved")]
+                 "epilogue")]
 
 
 @dataclass(frozen=True)
@@ -58,14 +61,16 @@ class GemmConfig:
     depth: int
     split_k: int = 1
     reduce: int = REDUCE_KERNEL
+    epilogue: int = EPILOGUE_SEPARATE
 
     def _c(self) -> _Config:
         return _Config(self.path, self.tiles_n, self.waves_n, self.waves_k, self.depth,
-                       self.split_k, self.reduce, 0)
+                       self.split_k, self.reduce, self.epilogue)
 
     @staticmethod
     def _from_c(c: _Config) -> "GemmConfig":
-        return GemmConfig(c.path, c.tiles_n, c.waves_n, c.waves_k, c.depth, c.split_k, c.reduce)
+        return GemmConfig(c.path, c.tiles_n, c.waves_n, c.waves_k, c.depth, c.split_k, c.reduce,
+                          c.epilogue)
 
 
 def library_path() -> str:
@@ -92,6 +97,12 @@ def load() -> ctypes.CDLL:
         "fp8bs_gemm_config_workspace_bytes": (sz, [ctypes.POINTER(_Config), i64, i64, i64]),
         "fp8bs_gemm_ex": (i32, [vp, vp, vp, i64, vp, vp, i64, i64, vp, vp, sz,
                                 ctypes.POINTER(_Config), vp]),
+        "fp8bs_swiglu_quant": (i32, [vp, i64, i64, vp, vp, vp]),
+        "fp8bs_gemm_swiglu": (i32, [vp, i64, vp, vp, i64, i64, vp, vp, vp, vp, sz, vp]),
+        "fp8bs_gemm_swiglu_ex": (i32, [vp, vp, vp, i64, vp, vp, i64, i64, vp, vp, vp, vp, sz,
+                                       ctypes.POINTER(_Config), vp]),
+        "fp8bs_gemm_swiglu_select_config": (i32, [i64, i64, i64, ctypes.POINTER(_Config)]),
+        "fp8bs_gemm_swiglu_workspace_bytes": (sz, [ctypes.POINTER(_Config), i64, i64, i64]),
         "fp8bs_encode_e4m3": (i32, [vp, i64, vp, i32, vp]),
         "fp8bs_status_string": (ctypes.c_char_p, [i32]),
         "fp8bs_launch_count": (ctypes.c_uint64, [i32]),
@@ -171,12 +182,24 @@ def select_config(m: int, n: int, k: int) -> GemmConfig:
 
 
 def _out_ws(m, n, device, out, workspace, need):
+    """Output tensor and workspace of one call. Returns (y, workspace tensor,
+    pointer, bytes): the caller keeps the workspace tensor referenced until the
+    launch is queued (a workspace freed earlier could be handed to another
+    tensor of the same call) and then passes it to _done."""
     y = out if out is not None else torch.empty((m, n), dtype=torch.bfloat16, device=device)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    return y, ws_ptr, ws_len
+    return y, workspace, ws_ptr, ws_len
+
+
+def _done(workspace, stream) -> None:
+    """After the launch: a workspace used on a stream other than the current
+    one is recorded on that stream, so the caching allocator does not reuse it
+    before the kernels that read it have run."""
+    if workspace is not None and stream is not None:
+        workspace.record_stream(stream)
 
 
 def gemm(x: torch.Tensor, w_q: torch.Tensor, w_s: torch.Tensor, out=None, workspace=None,
@@ -184,10 +207,11 @@ def gemm(x: torch.Tensor, w_q: torch.Tensor, w_s: torch.Tensor, out=None, worksp
     """Y[m][n] (bf16) = X[m][k] . W^T with the per-row 1x128 FP8 cast fused in."""
     m, k = x.shape
     n = w_q.shape[0]
-    y, ws, wl = _out_ws(m, n, x.device, out, workspace, workspace_bytes(m, n, k))
+    y, wst, ws, wl = _out_ws(m, n, x.device, out, workspace, workspace_bytes(m, n, k))
     _check(load().fp8bs_gemm(_dev(x, torch.bfloat16, "x", 2), m,
                              _dev(w_q, torch.uint8, "w_fp8", 2), _dev(w_s, torch.float32, "w_scale", 2),
                              n, k, _dev(y, torch.bfloat16, "y", 2), ws, wl, _stream(stream)))
+    _done(wst, stream)
     return y
 
 
@@ -196,11 +220,12 @@ def gemm_q(x_q: torch.Tensor, x_s: torch.Tensor, w_q: torch.Tensor, w_s: torch.T
     """Same product from pre-quantized activations (codes and scales)."""
     m, k = x_q.shape
     n = w_q.shape[0]
-    y, ws, wl = _out_ws(m, n, x_q.device, out, workspace, workspace_bytes(m, n, k))
+    y, wst, ws, wl = _out_ws(m, n, x_q.device, out, workspace, workspace_bytes(m, n, k))
     _check(load().fp8bs_gemm_q(_dev(x_q, torch.uint8, "x_fp8", 2), _dev(x_s, torch.float32, "x_scale", 2),
                                m, _dev(w_q, torch.uint8, "w_fp8", 2),
                                _dev(w_s, torch.float32, "w_scale", 2), n, k,
                                _dev(y, torch.bfloat16, "y", 2), ws, wl, _stream(stream)))
+    _done(wst, stream)
     return y
 
 
@@ -219,13 +244,92 @@ def gemm_ex(cfg: GemmConfig, w_q: torch.Tensor, w_s: torch.Tensor, x: torch.Tens
         xqp, xsp = _dev(x_q, torch.uint8, "x_fp8", 2), _dev(x_s, torch.float32, "x_scale", 2)
         device = x_q.device
     n = w_q.shape[0]
-    y, ws, wl = _out_ws(m, n, device, out, workspace, config_workspace_bytes(cfg, m, n, k))
+    y, wst, ws, wl = _out_ws(m, n, device, out, workspace, config_workspace_bytes(cfg, m, n, k))
     c = cfg._c()
     _check(load().fp8bs_gemm_ex(xp, xqp, xsp, m, _dev(w_q, torch.uint8, "w_fp8", 2),
                                 _dev(w_s, torch.float32, "w_scale", 2), n, k,
                                 _dev(y, torch.bfloat16, "y", 2), ws, wl, ctypes.byref(c),
                                 _stream(stream)))
+    _done(wst, stream)
     return y
+
+
+def _h_out(m, inter, device, h):
+    if h is not None:
+        return h
+    return (torch.empty((m, inter), dtype=torch.uint8, device=device),
+            torch.empty((m, inter // 128), dtype=torch.float32, device=device))
+
+
+def swiglu_quant(y: torch.Tensor, h=None, stream=None):
+    """MLP epilogue alone: y[m][2I] bf16 (gate | up) -> (codes uint8 [m][I],
+    fp32 scales [m][I/128]) of h = silu(gate) * up."""
+    m, n2 = y.shape
+    inter = n2 // 2
+    hq, hs = _h_out(m, inter, y.device, h)
+    _check(load().fp8bs_swiglu_quant(_dev(y, torch.bfloat16, "y", 2), m, inter,
+                                     _dev(hq, torch.uint8, "h_fp8", 2),
+                                     _dev(hs, torch.float32, "h_scale", 2), _stream(stream)))
+    return hq, hs
+
+
+def swiglu_select_config(m: int, n: int, k: int) -> GemmConfig:
+    c = _Config()
+    _check(load().fp8bs_gemm_swiglu_select_config(m, n, k, ctypes.byref(c)))
+    return GemmConfig._from_c(c)
+
+
+def swiglu_workspace_bytes(m: int, n: int, k: int, cfg: GemmConfig | None = None) -> int:
+    c = cfg._c() if cfg is not None else None
+    return int(load().fp8bs_gemm_swiglu_workspace_bytes(
+        ctypes.byref(c) if c is not None else None, m, n, k))
+
+
+def gemm_swiglu(x: torch.Tensor, w_q: torch.Tensor, w_s: torch.Tensor, out=None, h=None,
+                workspace=None, stream=None):
+    """Up/gate projection with the SwiGLU epilogue fused in: returns
+    (y [m][n] bf16, h codes [m][n/2], h scales [m][n/256])."""
+    m, k = x.shape
+    n = w_q.shape[0]
+    y, wst, ws, wl = _out_ws(m, n, x.device, out, workspace, swiglu_workspace_bytes(m, n, k))
+    hq, hs = _h_out(m, n // 2, x.device, h)
+    _check(load().fp8bs_gemm_swiglu(_dev(x, torch.bfloat16, "x", 2), m,
+                                    _dev(w_q, torch.uint8, "w_fp8", 2),
+                                    _dev(w_s, torch.float32, "w_scale", 2), n, k,
+                                    _dev(y, torch.bfloat16, "y", 2),
+                                    _dev(hq, torch.uint8, "h_fp8", 2),
+                                    _dev(hs, torch.float32, "h_scale", 2), ws, wl,
+                                    _stream(stream)))
+    _done(wst, stream)
+    return y, hq, hs
+
+
+def gemm_swiglu_ex(cfg: GemmConfig, w_q: torch.Tensor, w_s: torch.Tensor,
+                   x: torch.Tensor | None = None, x_q: torch.Tensor | None = None,
+                   x_s: torch.Tensor | None = None, out=None, h=None, workspace=None,
+                   stream=None):
+    """gemm_swiglu with an explicit kernel configuration."""
+    if x is not None:
+        m, k = x.shape
+        xp, xqp, xsp = _dev(x, torch.bfloat16, "x", 2), None, None
+        device = x.device
+    else:
+        m, k = x_q.shape
+        xp = None
+        xqp, xsp = _dev(x_q, torch.uint8, "x_fp8", 2), _dev(x_s, torch.float32, "x_scale", 2)
+        device = x_q.device
+    n = w_q.shape[0]
+    y, wst, ws, wl = _out_ws(m, n, device, out, workspace, swiglu_workspace_bytes(m, n, k, cfg))
+    hq, hs = _h_out(m, n // 2, device, h)
+    c = cfg._c()
+    _check(load().fp8bs_gemm_swiglu_ex(xp, xqp, xsp, m, _dev(w_q, torch.uint8, "w_fp8", 2),
+                                       _dev(w_s, torch.float32, "w_scale", 2), n, k,
+                                       _dev(y, torch.bfloat16, "y", 2),
+                                       _dev(hq, torch.uint8, "h_fp8", 2),
+                                       _dev(hs, torch.float32, "h_scale", 2), ws, wl,
+                                       ctypes.byref(c), _stream(stream)))
+    _done(wst, stream)
+    return y, hq, hs
 
 
 def encode_e4m3(v: torch.Tensor, mode: int = 0, out=None, stream=None) -> torch.Tensor:

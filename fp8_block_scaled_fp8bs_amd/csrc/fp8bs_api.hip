@@ -19,7 +19,10 @@ namespace {
 std::atomic<uint64_t> g_counts[8];
 std::atomic<uint64_t> g_epoch{1};  // launch tags for the last-arriver counters (never 0)
 
-enum { CNT_QW = 0, CNT_QA = 1, CNT_MFMA = 2, CNT_DOT = 3, CNT_RED = 4, CNT_ENC = 5, CNT_DIAG = 6 };
+enum {
+  CNT_QW = 0, CNT_QA = 1, CNT_MFMA = 2, CNT_DOT = 3, CNT_RED = 4, CNT_ENC = 5, CNT_DIAG = 6,
+  CNT_SWIGLU = 7
+};
 
 constexpr int kMaxDevices = 64;
 struct DeviceInfo {
@@ -95,7 +98,9 @@ inline bool is_row_range(int path) {
 // activations must stay below that.
 inline bool stream_offsets_fit(int64_t m, int64_t k) { return m * k * 2 < ((int64_t)1 << 31); }
 
-const KernelEntry* find_kernel(const fp8bs_gemm_config& c, int m, bool fused) {
+// swiglu: the row-range kernels instantiated with the SwiGLU epilogue.
+const KernelEntry* find_kernel(const fp8bs_gemm_config& c, int m, bool fused,
+                               bool swiglu = false) {
   int mt;
   if (c.path == FP8BS_PATH_MFMA || c.path == FP8BS_PATH_MFMA_ROWS) {
     mt = m <= 16 ? 1 : 2;
@@ -111,7 +116,8 @@ const KernelEntry* find_kernel(const fp8bs_gemm_config& c, int m, bool fused) {
   const bool rows = is_row_range(c.path);  // waves_n unused
   for (const KernelEntry& e : kernel_registry())
     if (e.path == c.path && e.mt == mt && e.tn == c.tiles_n && (rows || e.wn == c.waves_n) &&
-        e.wk == c.waves_k && e.d == c.depth && e.fused == (int)fused)
+        e.wk == c.waves_k && e.d == c.depth && e.fused == (int)fused &&
+        e.swiglu == (int)(swiglu && rows))
       return &e;
   return nullptr;
 }
@@ -131,14 +137,18 @@ int rows_per_workgroup(int64_t n, int num_cu) {
   return (int)((r + 3) / 4 * 4);
 }
 
-size_t config_lds_bytes(const fp8bs_gemm_config& c, int m, int64_t n, int kbn, int num_cu) {
+size_t config_lds_bytes(const fp8bs_gemm_config& c, int m, int64_t n, int kbn, int num_cu,
+                        bool swiglu = false) {
   const int mt = m <= 16 ? 1 : 2;
   if (is_row_range(c.path)) {
-    // weight scales of the row range first, then the kernel's own layout
-    const size_t ws = (size_t)lds_wscale_bytes(rows_per_workgroup(n, num_cu), kbn);
+    // weight scales of the row range first, then the kernel's own layout,
+    // then (SwiGLU epilogue) the staged outputs
+    const int rows = rows_per_workgroup(n, num_cu);
+    const size_t ws = (size_t)lds_wscale_bytes(rows, kbn);
+    const size_t ys = swiglu ? (size_t)lds_ystage_bytes(m, rows) : 0;
     if (c.path == FP8BS_PATH_MFMA_STREAM)
-      return ws + (size_t)lds_stream_bytes(kbn, m, c.waves_k, mt);
-    return ws + (size_t)lds_act_bytes(kbn, m) + (size_t)2 * (c.waves_k - 1) * mt * 64 * 16;
+      return ws + (size_t)lds_stream_bytes(kbn, m, c.waves_k, mt) + ys;
+    return ws + (size_t)lds_act_bytes(kbn, m) + (size_t)2 * (c.waves_k - 1) * mt * 64 * 16 + ys;
   }
   const int nblk = (kbn + c.split_k - 1) / c.split_k;
   size_t red = 0;
@@ -180,6 +190,18 @@ constexpr int RW = FP8BS_PATH_MFMA_ROWS;
 constexpr int ST = FP8BS_PATH_MFMA_STREAM;
 constexpr int kTableCUs = 256;  // the configuration table assumes a full MI355X
 
+// Configurations the SwiGLU call accepts. With the separate epilogue:
+// everything but the last-arriver reduce (the split sum carries the
+// epilogue, or a second kernel runs it). Inside the GEMM: unsplit MFMA grid
+// and the row-range kernels compiled with the epilogue.
+bool swiglu_supported(const fp8bs_gemm_config& c, int m) {
+  if (c.epilogue == FP8BS_EPILOGUE_SEPARATE)
+    return c.split_k == 1 || c.reduce == FP8BS_REDUCE_KERNEL;
+  if (c.epilogue != FP8BS_EPILOGUE_IN_GEMM || c.split_k != 1) return false;
+  if (is_row_range(c.path)) return find_kernel(c, m, true, true) != nullptr;
+  return c.path == FP8BS_PATH_MFMA;
+}
+
 bool candidate_fits(const Candidate& cd, int64_t m, int64_t n, int kbn, fp8bs_gemm_config* out) {
   fp8bs_gemm_config c = make_cfg(cd.path, cd.tn, cd.wn, cd.wk, cd.d, cd.split);
   c.reduce = cd.split > 1 ? cd.reduce : RK;
@@ -200,9 +222,11 @@ bool candidate_fits(const Candidate& cd, int64_t m, int64_t n, int kbn, fp8bs_ge
 // launches over a rotating 1 GiB weight pool. The first candidate that fits
 // the shape (rows dividing n, split not above the number of K blocks,
 // staged activations within the LDS budget) is used; a fallback list with
-// growing split catches everything else.
-bool select_config(int64_t m, int64_t n, int64_t k, fp8bs_gemm_config* out) {
+// growing split catches everything else. The SwiGLU call (swiglu set) uses
+// the same choice with the separate epilogue, so its y equals fp8bs_gemm's.
+bool select_config(int64_t m, int64_t n, int64_t k, fp8bs_gemm_config* out, bool swiglu = false) {
   if (m < 0 || m > 32 || n < 0 || k < 0 || n % BLK || k % BLK) return false;
+  if (swiglu && n % (2 * BLK)) return false;
   const int kbn = (int)(k / BLK);
   const int64_t nbn = n / BLK;
   if (m == 0 || n == 0 || kbn == 0) {
@@ -273,24 +297,49 @@ size_t cfg_workspace(const fp8bs_gemm_config& c, int64_t m, int64_t n) {
   return b;
 }
 
+// SwiGLU workspace: the split partials, or (epilogue inside the GEMM) one
+// 64-bit arrival counter per 128-column block of h.
+size_t swiglu_workspace(const fp8bs_gemm_config& c, int64_t m, int64_t n) {
+  if (c.split_k > 1) return cfg_partial_bytes(c, m, n);
+  if (c.epilogue != FP8BS_EPILOGUE_IN_GEMM) return 0;
+  return (size_t)((n / (2 * BLK)) * sizeof(uint64_t) + 15) / 16 * 16;
+}
 
+// The standalone MLP epilogue launch (also used by the fused call when k == 0).
+fp8bs_status launch_swiglu_quant(const void* y_bf16, int64_t m, int64_t inter, uint8_t* h_fp8,
+                                 float* h_scale, void* stream) {
+  const uint16_t* y = static_cast<const uint16_t*>(y_bf16);
+  int64_t in = inter;
+  void* args[] = {&y, &in, &h_fp8, &h_scale};
+  g_counts[CNT_SWIGLU]++;
+  return launch(reinterpret_cast<const void*>(swiglu_quant_kernel),
+                dim3((unsigned)(inter / BLK), (unsigned)m), dim3(64), 0, stream, args);
+}
+
+
+// The GEMM, optionally with the SwiGLU epilogue (swiglu: h_fp8 and h_scale
+// receive the re-quantized SwiGLU output).
 fp8bs_status gemm_impl(const void* x_bf16, const uint8_t* x_fp8, const float* x_scale, int64_t m,
                        const uint8_t* w_fp8, const float* w_scale, int64_t n, int64_t k,
                        void* y_bf16, void* workspace, size_t workspace_bytes,
-                       const fp8bs_gemm_config* cfg_in, void* stream) {
+                       const fp8bs_gemm_config* cfg_in, void* stream, bool swiglu = false,
+                       uint8_t* h_fp8 = nullptr, float* h_scale = nullptr) {
   // shapes
   if (m < 0 || m > 32 || n < 0 || k < 0 || n % BLK || k % BLK) return FP8BS_ERR_SHAPE;
   if (n / BLK > (int64_t)1 << 24 || k / BLK > (int64_t)1 << 20) return FP8BS_ERR_SHAPE;
+  if (swiglu && n % (2 * BLK)) return FP8BS_ERR_SHAPE;
   if (m == 0 || n == 0) return FP8BS_OK;
   const bool fused = x_bf16 != nullptr;
   // pointers
   if (!y_bf16) return FP8BS_ERR_NULL;
+  if (swiglu && (!h_fp8 || !h_scale)) return FP8BS_ERR_NULL;
   if (k > 0) {
     if (!w_fp8 || !w_scale) return FP8BS_ERR_NULL;
     if (!fused && (!x_fp8 || !x_scale)) return FP8BS_ERR_NULL;
   }
   // alignment
   if (!aligned(y_bf16, 16)) return FP8BS_ERR_ALIGN;
+  if (swiglu && (!aligned(h_fp8, 16) || !aligned(h_scale, 4))) return FP8BS_ERR_ALIGN;
   if (k > 0) {
     if (!aligned(w_fp8, 16) || !aligned(w_scale, 4)) return FP8BS_ERR_ALIGN;
     if (fused ? !aligned(x_bf16, 16) : (!aligned(x_fp8, 16) || !aligned(x_scale, 4)))
@@ -305,15 +354,17 @@ fp8bs_status gemm_impl(const void* x_bf16, const uint8_t* x_fp8, const float* x_
     int64_t n8v = n8;
     void* args[] = {&y, &n8v};
     g_counts[CNT_RED]++;
-    return launch(reinterpret_cast<const void*>(zero_fill_kernel),
-                  dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream, args);
+    const fp8bs_status zs = launch(reinterpret_cast<const void*>(zero_fill_kernel),
+                                   dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream, args);
+    if (zs != FP8BS_OK || !swiglu) return zs;
+    return launch_swiglu_quant(y_bf16, m, n / 2, h_fp8, h_scale, stream);
   }
   const int kbn = (int)(k / BLK);
   // configuration
   fp8bs_gemm_config c;
   if (cfg_in) {
     c = *cfg_in;
-  } else if (!select_config(m, n, k, &c)) {
+  } else if (!select_config(m, n, k, &c, swiglu)) {
     return FP8BS_ERR_SHAPE;
   }
   if (c.split_k < 1 || c.split_k > 64 || c.split_k > kbn) return FP8BS_ERR_CONFIG;
@@ -321,14 +372,16 @@ fp8bs_status gemm_impl(const void* x_bf16, const uint8_t* x_fp8, const float* x_
   if (c.path == FP8BS_PATH_MFMA_STREAM && !stream_offsets_fit(m, k)) return FP8BS_ERR_CONFIG;
   if (c.reduce != FP8BS_REDUCE_KERNEL && c.reduce != FP8BS_REDUCE_LAST_ARRIVER)
     return FP8BS_ERR_CONFIG;
+  if (swiglu && !swiglu_supported(c, (int)m)) return FP8BS_ERR_CONFIG;
+  const bool in_gemm = swiglu && c.epilogue == FP8BS_EPILOGUE_IN_GEMM;
   const bool split = c.split_k > 1;
   const bool last_arriver = split && c.reduce == FP8BS_REDUCE_LAST_ARRIVER;
-  const KernelEntry* ke = find_kernel(c, (int)m, fused);
+  const KernelEntry* ke = find_kernel(c, (int)m, fused, in_gemm);
   if (!ke) return FP8BS_ERR_CONFIG;
   const int rows = config_rows(c);
   if (n % rows) return FP8BS_ERR_CONFIG;
   // workspace
-  const size_t need = cfg_workspace(c, m, n);
+  const size_t need = swiglu ? swiglu_workspace(c, m, n) : cfg_workspace(c, m, n);
   if (need > 0) {
     if (!workspace || workspace_bytes < need) return FP8BS_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return FP8BS_ERR_ALIGN;
@@ -337,7 +390,7 @@ fp8bs_status gemm_impl(const void* x_bf16, const uint8_t* x_fp8, const float* x_
   DeviceInfo dev;
   const fp8bs_status st = current_device(&dev);
   if (st != FP8BS_OK) return st;
-  const size_t lds = config_lds_bytes(c, (int)m, n, kbn, dev.num_cu);
+  const size_t lds = config_lds_bytes(c, (int)m, n, kbn, dev.num_cu, in_gemm);
   if (lds > (size_t)dev.max_lds) return FP8BS_ERR_CONFIG;
   if (lds > 64 * 1024) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(ke->fn),
@@ -358,23 +411,42 @@ fp8bs_status gemm_impl(const void* x_bf16, const uint8_t* x_fp8, const float* x_
   p.counters = last_arriver ? reinterpret_cast<uint64_t*>(static_cast<uint8_t*>(workspace) +
                                                           cfg_partial_bytes(c, m, n))
                             : nullptr;
+  if (in_gemm) p.counters = static_cast<uint64_t*>(workspace);
+  p.hq = h_fp8;
+  p.hs = h_scale;
   p.epoch = g_epoch.fetch_add(1) & ((uint64_t(1) << 56) - 1);
   p.m = (int)m;
   p.n = (int)n;
   p.k = (int)k;
   p.kbn = kbn;
   p.split = c.split_k;
-  p.out = !split ? OUT_DIRECT : (last_arriver ? OUT_LAST_ARRIVER : OUT_PARTIAL);
+  p.out = !split ? (in_gemm ? OUT_SWIGLU : OUT_DIRECT)
+                 : (last_arriver ? OUT_LAST_ARRIVER : OUT_PARTIAL);
   void* args[] = {&p};
   dim3 grid((unsigned)(n / rows), (unsigned)c.split_k);
   if (is_row_range(c.path)) {
     p.rows_per_wg = rows_per_workgroup(n, dev.num_cu);
     grid = dim3((unsigned)((n + p.rows_per_wg - 1) / p.rows_per_wg), 1);
   }
+  // the SwiGLU epilogue arrives on each (side, 128-column block) pair of a
+  // workgroup's range at once, one lane per pair
+  if (in_gemm && 2 * ((is_row_range(c.path) ? p.rows_per_wg : rows) / BLK + 2) >
+                     SWIGLU_MAX_ARRIVALS)
+    return FP8BS_ERR_CONFIG;
   const dim3 block(64 * (is_row_range(c.path) ? 1 : c.waves_n) * c.waves_k);
   g_counts[c.path == FP8BS_PATH_DOT ? CNT_DOT : CNT_MFMA]++;
   fp8bs_status ls = launch(reinterpret_cast<const void*>(ke->fn), grid, block, lds, stream, args);
-  if (ls != FP8BS_OK || !split || last_arriver) return ls;
+  if (ls != FP8BS_OK || last_arriver || in_gemm) return ls;
+  if (!split) return swiglu ? launch_swiglu_quant(y_bf16, m, n / 2, h_fp8, h_scale, stream) : ls;
+  if (swiglu) {
+    const float* part = p.part;
+    int sk = c.split_k, mm = (int)m, nn = (int)n;
+    uint16_t* y = p.y;
+    void* sargs[] = {&part, &sk, &mm, &nn, &y, &h_fp8, &h_scale};
+    g_counts[CNT_RED]++;
+    return launch(reinterpret_cast<const void*>(splitk_reduce_swiglu_kernel),
+                  dim3((unsigned)(n / (2 * BLK)), (unsigned)m), dim3(64), 0, stream, sargs);
+  }
   const float* part = p.part;
   int sk = c.split_k;
   int64_t mn4 = m * n / 4;
@@ -469,6 +541,58 @@ fp8bs_status fp8bs_gemm_ex(const void* x_bf16, const uint8_t* x_fp8, const float
   if (!cfg) return FP8BS_ERR_NULL;
   return gemm_impl(x_bf16, x_fp8, x_scale, m, w_fp8, w_scale, n, k, y_bf16, workspace,
                    workspace_bytes, cfg, stream);
+}
+
+fp8bs_status fp8bs_swiglu_quant(const void* y_bf16, int64_t m, int64_t inter, uint8_t* h_fp8,
+                               float* h_scale, void* stream) {
+  if (m < 0 || inter < 0 || inter % BLK) return FP8BS_ERR_SHAPE;
+  if (m == 0 || inter == 0) return FP8BS_OK;
+  if (inter / BLK > 0x7FFFFFFF || m > 65535) return FP8BS_ERR_SHAPE;
+  if (!y_bf16 || !h_fp8 || !h_scale) return FP8BS_ERR_NULL;
+  if (!aligned(y_bf16, 16) || !aligned(h_fp8, 16) || !aligned(h_scale, 4)) return FP8BS_ERR_ALIGN;
+  const fp8bs_status st = current_device(nullptr);
+  if (st != FP8BS_OK) return st;
+  return launch_swiglu_quant(y_bf16, m, inter, h_fp8, h_scale, stream);
+}
+
+fp8bs_status fp8bs_gemm_swiglu(const void* x_bf16, int64_t m, const uint8_t* w_fp8,
+                               const float* w_scale, int64_t n, int64_t k, void* y_bf16,
+                               uint8_t* h_fp8, float* h_scale, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (!x_bf16 && m > 0 && n > 0 && k > 0) {
+    if (m > 32 || n % (2 * BLK) || k % BLK) return FP8BS_ERR_SHAPE;
+    return FP8BS_ERR_NULL;
+  }
+  return gemm_impl(x_bf16, nullptr, nullptr, m, w_fp8, w_scale, n, k, y_bf16, workspace,
+                   workspace_bytes, nullptr, stream, true, h_fp8, h_scale);
+}
+
+fp8bs_status fp8bs_gemm_swiglu_ex(const void* x_bf16, const uint8_t* x_fp8, const float* x_scale,
+                                  int64_t m, const uint8_t* w_fp8, const float* w_scale,
+                                  int64_t n, int64_t k, void* y_bf16, uint8_t* h_fp8,
+                                  float* h_scale, void* workspace, size_t workspace_bytes,
+                                  const fp8bs_gemm_config* cfg, void* stream) {
+  return gemm_impl(x_bf16, x_fp8, x_scale, m, w_fp8, w_scale, n, k, y_bf16, workspace,
+                   workspace_bytes, cfg, stream, true, h_fp8, h_scale);
+}
+
+fp8bs_status fp8bs_gemm_swiglu_select_config(int64_t m, int64_t n, int64_t k,
+                                             fp8bs_gemm_config* out) {
+  if (!out) return FP8BS_ERR_NULL;
+  if (!select_config(m, n, k, out, true)) return FP8BS_ERR_SHAPE;
+  return FP8BS_OK;
+}
+
+size_t fp8bs_gemm_swiglu_workspace_bytes(const fp8bs_gemm_config* cfg, int64_t m, int64_t n,
+                                         int64_t k) {
+  fp8bs_gemm_config c;
+  if (cfg) {
+    c = *cfg;
+  } else if (!select_config(m, n, k, &c, true)) {
+    return 0;
+  }
+  if (m <= 0 || n <= 0 || k <= 0 || n % (2 * BLK)) return 0;
+  return swiglu_workspace(c, m, n);
 }
 
 fp8bs_status fp8bs_encode_e4m3(const float* in, int64_t count, uint8_t* out, int32_t mode,

@@ -213,4 +213,48 @@ __device__ __forceinline__ float cast_quarter(const uint4 (&xw)[4], uint32_t (&c
   return s;
 }
 
+// ----------------------------------------------------- SwiGLU epilogue ---
+
+// h = silu(g) * u for a pair of (gate, up) bf16 values packed in one dword
+// each, rounded to bf16: silu(g) = g / (1 + e^-g) (the gated unit of
+// Shazeer, "GLU Variants Improve Transformer"), evaluated in fp32 with a
+// correctly rounded division and without contraction into fused
+// multiply-adds, so every kernel that applies it gives the same bits.
+__device__ __forceinline__ uint32_t swiglu_pair(uint32_t g, uint32_t u) {
+#pragma clang fp contract(off)
+  const float g0 = bf16_lo(g), g1 = bf16_hi(g);
+  const float u0 = bf16_lo(u), u1 = bf16_hi(u);
+  const float h0 = g0 / (1.0f + expf(-g0)) * u0;
+  const float h1 = g1 / (1.0f + expf(-g1)) * u1;
+  return pack_bf16x2(h0, h1);
+}
+
+// The SwiGLU step and the 1x128 cast for one activation row of one 128-column
+// block, by one wave: lane l holds gate and up columns 2l, 2l+1 (one dword of
+// bf16 pairs each). The block amax is reduced over the wave; scale and codes
+// follow the activation rule (the same quotient and encoder as cast_quarter).
+// Writes codes 2l, 2l+1 to hq_row (the block's 128 codes) and, from lane 0,
+// the scale to *hs.
+__device__ __forceinline__ void swiglu_cast_wave(uint32_t gw, uint32_t uw, int l,
+                                                 uint8_t* hq_row, float* hs) {
+  const uint32_t hw = swiglu_pair(gw, uw);
+  float x[2] = {bf16_lo(hw), bf16_hi(hw)};
+  const float am = wave_max(__builtin_fmaxf(__builtin_fabsf(x[0]), __builtin_fabsf(x[1])));
+  const float sc = am / 448.0f;
+  block_quotients(x, am, sc);
+  const uint32_t codes = e4m3x4(x[0], x[1], 0.0f, 0.0f);
+  *reinterpret_cast<uint16_t*>(hq_row + 2 * l) = (uint16_t)codes;
+  if (l == 0) *hs = sc;
+}
+
+// 32 pairs: g, u hold 16 dwords (32 bf16) each in column order; h gets 16 dwords.
+__device__ __forceinline__ void swiglu_quarter(const uint32_t (&g)[16], const uint32_t (&u)[16],
+                                               uint4 (&h)[4]) {
+  uint32_t hw[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) hw[i] = swiglu_pair(g[i], u[i]);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) h[j] = make_uint4(hw[4 * j], hw[4 * j + 1], hw[4 * j + 2], hw[4 * j + 3]);
+}
+
 }  // namespace fp8bs

@@ -27,7 +27,9 @@
 namespace fp8bs {
 
 // Output handling of a kernel instance.
-enum { OUT_DIRECT = 0, OUT_PARTIAL = 1, OUT_LAST_ARRIVER = 2 };
+// OUT_SWIGLU: as OUT_DIRECT, and the workgroup finishing the last columns of
+// a 128-column block of the SwiGLU output runs the MLP epilogue for it.
+enum { OUT_DIRECT = 0, OUT_PARTIAL = 1, OUT_LAST_ARRIVER = 2, OUT_SWIGLU = 3 };
 
 struct GemmParams {
   const uint16_t* x;    // bf16 [m][k] (fused cast) or nullptr
@@ -37,12 +39,15 @@ struct GemmParams {
   const float* ws;      // fp32 [n/128][k/128]
   uint16_t* y;          // bf16 [m][n]
   float* part;          // fp32 [split][m][n] when split > 1
-  uint64_t* counters;   // [row groups] arrival counters (last-arriver reduce)
+  uint64_t* counters;   // arrival counters: [row groups] (last-arriver reduce) or
+                        // [n/256] (SwiGLU epilogue)
   uint64_t epoch;       // nonzero tag of this launch (last-arriver reduce)
   int m, n, k, kbn;     // kbn = k / 128
   int split;
   int out;              // OUT_DIRECT, OUT_PARTIAL or OUT_LAST_ARRIVER
   int rows_per_wg;      // row-range kernel: output columns per workgroup (multiple of 4)
+  uint8_t* hq;          // SwiGLU epilogue: E4M3 codes [m][n/2]
+  float* hs;            // SwiGLU epilogue: fp32 scales [m][n/256]
 };
 
 // LDS layout of a workgroup:
@@ -204,61 +209,76 @@ __device__ __forceinline__ void stage_act(const GemmParams& p, int kb0, int nblk
 
 // ------------------------------------------------------ split-K epilogue ---
 
-// Partials that another workgroup sums in the same launch (last-arriver
-// reduce) are written and read with device-scope coherent accesses: the
-// stores write through this XCD's L2 and the loads do not hit stale lines
-// of another XCD's L2. No cache-wide writeback or invalidate is needed.
-__device__ __forceinline__ void store_coherent(float* dst, float v) {
-  __hip_atomic_store(dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Cross-workgroup handoff in one launch (last-arriver reduce, SwiGLU
+// epilogue). Workgroups on different XCDs do not share an L2, so the data
+// one workgroup hands to another are written and read only with
+// device-scope atomic accesses: the stores write through this XCD's L2 and
+// the loads are not served from stale lines of the reader's caches. Each
+// thread waits until its own stores are performed (vmcnt counts stores on
+// this architecture), a barrier orders the whole workgroup's stores before
+// the arrival, and the arrival is a device-scope read-modify-write on an
+// integer counter. The arrival that completes the count reads the data after
+// it. The protocol needs no cache-wide write-back or invalidate (those cost
+// far more than the handoff itself when every workgroup arrives).
+//
+// Counter: 64 bits, (launch epoch << 8) | arrivals. An arrival that finds
+// another epoch (a previous launch, or whatever the memory held) starts this
+// launch's count at 1; the arrival that brings the count to `expected` is the
+// last one, and clears the counter. The epoch is unique per host-side launch
+// call, so the counters never need initialization; a replayed graph reuses
+// its epoch, which the clearing makes safe.
+
+__device__ __forceinline__ void store_coherent64(void* dst, uint64_t v) {
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(dst), v, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ float load_coherent(const float* src) {
-  return __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ uint64_t load_coherent64(const void* src) {
+  return __hip_atomic_load(reinterpret_cast<const uint64_t*>(src), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Store an fp32 partial of 4 consecutive outputs: plain vector store when a
-// second kernel sums the partials, coherent stores for the last-arriver
-// reduce.
+// One arrival (any single thread). Returns whether it completed the count.
+__device__ __forceinline__ bool arrive(uint64_t* c, uint64_t epoch, uint64_t expected) {
+  uint64_t old = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  uint64_t nv;
+  for (;;) {
+    nv = ((old >> 8) == epoch) ? old + 1 : ((epoch << 8) | 1u);
+    if (__hip_atomic_compare_exchange_strong(c, &old, nv, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT))
+      break;
+  }
+  const bool last = (nv & 0xFFu) == expected;
+  if (last) __hip_atomic_store(c, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return last;
+}
+
+// Every thread: wait for this thread's coherent stores, then meet the others.
+__device__ __forceinline__ void stores_performed_barrier() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
+
+// Store an fp32 partial of 4 consecutive outputs: plain when a second kernel
+// sums the partials, coherent for the last-arriver reduce.
 __device__ __forceinline__ void store_partial4(const GemmParams& p, float* dst, float a, float b,
                                                float c, float d) {
   if (p.out == OUT_LAST_ARRIVER) {
-    store_coherent(dst, a);
-    store_coherent(dst + 1, b);
-    store_coherent(dst + 2, c);
-    store_coherent(dst + 3, d);
+    store_coherent64(dst, (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32));
+    store_coherent64(dst + 2, (uint64_t)__float_as_uint(c) | ((uint64_t)__float_as_uint(d) << 32));
   } else {
     *reinterpret_cast<float4*>(dst) = make_float4(a, b, c, d);
   }
 }
 
-// Called by every thread of a workgroup after it stored (coherently) its fp32
-// partial tile part[s][m][n0 .. n0+ROWS). Each thread first waits until its
-// own stores are performed at device scope; after the barrier the whole
-// tile is visible to every workgroup. One 64-bit counter per row group
-// holds (launch epoch << 8) | arrivals. An arrival that finds another epoch
-// in the counter (a previous launch, or whatever the memory held) starts
-// this launch's count at 1; the arrival that brings the count to `split` is
-// the last one and sums the split partials in order s = 0, 1, ..., split-1
-// (coherent loads), then clears the counter. The epoch is unique per
-// host-side launch call, so no initialization of the counters is ever
-// needed; a replayed graph reuses its epoch, which the clearing makes safe.
+// Called by every thread of a workgroup after it stored its fp32 partial
+// tile part[s][m][n0 .. n0+ROWS). The last of the split workgroups of a row
+// group (one counter per row group) sums the split partials in order
+// s = 0, 1, ..., split-1 and writes the bf16 outputs.
 template <int NT, int ROWS>
 __device__ __forceinline__ void last_arriver_reduce(const GemmParams& p, int n0, int tid) {
   __shared__ int s_last;
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  if (tid == 0) {
-    uint64_t* c = p.counters + blockIdx.x;
-    uint64_t old = __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    uint64_t nv;
-    for (;;) {
-      nv = ((old >> 8) == p.epoch) ? old + 1 : ((p.epoch << 8) | 1u);
-      if (__hip_atomic_compare_exchange_strong(c, &old, nv, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT))
-        break;
-    }
-    s_last = (int)(nv & 0xFFu) == p.split;
-    if (s_last) __hip_atomic_store(c, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  stores_performed_barrier();
+  if (tid == 0) s_last = arrive(p.counters + blockIdx.x, p.epoch, (uint64_t)p.split);
   __syncthreads();
   if (!s_last) return;
   const int M = p.m;
@@ -267,14 +287,129 @@ __device__ __forceinline__ void last_arriver_reduce(const GemmParams& p, int n0,
     const int m = i / (ROWS / 4), r4 = i - m * (ROWS / 4);
     const size_t off = (size_t)m * (size_t)p.n + n0 + 4 * r4;
     float a[4];
+    for (int s = 0; s < p.split; ++s) {
+      const uint64_t lo = load_coherent64(p.part + (size_t)s * mn + off);
+      const uint64_t hi = load_coherent64(p.part + (size_t)s * mn + off + 2);
+      const float v[4] = {__uint_as_float((uint32_t)lo), __uint_as_float((uint32_t)(lo >> 32)),
+                          __uint_as_float((uint32_t)hi), __uint_as_float((uint32_t)(hi >> 32))};
 #pragma unroll
-    for (int q = 0; q < 4; ++q) a[q] = load_coherent(p.part + off + q);
-    for (int s = 1; s < p.split; ++s) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) a[q] += load_coherent(p.part + (size_t)s * mn + off + q);
+      for (int q = 0; q < 4; ++q) a[q] = s == 0 ? v[q] : a[q] + v[q];
     }
     *reinterpret_cast<uint2*>(p.y + off) =
         make_uint2(pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]));
+  }
+}
+
+// ------------------------------------------------- SwiGLU epilogue ---
+
+// The MLP up/gate projection with SwiGLU and the 1x128 FP8 cast of its
+// result fused in ("Kernel-Level Optimisations for LLM Inference and
+// Training", section "Scheduling decides the shapes your kernels see", on
+// fusing element-wise steps into the matmul). Output columns [0, I) are the
+// gate, [I, 2I) the up projection (I = n/2). A 128-column block b of h needs
+// gate columns 128b.. and up columns I+128b.., which other workgroups may
+// produce. Every workgroup stores its bf16 outputs coherently and arrives on
+// the counter of each block b it produced columns of, once per side, all
+// arrivals at the same time (one lane each); the workgroup whose arrival
+// completes a block's count runs the epilogue for that block from the stored
+// bf16 outputs (swiglu_cast_wave, the function the standalone epilogue
+// runs). The result therefore depends only on the bf16 outputs, never on
+// which workgroup arrives last.
+
+constexpr int SWIGLU_MAX_ARRIVALS = 64;  // (side, block) pairs of one workgroup
+
+// Store 4 consecutive bf16 outputs (8 bytes): coherent when another
+// workgroup reads them in the same launch.
+__device__ __forceinline__ void store_y4(const GemmParams& p, uint16_t* dst, float a, float b,
+                                         float c, float d) {
+  const uint32_t lo = pack_bf16x2(a, b), hi = pack_bf16x2(c, d);
+  if (p.out == OUT_SWIGLU)
+    store_coherent64(dst, (uint64_t)lo | ((uint64_t)hi << 32));
+  else
+    *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+}
+
+// Row-range kernels with the SwiGLU epilogue (instantiated with SW = true)
+// keep their bf16 outputs in LDS
+// ([m][rows_per_wg], after the kernel's own areas) until the last tile and
+// then write them all at once: a device-coherent store is slow to complete,
+// and since stores and the weight loads share one in-order wait counter, a
+// store issued after every tile would hold up the weight stream.
+__host__ __device__ inline int lds_ystage_bytes(int m, int rows) { return (m * rows * 2 + 15) & ~15; }
+
+__device__ __forceinline__ void stage_y4(uint16_t* ystage, int rows, int m, int rl, float a,
+                                         float b, float c, float d) {
+  *reinterpret_cast<uint2*>(ystage + (size_t)m * rows + rl) =
+      make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
+}
+
+// Every thread: copy the staged outputs of rows [r0, r0 + nrows) to y with
+// coherent stores (after a barrier that makes the staging visible).
+template <int NT>
+__device__ __forceinline__ void flush_ystage(const GemmParams& p, const uint16_t* ystage, int r0,
+                                             int nrows, int tid) {
+  __syncthreads();
+  const int rows = p.rows_per_wg, q4 = rows / 4;
+  for (int i = tid; i < p.m * q4; i += NT) {
+    const int m = i / q4, rl = 4 * (i - m * q4);
+    if (rl < nrows) {
+      const uint2 v = *reinterpret_cast<const uint2*>(ystage + (size_t)m * rows + rl);
+      store_coherent64(p.y + (size_t)m * (size_t)p.n + r0 + rl,
+                       (uint64_t)v.x | ((uint64_t)v.y << 32));
+    }
+  }
+}
+
+// Workgroups (consecutive ranges of R output columns, nwg of them) holding a
+// column of [lo, lo + 128).
+__device__ __forceinline__ int wgs_touching(int lo, int R, int nwg) {
+  const int a = lo / R;
+  int b = (lo + BLK - 1) / R;
+  b = b < nwg - 1 ? b : nwg - 1;
+  return b - a + 1;
+}
+
+// Called by every thread of a workgroup after its last output store. The
+// workgroup produced output columns [r0, r1); workgroups own consecutive
+// ranges of R columns, nwg of them.
+template <int NT>
+__device__ __forceinline__ void swiglu_arrive(const GemmParams& p, int r0, int r1, int R,
+                                              int nwg, int tid) {
+  __shared__ int s_done[SWIGLU_MAX_ARRIVALS];
+  __shared__ int s_ndone;
+  const int inter = p.n >> 1;
+  // gate blocks [g0, g1] and up blocks [u0, u1] this workgroup produced columns of
+  int g0 = 0, g1 = -1, u0 = 0, u1 = -1;
+  if (r0 < inter) {
+    g0 = r0 / BLK;
+    g1 = ((r1 < inter ? r1 : inter) - 1) / BLK;
+  }
+  if (r1 > inter) {
+    u0 = ((r0 > inter ? r0 : inter) - inter) / BLK;
+    u1 = (r1 - 1 - inter) / BLK;
+  }
+  const int ng = g1 - g0 + 1, na = ng + (u1 - u0 + 1);  // na <= SWIGLU_MAX_ARRIVALS (host check)
+  if (tid == 0) s_ndone = 0;
+  stores_performed_barrier();
+  if (tid < na) {
+    const int b = tid < ng ? g0 + tid : u0 + (tid - ng);
+    const uint64_t expected =
+        (uint64_t)(wgs_touching(b * BLK, R, nwg) + wgs_touching(inter + b * BLK, R, nwg));
+    if (arrive(p.counters + b, p.epoch, expected)) s_done[atomicAdd(&s_ndone, 1)] = b;
+  }
+  __syncthreads();
+  const int nd = s_ndone;
+  // the epilogue of every completed block: one wave per (block, row) task
+  const int wave = tid >> 6, l = tid & 63;
+  for (int t = wave; t < nd * p.m; t += NT / 64) {
+    const int b = s_done[t / p.m], m = t - (t / p.m) * p.m;
+    const uint16_t* gp = p.y + (size_t)m * (size_t)p.n + b * BLK + 2 * l;
+    const uint32_t gw = __hip_atomic_load(reinterpret_cast<const uint32_t*>(gp),
+                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t uw = __hip_atomic_load(reinterpret_cast<const uint32_t*>(gp + inter),
+                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    swiglu_cast_wave(gw, uw, l, p.hq + (size_t)m * (size_t)inter + b * BLK,
+                     p.hs + (size_t)m * (size_t)(inter / BLK) + b);
   }
 }
 
@@ -461,10 +596,9 @@ __device__ __forceinline__ void gemm_mfma_body(const GemmParams& p, uint8_t* lds
         const int m = l16 + 16 * mt;
         if (m < M) {
           const int n = row0 + 16 * t + 4 * g16;
-          if (p.out == OUT_DIRECT) {
-            uint2* dst = reinterpret_cast<uint2*>(p.y + (size_t)m * (size_t)p.n + n);
-            *dst = make_uint2(pack_bf16x2(acc[t][mt][0], acc[t][mt][1]),
-                              pack_bf16x2(acc[t][mt][2], acc[t][mt][3]));
+          if (p.out == OUT_DIRECT || p.out == OUT_SWIGLU) {
+            store_y4(p, p.y + (size_t)m * (size_t)p.n + n, acc[t][mt][0], acc[t][mt][1],
+                     acc[t][mt][2], acc[t][mt][3]);
           } else {
             store_partial4(p, p.part + ((size_t)s * M + m) * (size_t)p.n + n, acc[t][mt][0],
                            acc[t][mt][1], acc[t][mt][2], acc[t][mt][3]);
@@ -473,6 +607,7 @@ __device__ __forceinline__ void gemm_mfma_body(const GemmParams& p, uint8_t* lds
       }
   }
   if (p.out == OUT_LAST_ARRIVER) last_arriver_reduce<NT, ROWS>(p, n0, tid);
+  if (p.out == OUT_SWIGLU) swiglu_arrive<NT>(p, n0, n0 + ROWS, ROWS, gridDim.x, tid);
 }
 
 // Rounds of activation loads a workgroup needs for its G quarter blocks
@@ -516,7 +651,7 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_mfma_kernel(GemmParams p) {
 // barrier per tile) and wave 0 writes the tile's outputs.
 // ====================================================================
 
-template <int MT, int WK, int D, int PRE, bool FUSED>
+template <int MT, int WK, int D, int PRE, bool FUSED, bool SW = false>
 __global__ __launch_bounds__(64 * WK) void gemm_rows_kernel(GemmParams p) {
   constexpr int NT = 64 * WK;
   constexpr int CR = FUSED ? 3 : 1;
@@ -540,6 +675,8 @@ __global__ __launch_bounds__(64 * WK) void gemm_rows_kernel(GemmParams p) {
   uint8_t* act = lds;
   float* act_s = reinterpret_cast<float*>(lds + kbn * M * ACT_STRIDE);
   f32x4* red = reinterpret_cast<f32x4*>(lds + lds_act_bytes(kbn, M));
+  uint16_t* ystage = reinterpret_cast<uint16_t*>(lds + lds_act_bytes(kbn, M) +
+                                                 2 * (WK - 1) * MT * 64 * 16);
 
   const int l16 = lane & 15, g16 = lane >> 4;
   const int l7 = lane & 7, hb = (lane >> 3) & 1;
@@ -651,9 +788,14 @@ __global__ __launch_bounds__(64 * WK) void gemm_rows_kernel(GemmParams p) {
         for (int mt = 0; mt < MT; ++mt) {
           const int m = l16 + 16 * mt;
           if (m < M && rl < nrows) {
-            uint2* dst = reinterpret_cast<uint2*>(p.y + (size_t)m * (size_t)p.n + r0 + rl);
-            *dst = make_uint2(pack_bf16x2(acc[mt][0], acc[mt][1]),
-                              pack_bf16x2(acc[mt][2], acc[mt][3]));
+            if constexpr (SW) {
+              stage_y4(ystage, p.rows_per_wg, m, rl, acc[mt][0], acc[mt][1], acc[mt][2],
+                       acc[mt][3]);
+            } else {
+              uint2* dst = reinterpret_cast<uint2*>(p.y + (size_t)m * (size_t)p.n + r0 + rl);
+              *dst = make_uint2(pack_bf16x2(acc[mt][0], acc[mt][1]),
+                                pack_bf16x2(acc[mt][2], acc[mt][3]));
+            }
           }
         }
       }
@@ -674,6 +816,10 @@ __global__ __launch_bounds__(64 * WK) void gemm_rows_kernel(GemmParams p) {
   for (int d = 0; d < D; ++d) {
     const int i = (ngrp - 1) * D + d;
     if (i < nitem) compute(d, i);
+  }
+  if constexpr (SW) {
+    flush_ystage<NT>(p, ystage, r0, nrows, tid);
+    swiglu_arrive<NT>(p, r0, r1, p.rows_per_wg, gridDim.x, tid);
   }
 }
 
@@ -737,7 +883,7 @@ struct ActFetch {
 };
 
 // XP = staging passes (1, 2, 4): 8 * XP >= m activation rows.
-template <int XP, int WK, int D, bool FUSED>
+template <int XP, int WK, int D, bool FUSED, bool SW = false>
 __global__ __launch_bounds__(64 * WK) void gemm_stream_kernel(GemmParams p) {
   constexpr int MT = XP > 2 ? 2 : 1;  // 16-row activation tiles of the MFMA B operand
   extern __shared__ __align__(16) uint8_t lds_all[];
@@ -760,6 +906,7 @@ __global__ __launch_bounds__(64 * WK) void gemm_stream_kernel(GemmParams p) {
   uint4* act = reinterpret_cast<uint4*>(lds);                     // [kbn][8][M] chunks
   float* act_s = reinterpret_cast<float*>(lds + kbn * M * BLK);    // [kbn][M]
   f32x4* red = reinterpret_cast<f32x4*>(lds + kbn * M * BLK + ((kbn * M * 4 + 15) & ~15));
+  uint16_t* ystage = reinterpret_cast<uint16_t*>(lds + lds_stream_bytes(kbn, M, WK, MT));
 
   const int l16 = lane & 15, g16 = lane >> 4;
   const int l7 = lane & 7, hb = (lane >> 3) & 1;
@@ -906,9 +1053,14 @@ __global__ __launch_bounds__(64 * WK) void gemm_stream_kernel(GemmParams p) {
         for (int mt = 0; mt < MT; ++mt) {
           const int m = l16 + 16 * mt;
           if (m < M && rl < nrows) {
-            uint2* dst = reinterpret_cast<uint2*>(p.y + (size_t)m * (size_t)p.n + r0 + rl);
-            *dst = make_uint2(pack_bf16x2(acc[mt][0], acc[mt][1]),
-                              pack_bf16x2(acc[mt][2], acc[mt][3]));
+            if constexpr (SW) {
+              stage_y4(ystage, p.rows_per_wg, m, rl, acc[mt][0], acc[mt][1], acc[mt][2],
+                       acc[mt][3]);
+            } else {
+              uint2* dst = reinterpret_cast<uint2*>(p.y + (size_t)m * (size_t)p.n + r0 + rl);
+              *dst = make_uint2(pack_bf16x2(acc[mt][0], acc[mt][1]),
+                                pack_bf16x2(acc[mt][2], acc[mt][3]));
+            }
           }
         }
       }
@@ -929,6 +1081,10 @@ __global__ __launch_bounds__(64 * WK) void gemm_stream_kernel(GemmParams p) {
   for (int d = 0; d < D; ++d) {
     const int i = (ngrp - 1) * D + d;
     if (i < nitem) compute(d, i);
+  }
+  if constexpr (SW) {
+    flush_ystage<64 * WK>(p, ystage, r0, nrows, tid);
+    swiglu_arrive<64 * WK>(p, r0, r1, p.rows_per_wg, gridDim.x, tid);
   }
 }
 
@@ -1083,7 +1239,8 @@ __device__ __forceinline__ void gemm_dot_body(const GemmParams& p, uint8_t* lds_
           if (p.out == OUT_DIRECT)
             p.y[(size_t)m * (size_t)p.n + n] = (uint16_t)bf16_rne(acc[t][m]);
           else if (p.out == OUT_LAST_ARRIVER)
-            store_coherent(p.part + ((size_t)s * M + m) * (size_t)p.n + n, acc[t][m]);
+            __hip_atomic_store(p.part + ((size_t)s * M + m) * (size_t)p.n + n, acc[t][m],
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           else
             p.part[((size_t)s * M + m) * (size_t)p.n + n] = acc[t][m];
         }

@@ -80,6 +80,23 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const uint16_t* __restri
   }
 }
 
+// Standalone MLP epilogue: y[m][2I] bf16 (gate in columns 0..I-1, up in
+// I..2I-1) -> h = silu(gate) * up rounded to bf16, cast per row per 128
+// columns: codes hq[m][I], scales hs[m][I/128]. One wave per (128-column
+// block, row), running swiglu_cast_wave, the function the fused GEMM
+// epilogues run on the same bf16 values. Grid: (I/128, m) waves.
+__global__ __launch_bounds__(64) void swiglu_quant_kernel(const uint16_t* __restrict__ y,
+                                                          int64_t inter,
+                                                          uint8_t* __restrict__ hq,
+                                                          float* __restrict__ hs) {
+  const int64_t b = blockIdx.x, row = blockIdx.y;
+  const int l = threadIdx.x;
+  const uint16_t* g = y + row * (2 * inter) + b * BLK + 2 * l;
+  const uint32_t gw = *reinterpret_cast<const uint32_t*>(g);
+  const uint32_t uw = *reinterpret_cast<const uint32_t*>(g + inter);
+  swiglu_cast_wave(gw, uw, l, hq + row * inter + b * BLK, hs + row * (inter / BLK) + b);
+}
+
 // Encoder utility: mode 0 = the quantizers' encoder, 1 = hardware, 2 = software.
 __global__ __launch_bounds__(256) void encode_kernel(const float* __restrict__ in, int64_t count,
                                                      uint8_t* __restrict__ out, int mode) {

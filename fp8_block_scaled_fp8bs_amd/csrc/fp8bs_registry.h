@@ -16,6 +16,7 @@ struct KernelEntry {
   int wn, wk, d;
   int fused;   // activations cast in the kernel (1) or given as codes and scales (0)
   void (*fn)(GemmParams);
+  int swiglu = 0;  // row-range kernels with the SwiGLU epilogue (1)
 };
 
 std::vector<KernelEntry>& kernel_registry();
@@ -49,6 +50,22 @@ struct KernelRegistrar {
   {3, 2, PRE, 1, WK, D, 1, gemm_rows_kernel<2, WK, D, PRE, true>},           \
   {3, 1, PRE, 1, WK, D, 0, gemm_rows_kernel<1, WK, D, PRE, false>},          \
   {3, 2, PRE, 1, WK, D, 0, gemm_rows_kernel<2, WK, D, PRE, false>},
+
+// Row-range kernels with the SwiGLU epilogue, for the configurations the
+// fused up/gate call selects.
+#define FP8BS_ROWS_SWIGLU_ENTRY(WK, D, PRE)                                       \
+  {3, 1, PRE, 1, WK, D, 1, gemm_rows_kernel<1, WK, D, PRE, true, true>, 1},       \
+  {3, 2, PRE, 1, WK, D, 1, gemm_rows_kernel<2, WK, D, PRE, true, true>, 1},       \
+  {3, 1, PRE, 1, WK, D, 0, gemm_rows_kernel<1, WK, D, PRE, false, true>, 1},      \
+  {3, 2, PRE, 1, WK, D, 0, gemm_rows_kernel<2, WK, D, PRE, false, true>, 1},
+
+#define FP8BS_STREAM_SWIGLU_ENTRY(WK, D)                                          \
+  {4, 1, 1, 1, WK, D, 1, gemm_stream_kernel<1, WK, D, true, true>, 1},           \
+  {4, 2, 1, 1, WK, D, 1, gemm_stream_kernel<2, WK, D, true, true>, 1},           \
+  {4, 4, 1, 1, WK, D, 1, gemm_stream_kernel<4, WK, D, true, true>, 1},           \
+  {4, 1, 1, 1, WK, D, 0, gemm_stream_kernel<1, WK, D, false, true>, 1},          \
+  {4, 2, 1, 1, WK, D, 0, gemm_stream_kernel<2, WK, D, false, true>, 1},          \
+  {4, 4, 1, 1, WK, D, 0, gemm_stream_kernel<4, WK, D, false, true>, 1},
 
 // Streaming row-range kernel: (waves along K, tiles in flight); the entry's
 // mt field holds the staging passes (1: m <= 8, 2: m <= 16, 4: m <= 32).

@@ -129,6 +129,7 @@ enum {
   FP8BS_PATH_MFMA_STREAM = 4
 };
 enum { FP8BS_REDUCE_KERNEL = 0, FP8BS_REDUCE_LAST_ARRIVER = 1 };
+enum { FP8BS_EPILOGUE_SEPARATE = 0, FP8BS_EPILOGUE_IN_GEMM = 1 };
 
 /* How one GEMM is laid out on the GPU.
  *   path      MFMA (16x16x128 FP8 matrix instructions, a grid of row
@@ -156,7 +157,15 @@ enum { FP8BS_REDUCE_KERNEL = 0, FP8BS_REDUCE_LAST_ARRIVER = 1 };
  *             tile, kept in the workspace and tagged with a per-launch epoch,
  *             so the workspace still needs no initialization. The integer
  *             counter is the only atomic; the partials are plain loads and
- *             stores summed in a fixed order.                              */
+ *             stores summed in a fixed order.
+ *   epilogue  where the SwiGLU epilogue of fp8bs_gemm_swiglu* runs (ignored
+ *             by the plain GEMM calls; set it to 0 there):
+ *             FP8BS_EPILOGUE_SEPARATE = with split_k > 1 in the kernel that
+ *             sums the split partials, otherwise in a second small kernel;
+ *             FP8BS_EPILOGUE_IN_GEMM = (split_k == 1, MFMA grid or row-range
+ *             paths) inside the GEMM launch: the workgroup that completes
+ *             the outputs of a 128-column block of h, found with one 64-bit
+ *             arrival counter per block in the workspace, applies it.     */
 typedef struct {
   int32_t path;
   int32_t tiles_n;
@@ -165,7 +174,7 @@ typedef struct {
   int32_t depth;
   int32_t split_k;
   int32_t reduce;
-  int32_t reserved;
+  int32_t epilogue;
 } fp8bs_gemm_config;
 
 /* The configuration fp8bs_gemm uses for this shape (a fixed table: the same
@@ -186,6 +195,69 @@ fp8bs_status fp8bs_gemm_ex(const void* x_bf16, const uint8_t* x_fp8, const float
                            void* y_bf16, void* workspace, size_t workspace_bytes,
                            const fp8bs_gemm_config* cfg, void* stream);
 
+/* ---- MLP epilogue: SwiGLU and the FP8 cast of its output ------------------
+ * Fusing the element-wise steps between the matmuls of a transformer layer
+ * into the matmul ("Kernel-Level Optimisations for LLM Inference and
+ * Training", section "Scheduling decides the shapes your kernels see", on
+ * fused SwiGLU) and casting the down projection's input to FP8 ("The
+ * profiler said the kernel ran zero times", section "What the trace
+ * showed"). SwiGLU is the published gated unit (Shazeer, "GLU Variants
+ * Improve Transformer"): h = silu(gate) * up, silu(g) = g / (1 + e^-g).
+ *
+ * Layout: the up/gate projection's output y [m][2*inter] bf16 holds the gate
+ * in columns 0 .. inter-1 and the up projection in inter .. 2*inter-1 (its
+ * weight stacks the gate rows above the up rows). h is evaluated in fp32 on
+ * the bf16 gate and up values, rounded to bf16, then cast per row per 128
+ * columns with the activation rule of fp8bs_quantize_act: codes h_fp8
+ * [m][inter], scales h_scale [m][inter/128] fp32, ready for fp8bs_gemm_q of
+ * the down projection. inter must be a multiple of 128. Every way of running
+ * it (standalone, after a split sum, inside the GEMM) gives the same bits.
+ * Alignment: y_bf16 and h_fp8 16 bytes, h_scale 4 bytes.                    */
+
+/* Standalone epilogue: y [m][2*inter] bf16 -> h codes and scales.           */
+fp8bs_status fp8bs_swiglu_quant(const void* y_bf16, int64_t m, int64_t inter, uint8_t* h_fp8,
+                                float* h_scale, void* stream);
+
+/* The up/gate projection with the epilogue fused in, in one call: y = X . W^T
+ * exactly as fp8bs_gemm computes it (written to y_bf16, [m][n]; with the
+ * same kernel configuration the bits are identical), and h_fp8 / h_scale as
+ * fp8bs_swiglu_quant(y) gives them, bit for bit. n = 2*inter must be a
+ * multiple of 256; 0 <= m <= 32. The automatic choice is fp8bs_gemm's
+ * configuration with FP8BS_EPILOGUE_SEPARATE (the faster way at decode sizes
+ * on MI355X: the epilogue rides on the split-sum kernel when K is split, and
+ * takes a second small kernel otherwise). The workspace holds the split
+ * partials or, for FP8BS_EPILOGUE_IN_GEMM, one 64-bit arrival counter per
+ * 128-column block of h (tagged with a per-launch epoch: no initialization
+ * needed); size from fp8bs_gemm_swiglu_workspace_bytes. Calls that share a
+ * workspace must be ordered on one stream.                                  */
+fp8bs_status fp8bs_gemm_swiglu(const void* x_bf16, int64_t m, const uint8_t* w_fp8,
+                               const float* w_scale, int64_t n, int64_t k, void* y_bf16,
+                               uint8_t* h_fp8, float* h_scale, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/* Same with an explicit configuration (cfg != NULL; x_bf16 != NULL selects
+ * the fused cast, otherwise x_fp8 / x_scale). Accepted with
+ * FP8BS_EPILOGUE_SEPARATE: every configuration fp8bs_gemm_ex accepts except
+ * the last-arriver reduce. With FP8BS_EPILOGUE_IN_GEMM: split_k == 1 on the
+ * MFMA path, or on the MFMA_ROWS / MFMA_STREAM paths for the compiled
+ * shapes (waves_k 8 with depth 3, 4 or 6 and, MFMA_STREAM, depth 4 or 6).
+ * Anything else is FP8BS_ERR_CONFIG.                                        */
+fp8bs_status fp8bs_gemm_swiglu_ex(const void* x_bf16, const uint8_t* x_fp8, const float* x_scale,
+                                  int64_t m, const uint8_t* w_fp8, const float* w_scale,
+                                  int64_t n, int64_t k, void* y_bf16, uint8_t* h_fp8,
+                                  float* h_scale, void* workspace, size_t workspace_bytes,
+                                  const fp8bs_gemm_config* cfg, void* stream);
+
+/* The configuration fp8bs_gemm_swiglu uses (fp8bs_gemm's, epilogue
+ * FP8BS_EPILOGUE_SEPARATE).                                                 */
+fp8bs_status fp8bs_gemm_swiglu_select_config(int64_t m, int64_t n, int64_t k,
+                                             fp8bs_gemm_config* out);
+
+/* Workspace bytes of the fused call for cfg (NULL = the automatic choice);
+ * 0 for shapes it rejects or that need none.                                */
+size_t fp8bs_gemm_swiglu_workspace_bytes(const fp8bs_gemm_config* cfg, int64_t m, int64_t n,
+                                         int64_t k);
+
 /* ---- utilities ----------------------------------------------------------- */
 
 /* Encode fp32 values to E4M3 codes with the quantizers' rounding rule
@@ -200,7 +272,8 @@ const char* fp8bs_status_string(fp8bs_status s);
 
 /* Host-side count of launches of each kernel family since load: 0 = weight
  * quantizer, 1 = activation quantizer, 2 = MFMA GEMM, 3 = DOT GEMM,
- * 4 = split reduce, 5 = encoder utility, 6 = read/copy diagnostics.
+ * 4 = split reduce (plain or with the SwiGLU epilogue), 5 = encoder utility,
+ * 6 = read/copy diagnostics, 7 = standalone SwiGLU epilogue.
  * Lets a caller check that the kernels it benchmarks actually ran.          */
 uint64_t fp8bs_launch_count(int32_t which);
 

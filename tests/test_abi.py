@@ -161,3 +161,59 @@ def test_config_table_is_a_pure_function_of_shape(lib):
             assert s[0] <= 4
     with pytest.raises(fp8bs.Fp8bsError):
         fp8bs.select_config(8, 100, 128)
+
+
+def swiglu(lib, x=P, m=8, w=P, ws=P, n=1024, k=1024, y=P, hq=P, hs=P, work=P, wbytes=1 << 20):
+    return lib.fp8bs_gemm_swiglu(x, m, w, ws, n, k, y, hq, hs, work, wbytes, None)
+
+
+def test_swiglu_argument_errors_before_any_launch(lib):
+    """The fused up/gate + SwiGLU call and the standalone epilogue check
+    their arguments in the documented order before touching the device."""
+    assert swiglu(lib, n=640) == E_SHAPE        # n/2 not a multiple of 128
+    assert swiglu(lib, m=33) == E_SHAPE
+    assert swiglu(lib, k=1000) == E_SHAPE
+    assert swiglu(lib, x=None) == E_NULL
+    assert swiglu(lib, hq=None) == E_NULL
+    assert swiglu(lib, hs=None) == E_NULL
+    assert swiglu(lib, y=None) == E_NULL
+    assert swiglu(lib, hq=P + 8) == E_ALIGN
+    assert swiglu(lib, hs=P + 2) == E_ALIGN
+    assert swiglu(lib, k=17408, work=None, wbytes=0) == E_WS   # split-K partials
+    assert swiglu(lib, m=0, x=None, y=None, hq=None, hs=None) == OK
+    assert lib.fp8bs_swiglu_quant(P, 8, 100, P, P, None) == E_SHAPE
+    assert lib.fp8bs_swiglu_quant(None, 8, 128, P, P, None) == E_NULL
+    assert lib.fp8bs_swiglu_quant(P, 8, 128, P + 4, P, None) == E_ALIGN
+    assert lib.fp8bs_swiglu_quant(None, 0, 128, None, None, None) == OK
+    import torch
+    if not torch.cuda.is_available():
+        assert swiglu(lib) == E_DEV
+        assert lib.fp8bs_swiglu_quant(P, 8, 128, P, P, None) == E_DEV
+
+
+def test_swiglu_config_rules(lib):
+    """Configurations that cannot carry the epilogue are refused; the
+    automatic choice is the plain GEMM's, with the separate epilogue."""
+    import fp8_block_scaled_fp8bs_amd as fp8bs
+    from fp8_block_scaled_fp8bs_amd import GemmConfig
+
+    def ex(cfg, n=1024, k=1024, m=8):
+        c = cfg._c()
+        return lib.fp8bs_gemm_swiglu_ex(P, None, None, m, P, P, n, k, P, P, P, P, 1 << 24,
+                                        ctypes.byref(c), None)
+    IN = fp8bs.EPILOGUE_IN_GEMM
+    assert ex(GemmConfig(2, 2, 1, 8, 5, epilogue=IN), m=2) == E_CFG          # DOT in the GEMM
+    assert ex(GemmConfig(1, 1, 1, 4, 5, split_k=4, epilogue=IN)) == E_CFG    # split in the GEMM
+    assert ex(GemmConfig(1, 1, 1, 4, 5, split_k=4, reduce=1)) == E_CFG       # last-arriver
+    assert ex(GemmConfig(3, 2, 1, 8, 2, epilogue=IN)) == E_CFG               # rows shape not compiled
+    assert ex(GemmConfig(1, 1, 1, 4, 5, epilogue=2)) == E_CFG                # unknown placement
+    for m in (1, 2, 3, 8, 16, 32):
+        for n, k in ((34816, 5120), (5120, 5120), (1024, 17408), (256, 128)):
+            c = fp8bs.swiglu_select_config(m, n, k)
+            assert c == fp8bs.select_config(m, n, k) and c.epilogue == fp8bs.EPILOGUE_SEPARATE
+            need = fp8bs.swiglu_workspace_bytes(m, n, k)
+            assert need == (c.split_k * m * n * 4 if c.split_k > 1 else 0)
+            cin = GemmConfig(1, 1, 1, 4, 5, epilogue=IN)
+            assert fp8bs.swiglu_workspace_bytes(m, n, k, cin) >= (n // 256) * 8
+    with pytest.raises(fp8bs.Fp8bsError):
+        fp8bs.swiglu_select_config(8, 384, 128)
