@@ -30,7 +30,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "µs/GEMM and achieved HBM GB/s (% of 8 TB/s) at M=8, K=5120 FP8 block-scaled"
 HBM_PEAK_GBPS = 8000.0
-PATH_NAMES = {1: "mfma", 2: "dot", 3: "mfma_rows", 4: "mfma_stream"}
+PATH_NAMES = {5: "prefill", 1: "mfma", 2: "dot", 3: "mfma_rows", 4: "mfma_stream"}
 FP8_DENSE_PEAK_TFLOPS = 5000.0
 
 WORKLOAD_DESCR = {
@@ -184,6 +184,48 @@ def step_mix(args, fp8bs, dev) -> int:
     return 0
 
 
+def library_reference(args, x, n, k, gen, dev, stream) -> dict:
+    """The same product with bf16 weights through torch.nn.functional.linear
+    (hipBLASLt on ROCm), timed the same way as the kernel under test: a
+    captured graph of calls over a rotating pool of distinct weights of at
+    least --pool-gib GiB (one weight when a single one is larger)."""
+    import torch
+
+    m = x.shape[0]
+    bf_bytes = 2 * n * k
+    count = max(1, math.ceil(args.pool_gib * (1 << 30) / bf_bytes))
+    pool = [(torch.randn((n, k), generator=gen, device=dev, dtype=torch.float32) * 0.02)
+            .to(torch.bfloat16) for _ in range(count)]
+    steps = max(10, min(200, args.steps // 2))
+
+    def run():
+        for i in range(steps):
+            torch.nn.functional.linear(x, pool[i % count])
+
+    run()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            run()
+    stream.wait_stream(cap)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    nbytes = bf_bytes + 2 * m * k + 2 * m * n
+    del g, pool
+    return {"op": "torch.nn.functional.linear, bf16 weights (hipBLASLt)", "us_per_gemm": round(us, 3),
+            "GBps": round(nbytes / (us * 1e3), 1), "bytes": nbytes, "weight_pool": count,
+            "timing": "hip graph of the calls, replayed"}
+
+
 def mlp_swiglu(args, fp8bs, dev) -> int:
     """MLP up/gate projection with the SwiGLU epilogue and the FP8 cast of its
     output (one fp8bs_gemm_swiglu call), at every M of the step mix, on the
@@ -274,6 +316,86 @@ def mlp_swiglu(args, fp8bs, dev) -> int:
     return 0
 
 
+MFMA_FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 matrix peak
+
+
+def prefill(args, fp8bs, dev) -> int:
+    """Prefill sizes (m > 32: the tiled matrix-core kernel, activations cast
+    first): the square, MLP-up and MLP-down weight shapes at several m. Times
+    the fused call (cast + GEMM, two kernels) and the GEMM on pre-quantized
+    activations, each as a captured graph of calls over a rotating weight
+    pool, plus torch.nn.functional.linear with bf16 weights (hipBLASLt) on the
+    same shape. One JSON line per (shape, m), with TFLOP/s = 2 m n k / time
+    against the dense FP8 peak."""
+    import torch
+
+    from workloads import WORKLOADS
+
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, steps):
+        for i in range(2):
+            fn(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                for i in range(steps):
+                    fn(i)
+        stream.wait_stream(cap)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        best = float("inf")
+        for _ in range(3):
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) * 1e3 / steps)
+        return best
+
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1600)
+    for name in args.prefill_shapes.split(","):
+        wl = WORKLOADS[name]
+        n, k = wl.n, wl.k
+        count = max(1, math.ceil(args.pool_gib * (1 << 30) / (n * k)))
+        pool = []
+        for _ in range(count):
+            w = (torch.randn((n, k), generator=gen, device=dev, dtype=torch.float32) * 0.02).to(torch.bfloat16)
+            pool.append(fp8bs.quantize_weight(w))
+            del w
+        wbf = (torch.randn((n, k), generator=gen, device=dev, dtype=torch.float32) * 0.02).to(torch.bfloat16)
+        P = len(pool)
+        for m in [int(v) for v in args.prefill_m.split(",")]:
+            x = torch.randn((m, k), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+            xq, xs = fp8bs.quantize_act(x)
+            y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            work = torch.empty(max(fp8bs.workspace_bytes(m, n, k), 16), dtype=torch.uint8, device=dev)
+            flop = 2.0 * m * n * k
+            steps = max(5, min(50, int(2e13 / flop)))
+            t_fused = timed(lambda i: fp8bs.gemm(x, pool[i % P][0], pool[i % P][1], out=y,
+                                                 workspace=work), steps)
+            t_q = timed(lambda i: fp8bs.gemm_q(xq, xs, pool[i % P][0], pool[i % P][1], out=y), steps)
+            t_lib = timed(lambda i: torch.nn.functional.linear(x, wbf), steps)
+            cfg = fp8bs.select_config(m, n, k)
+            print(json.dumps({
+                "mode": "prefill", "shape": name, "m": m, "n": n, "k": k,
+                "path": PATH_NAMES.get(cfg.path, str(cfg.path)),
+                "us_fused_call": round(t_fused, 2), "TFLOPs_fused_call": round(flop / (t_fused * 1e6), 1),
+                "us_gemm_q": round(t_q, 2), "TFLOPs_gemm_q": round(flop / (t_q * 1e6), 1),
+                "pct_of_fp8_peak_gemm_q": round(100 * flop / (t_q * 1e6) / MFMA_FP8_PEAK_TFLOPS, 2),
+                "bf16_library_us": round(t_lib, 2), "bf16_library_TFLOPs": round(flop / (t_lib * 1e6), 1),
+                "timing": f"captured graph of {steps} calls over a {P}-weight pool, best of 3 replays"}),
+                flush=True)
+            del x, xq, xs, y, work
+        del pool, wbf
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -284,6 +406,8 @@ def main() -> int:
     ap.add_argument("--pool-gib", type=float, default=1.0)
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-library-ref", action="store_true",
+                    help="skip the bf16 torch.nn.functional.linear reference")
     ap.add_argument("--eager-only", action="store_true", help="time stream launches only")
     ap.add_argument("--diag-copy-mib", type=int, default=0,
                     help="run only the plain copy kernel over this many MiB (counter calibration)")
@@ -291,6 +415,11 @@ def main() -> int:
                     help="decode-step mix: 256 GEMMs over the four shapes per step, at every M; "
                          "prints one JSON line per M")
     ap.add_argument("--step-m", default="1,2,4,8,16,32", help="M values of the step mix")
+    ap.add_argument("--prefill", action="store_true",
+                    help="prefill sizes (m > 32) on the square and MLP shapes; one JSON line each")
+    ap.add_argument("--prefill-m", default="128,512,2048,8192", help="m values of --prefill")
+    ap.add_argument("--prefill-shapes", default="square,mlp_up,mlp_down",
+                    help="weight shapes of --prefill")
     ap.add_argument("--mlp-swiglu", action="store_true",
                     help="MLP up/gate projection with the SwiGLU epilogue at every M; "
                          "prints one JSON line per M")
@@ -318,6 +447,8 @@ def main() -> int:
         return step_mix(args, fp8bs, dev)
     if args.mlp_swiglu:
         return mlp_swiglu(args, fp8bs, dev)
+    if args.prefill:
+        return prefill(args, fp8bs, dev)
 
     if args.diag_copy_mib:
         nbytes = args.diag_copy_mib << 20
@@ -427,6 +558,9 @@ def main() -> int:
     read_us = r0.elapsed_time(r1) * 1e3 / reps
     read_gbps = code_bytes / (read_us * 1e3)
 
+    # --- library reference: the same product in bf16 through torch (hipBLASLt)
+    lib_ref = None if args.no_library_ref else library_reference(args, x, n, k, gen, dev, stream)
+
     step_ms = graph_ms if graph_ms is not None else eager_ms
     us = step_ms * 1e3
     gbps = alg_bytes / (us * 1e3)
@@ -468,6 +602,8 @@ def main() -> int:
         "pct_of_8TBps": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "eager_us_per_gemm": round(eager_ms * 1e3, 3),
         "stream_read_ceiling_GBps": round(read_gbps, 1),
+        "bf16_library_reference": (dict(lib_ref, fp8_speedup=round(lib_ref["us_per_gemm"] / us, 2))
+                                   if lib_ref else None),
         "mfma_flops_frac": round(2 * m * n * k / (us * 1e-6) / (FP8_DENSE_PEAK_TFLOPS * 1e12), 6),
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -8,6 +8,7 @@
 
 #include "fp8bs.h"
 #include "fp8bs_diag.h"
+#include "fp8bs_prefill.h"
 #include "fp8bs_quant.h"
 #include "fp8bs_reduce.h"
 #include "fp8bs_registry.h"
@@ -88,6 +89,9 @@ std::vector<KernelEntry>& kernel_registry() {
 
 namespace {
 
+constexpr int64_t kMaxDecodeM = 32;       // activation rows of the decode kernels (paths 1-4)
+constexpr int64_t kMaxM = (int64_t)1 << 20;  // activation rows of the prefill path
+
 // Row-range paths: one workgroup per compute unit, n split over them.
 inline bool is_row_range(int path) {
   return path == FP8BS_PATH_MFMA_ROWS || path == FP8BS_PATH_MFMA_STREAM;
@@ -110,6 +114,11 @@ const KernelEntry* find_kernel(const fp8bs_gemm_config& c, int m, bool fused,
   } else if (c.path == FP8BS_PATH_DOT) {
     if (m > 4) return nullptr;
     mt = m <= 1 ? 1 : (m <= 2 ? 2 : 4);
+  } else if (c.path == FP8BS_PATH_PREFILL) {
+    // one kernel; it reads activation codes (the fused call casts them first)
+    for (const KernelEntry& e : kernel_registry())
+      if (e.path == FP8BS_PATH_PREFILL && !swiglu) return &e;
+    return nullptr;
   } else {
     return nullptr;
   }
@@ -126,6 +135,7 @@ const KernelEntry* find_kernel(const fp8bs_gemm_config& c, int m, bool fused,
 // path divides n by the compute-unit count at launch instead).
 int config_rows(const fp8bs_gemm_config& c) {
   if (is_row_range(c.path)) return 4;
+  if (c.path == FP8BS_PATH_PREFILL) return PF_TILE;
   return (c.path == FP8BS_PATH_DOT ? 8 : 16) * c.tiles_n * c.waves_n;
 }
 
@@ -139,6 +149,7 @@ int rows_per_workgroup(int64_t n, int num_cu) {
 
 size_t config_lds_bytes(const fp8bs_gemm_config& c, int m, int64_t n, int kbn, int num_cu,
                         bool swiglu = false) {
+  if (c.path == FP8BS_PATH_PREFILL) return (size_t)PF_LDS_BYTES;
   const int mt = m <= 16 ? 1 : 2;
   if (is_row_range(c.path)) {
     // weight scales of the row range first, then the kernel's own layout,
@@ -225,8 +236,21 @@ bool candidate_fits(const Candidate& cd, int64_t m, int64_t n, int kbn, fp8bs_ge
 // growing split catches everything else. The SwiGLU call (swiglu set) uses
 // the same choice with the separate epilogue, so its y equals fp8bs_gemm's.
 bool select_config(int64_t m, int64_t n, int64_t k, fp8bs_gemm_config* out, bool swiglu = false) {
-  if (m < 0 || m > 32 || n < 0 || k < 0 || n % BLK || k % BLK) return false;
+  if (m < 0 || m > kMaxM || n < 0 || k < 0 || n % BLK || k % BLK) return false;
   if (swiglu && n % (2 * BLK)) return false;
+  if (m > kMaxDecodeM && n > 0 && k > 0) {
+    // prefill sizes: the tiled kernel (2 x 2 waves, two LDS stages), with K
+    // split when the 128 x 128 output tiles alone cannot fill the compute
+    // units (each split keeps at least two K blocks)
+    const int64_t tiles = (n / PF_TILE) * ((m + PF_TILE - 1) / PF_TILE);
+    int64_t split = (kTableCUs + tiles - 1) / tiles;
+    const int64_t kblocks = k / BLK;
+    const int64_t max_split = kblocks / 2 < 16 ? kblocks / 2 : 16;
+    split = split < max_split ? split : max_split;
+    split = split < 1 ? 1 : split;
+    *out = make_cfg(FP8BS_PATH_PREFILL, 1, 2, 2, 2, (int)split);
+    return true;
+  }
   const int kbn = (int)(k / BLK);
   const int64_t nbn = n / BLK;
   if (m == 0 || n == 0 || kbn == 0) {
@@ -288,7 +312,19 @@ size_t cfg_partial_bytes(const fp8bs_gemm_config& c, int64_t m, int64_t n) {
   return c.split_k > 1 ? (size_t)c.split_k * (size_t)m * (size_t)n * sizeof(float) : 0;
 }
 
-size_t cfg_workspace(const fp8bs_gemm_config& c, int64_t m, int64_t n) {
+// Prefill path, fused cast: the activation codes [m][k] and scales [m][k/128]
+// are written to the workspace first.
+size_t prefill_x_bytes(int64_t m, int64_t k) {
+  return (size_t)((m * k + 255) / 256 * 256) + (size_t)((m * (k / BLK) * 4 + 15) / 16 * 16);
+}
+
+// Prefill workspace: the cast activations (fused call), then the split partials.
+size_t prefill_workspace(const fp8bs_gemm_config& c, int64_t m, int64_t n, int64_t k, bool fused) {
+  return (fused ? prefill_x_bytes(m, k) : 0) + cfg_partial_bytes(c, m, n);
+}
+
+size_t cfg_workspace(const fp8bs_gemm_config& c, int64_t m, int64_t n, int64_t k, bool fused) {
+  if (c.path == FP8BS_PATH_PREFILL) return prefill_workspace(c, m, n, k, fused);
   size_t b = cfg_partial_bytes(c, m, n);
   if (c.split_k > 1 && c.reduce == FP8BS_REDUCE_LAST_ARRIVER) {
     const int rows = config_rows(c);
@@ -299,7 +335,8 @@ size_t cfg_workspace(const fp8bs_gemm_config& c, int64_t m, int64_t n) {
 
 // SwiGLU workspace: the split partials, or (epilogue inside the GEMM) one
 // 64-bit arrival counter per 128-column block of h.
-size_t swiglu_workspace(const fp8bs_gemm_config& c, int64_t m, int64_t n) {
+size_t swiglu_workspace(const fp8bs_gemm_config& c, int64_t m, int64_t n, int64_t k, bool fused) {
+  if (c.path == FP8BS_PATH_PREFILL) return prefill_workspace(c, m, n, k, fused);
   if (c.split_k > 1) return cfg_partial_bytes(c, m, n);
   if (c.epilogue != FP8BS_EPILOGUE_IN_GEMM) return 0;
   return (size_t)((n / (2 * BLK)) * sizeof(uint64_t) + 15) / 16 * 16;
@@ -325,9 +362,9 @@ fp8bs_status gemm_impl(const void* x_bf16, const uint8_t* x_fp8, const float* x_
                        const fp8bs_gemm_config* cfg_in, void* stream, bool swiglu = false,
                        uint8_t* h_fp8 = nullptr, float* h_scale = nullptr) {
   // shapes
-  if (m < 0 || m > 32 || n < 0 || k < 0 || n % BLK || k % BLK) return FP8BS_ERR_SHAPE;
+  if (m < 0 || m > kMaxM || n < 0 || k < 0 || n % BLK || k % BLK) return FP8BS_ERR_SHAPE;
   if (n / BLK > (int64_t)1 << 24 || k / BLK > (int64_t)1 << 20) return FP8BS_ERR_SHAPE;
-  if (swiglu && n % (2 * BLK)) return FP8BS_ERR_SHAPE;
+  if (swiglu && (n % (2 * BLK) || m > 65535)) return FP8BS_ERR_SHAPE;  // one epilogue wave row per m
   if (m == 0 || n == 0) return FP8BS_OK;
   const bool fused = x_bf16 != nullptr;
   // pointers
@@ -368,6 +405,8 @@ fp8bs_status gemm_impl(const void* x_bf16, const uint8_t* x_fp8, const float* x_
     return FP8BS_ERR_SHAPE;
   }
   if (c.split_k < 1 || c.split_k > 64 || c.split_k > kbn) return FP8BS_ERR_CONFIG;
+  if (c.path == FP8BS_PATH_PREFILL ? c.reduce != FP8BS_REDUCE_KERNEL : m > kMaxDecodeM)
+    return FP8BS_ERR_CONFIG;
   if (is_row_range(c.path) && (c.split_k != 1 || c.waves_n != 1)) return FP8BS_ERR_CONFIG;
   if (c.path == FP8BS_PATH_MFMA_STREAM && !stream_offsets_fit(m, k)) return FP8BS_ERR_CONFIG;
   if (c.reduce != FP8BS_REDUCE_KERNEL && c.reduce != FP8BS_REDUCE_LAST_ARRIVER)
@@ -376,12 +415,14 @@ fp8bs_status gemm_impl(const void* x_bf16, const uint8_t* x_fp8, const float* x_
   const bool in_gemm = swiglu && c.epilogue == FP8BS_EPILOGUE_IN_GEMM;
   const bool split = c.split_k > 1;
   const bool last_arriver = split && c.reduce == FP8BS_REDUCE_LAST_ARRIVER;
-  const KernelEntry* ke = find_kernel(c, (int)m, fused, in_gemm);
+  const bool prefill = c.path == FP8BS_PATH_PREFILL;
+  const KernelEntry* ke = find_kernel(c, (int)m, fused && !prefill, in_gemm);
   if (!ke) return FP8BS_ERR_CONFIG;
   const int rows = config_rows(c);
   if (n % rows) return FP8BS_ERR_CONFIG;
   // workspace
-  const size_t need = swiglu ? swiglu_workspace(c, m, n) : cfg_workspace(c, m, n);
+  const size_t need =
+      swiglu ? swiglu_workspace(c, m, n, k, fused) : cfg_workspace(c, m, n, k, fused);
   if (need > 0) {
     if (!workspace || workspace_bytes < need) return FP8BS_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return FP8BS_ERR_ALIGN;
@@ -433,7 +474,30 @@ fp8bs_status gemm_impl(const void* x_bf16, const uint8_t* x_fp8, const float* x_
   if (in_gemm && 2 * ((is_row_range(c.path) ? p.rows_per_wg : rows) / BLK + 2) >
                      SWIGLU_MAX_ARRIVALS)
     return FP8BS_ERR_CONFIG;
-  const dim3 block(64 * (is_row_range(c.path) ? 1 : c.waves_n) * c.waves_k);
+  dim3 block(64 * (is_row_range(c.path) ? 1 : c.waves_n) * c.waves_k);
+  if (prefill) {
+    grid = dim3((unsigned)(n / PF_TILE), (unsigned)((m + PF_TILE - 1) / PF_TILE),
+                (unsigned)c.split_k);
+    block = dim3(256);
+    p.part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
+                                      (fused ? prefill_x_bytes(m, k) : 0));
+    if (fused) {
+      // cast the activations into the workspace: codes, then scales
+      uint8_t* xq = static_cast<uint8_t*>(workspace);
+      float* xs = reinterpret_cast<float*>(xq + (m * k + 255) / 256 * 256);
+      const uint16_t* xb = static_cast<const uint16_t*>(x_bf16);
+      int64_t nb = m * kbn, kk = k;
+      void* qargs[] = {&xb, &nb, &kk, &xq, &xs};
+      g_counts[CNT_QA]++;
+      const fp8bs_status qs = launch(reinterpret_cast<const void*>(quant_act_kernel),
+                                     dim3((unsigned)((nb * 4 + 255) / 256)), dim3(256), 0, stream,
+                                     qargs);
+      if (qs != FP8BS_OK) return qs;
+      p.x = nullptr;
+      p.xq = xq;
+      p.xs = xs;
+    }
+  }
   g_counts[c.path == FP8BS_PATH_DOT ? CNT_DOT : CNT_MFMA]++;
   fp8bs_status ls = launch(reinterpret_cast<const void*>(ke->fn), grid, block, lds, stream, args);
   if (ls != FP8BS_OK || last_arriver || in_gemm) return ls;
@@ -501,7 +565,7 @@ fp8bs_status fp8bs_gemm(const void* x_bf16, int64_t m, const uint8_t* w_fp8, con
                         size_t workspace_bytes, void* stream) {
   if (!x_bf16 && m > 0 && n > 0 && k > 0) {
     // the shape checks come first; a NULL activation pointer is a NULL error
-    if (m > 32 || n % BLK || k % BLK) return FP8BS_ERR_SHAPE;
+    if (m > kMaxM || n % BLK || k % BLK) return FP8BS_ERR_SHAPE;
     return FP8BS_ERR_NULL;
   }
   return gemm_impl(x_bf16, nullptr, nullptr, m, w_fp8, w_scale, n, k, y_bf16, workspace,
@@ -518,7 +582,8 @@ fp8bs_status fp8bs_gemm_q(const uint8_t* x_fp8, const float* x_scale, int64_t m,
 size_t fp8bs_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k) {
   fp8bs_gemm_config c;
   if (!select_config(m, n, k, &c)) return 0;
-  return cfg_workspace(c, m, n);
+  if (m == 0 || n == 0 || k == 0) return 0;
+  return cfg_workspace(c, m, n, k, true);
 }
 
 fp8bs_status fp8bs_gemm_select_config(int64_t m, int64_t n, int64_t k, fp8bs_gemm_config* out) {
@@ -529,9 +594,8 @@ fp8bs_status fp8bs_gemm_select_config(int64_t m, int64_t n, int64_t k, fp8bs_gem
 
 size_t fp8bs_gemm_config_workspace_bytes(const fp8bs_gemm_config* cfg, int64_t m, int64_t n,
                                          int64_t k) {
-  (void)k;
-  if (!cfg || m < 0 || n < 0) return 0;
-  return cfg_workspace(*cfg, m, n);
+  if (!cfg || m <= 0 || n <= 0 || k <= 0) return 0;
+  return cfg_workspace(*cfg, m, n, k, true);
 }
 
 fp8bs_status fp8bs_gemm_ex(const void* x_bf16, const uint8_t* x_fp8, const float* x_scale,
@@ -560,7 +624,7 @@ fp8bs_status fp8bs_gemm_swiglu(const void* x_bf16, int64_t m, const uint8_t* w_f
                                uint8_t* h_fp8, float* h_scale, void* workspace,
                                size_t workspace_bytes, void* stream) {
   if (!x_bf16 && m > 0 && n > 0 && k > 0) {
-    if (m > 32 || n % (2 * BLK) || k % BLK) return FP8BS_ERR_SHAPE;
+    if (m > kMaxM || n % (2 * BLK) || k % BLK) return FP8BS_ERR_SHAPE;
     return FP8BS_ERR_NULL;
   }
   return gemm_impl(x_bf16, nullptr, nullptr, m, w_fp8, w_scale, n, k, y_bf16, workspace,
@@ -592,7 +656,7 @@ size_t fp8bs_gemm_swiglu_workspace_bytes(const fp8bs_gemm_config* cfg, int64_t m
     return 0;
   }
   if (m <= 0 || n <= 0 || k <= 0 || n % (2 * BLK)) return 0;
-  return swiglu_workspace(c, m, n);
+  return swiglu_workspace(c, m, n, k, true);
 }
 
 fp8bs_status fp8bs_encode_e4m3(const float* in, int64_t count, uint8_t* out, int32_t mode,

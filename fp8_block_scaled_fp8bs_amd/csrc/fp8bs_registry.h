@@ -10,7 +10,7 @@ namespace fp8bs {
 
 struct KernelEntry {
   int path;    // 1 = MFMA grid, 2 = DOT grid, 3 = MFMA row range (one workgroup per CU),
-               // 4 = MFMA streaming row range
+               // 4 = MFMA streaming row range, 5 = prefill-size tiled MFMA GEMM
   int mt;      // MFMA: 16-row activation tiles (1: m <= 16, 2: m <= 32); DOT: max m
   int tn;      // MFMA: 16-row weight tiles per wave; DOT: 8-row groups per wave
   int wn, wk, d;

@@ -93,7 +93,13 @@ fp8bs_status fp8bs_quantize_weight(const void* w_bf16, int64_t n, int64_t k,
 fp8bs_status fp8bs_quantize_act(const void* x_bf16, int64_t m, int64_t k,
                                 uint8_t* x_fp8, float* x_scale, void* stream);
 
-/* Y = X . W^T with the activation cast fused in; 0 <= m <= 32.
+/* Y = X . W^T with the activation cast fused in; 0 <= m <= 2^20.
+ * m <= 32 (decode) runs the bandwidth-bound kernels with the cast inside the
+ * GEMM. m > 32 (prefill, "Kernel-Level Optimisations for LLM Inference and
+ * Training", section "Start with the bound: memory or compute") runs the
+ * tiled matrix-core kernel: the activations are first cast into the
+ * workspace (m*k code bytes, padded to 256, then m*k/128 fp32 scales), with
+ * the same rule as fp8bs_quantize_act.
  *   x_bf16  [m][k] bf16; w_fp8 [n][k] codes; w_scale [n/128][k/128] fp32;
  *   y_bf16  [m][n] bf16, out.
  *   workspace: device scratch of at least fp8bs_gemm_workspace_bytes(m,n,k)
@@ -108,7 +114,8 @@ fp8bs_status fp8bs_gemm(const void* x_bf16, int64_t m,
 /* Same product from already-quantized activations (codes [m][k] and scales
  * [m][k/128] as produced by fp8bs_quantize_act). With the same shape it runs
  * the same kernel configuration as fp8bs_gemm, so
- * fp8bs_gemm(x) == fp8bs_gemm_q(fp8bs_quantize_act(x)) bit for bit.        */
+ * fp8bs_gemm(x) == fp8bs_gemm_q(fp8bs_quantize_act(x)) bit for bit. It needs
+ * no workspace on the prefill path.                                         */
 fp8bs_status fp8bs_gemm_q(const uint8_t* x_fp8, const float* x_scale, int64_t m,
                           const uint8_t* w_fp8, const float* w_scale, int64_t n, int64_t k,
                           void* y_bf16, void* workspace, size_t workspace_bytes,
@@ -126,7 +133,8 @@ enum {
   FP8BS_PATH_MFMA = 1,
   FP8BS_PATH_DOT = 2,
   FP8BS_PATH_MFMA_ROWS = 3,
-  FP8BS_PATH_MFMA_STREAM = 4
+  FP8BS_PATH_MFMA_STREAM = 4,
+  FP8BS_PATH_PREFILL = 5
 };
 enum { FP8BS_REDUCE_KERNEL = 0, FP8BS_REDUCE_LAST_ARRIVER = 1 };
 enum { FP8BS_EPILOGUE_SEPARATE = 0, FP8BS_EPILOGUE_IN_GEMM = 1 };
@@ -141,7 +149,11 @@ enum { FP8BS_EPILOGUE_SEPARATE = 0, FP8BS_EPILOGUE_IN_GEMM = 1 };
  *             waves_n and split_k must be 1), or MFMA_STREAM (the work split
  *             of MFMA_ROWS without a staging phase: each wave casts the
  *             activation blocks it uses as the first tile reaches them;
- *             tiles_n, waves_n and split_k must be 1; needs m*k*2 < 2^31)
+ *             tiles_n, waves_n and split_k must be 1; needs m*k*2 < 2^31), or
+ *             PREFILL (any m: workgroups of 4 waves own 128 x 128 output
+ *             tiles and step through K in 128-deep blocks staged in LDS;
+ *             split_k must be 1, the other fields are not used). Paths 1-4
+ *             take m <= 32.
  *   tiles_n   MFMA: 16-row tiles per wave (1, 2, 4); DOT: 8-row groups per wave (1, 2, 4)
  *   waves_n   waves side by side along N in one workgroup (1, 2, 4)
  *   waves_k   waves splitting a workgroup's K range (1, 2, 4, 8); their
@@ -222,7 +234,7 @@ fp8bs_status fp8bs_swiglu_quant(const void* y_bf16, int64_t m, int64_t inter, ui
  * exactly as fp8bs_gemm computes it (written to y_bf16, [m][n]; with the
  * same kernel configuration the bits are identical), and h_fp8 / h_scale as
  * fp8bs_swiglu_quant(y) gives them, bit for bit. n = 2*inter must be a
- * multiple of 256; 0 <= m <= 32. The automatic choice is fp8bs_gemm's
+ * multiple of 256; 0 <= m <= 65535. The automatic choice is fp8bs_gemm's
  * configuration with FP8BS_EPILOGUE_SEPARATE (the faster way at decode sizes
  * on MI355X: the epilogue rides on the split-sum kernel when K is split, and
  * takes a second small kernel otherwise). The workspace holds the split

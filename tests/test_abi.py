@@ -84,7 +84,8 @@ def gemm(lib, x=P, m=8, w=P, ws=P, n=512, k=1024, y=P, work=None, wbytes=0):
 def test_gemm_argument_errors_before_any_launch(lib):
     assert gemm(lib, n=500) == E_SHAPE
     assert gemm(lib, k=1000) == E_SHAPE
-    assert gemm(lib, m=33) == E_SHAPE
+    assert gemm(lib, m=(1 << 20) + 1) == E_SHAPE
+    assert gemm(lib, m=33) == E_WS       # prefill sizes cast X into the workspace first
     assert gemm(lib, m=-1) == E_SHAPE
     assert gemm(lib, x=None) == E_NULL
     assert gemm(lib, w=None) == E_NULL
@@ -171,7 +172,7 @@ def test_swiglu_argument_errors_before_any_launch(lib):
     """The fused up/gate + SwiGLU call and the standalone epilogue check
     their arguments in the documented order before touching the device."""
     assert swiglu(lib, n=640) == E_SHAPE        # n/2 not a multiple of 128
-    assert swiglu(lib, m=33) == E_SHAPE
+    assert swiglu(lib, m=(1 << 20) + 1) == E_SHAPE
     assert swiglu(lib, k=1000) == E_SHAPE
     assert swiglu(lib, x=None) == E_NULL
     assert swiglu(lib, hq=None) == E_NULL

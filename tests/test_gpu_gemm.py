@@ -333,4 +333,4 @@ def test_errors_raise(fp8bs):
     pr = _random_problem(fp8bs, 8, 256, 256, 4)
     with pytest.raises(fp8bs.Fp8bsError):
         bad = torch.zeros((40, 256), dtype=torch.bfloat16, device="cuda")
-        fp8bs.gemm(bad, pr.wq, pr.ws)  # m > 32
+        fp8bs.gemm_ex(fp8bs.GemmConfig(1, 1, 1, 4, 5), pr.wq, pr.ws, x=bad)  # decode kernel, m > 32
