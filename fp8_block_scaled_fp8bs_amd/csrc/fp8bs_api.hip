@@ -117,7 +117,7 @@ const KernelEntry* find_kernel(const fp8bs_gemm_config& c, int m, bool fused,
   } else if (c.path == FP8BS_PATH_PREFILL) {
     // one kernel; it reads activation codes (the fused call casts them first)
     for (const KernelEntry& e : kernel_registry())
-      if (e.path == FP8BS_PATH_PREFILL && !swiglu) return &e;
+      if (e.path == FP8BS_PATH_PREFILL && !swiglu && e.wn == c.waves_n && e.d == c.depth) return &e;
     return nullptr;
   } else {
     return nullptr;
@@ -135,7 +135,7 @@ const KernelEntry* find_kernel(const fp8bs_gemm_config& c, int m, bool fused,
 // path divides n by the compute-unit count at launch instead).
 int config_rows(const fp8bs_gemm_config& c) {
   if (is_row_range(c.path)) return 4;
-  if (c.path == FP8BS_PATH_PREFILL) return PF_TILE;
+  if (c.path == FP8BS_PATH_PREFILL) return pf_tile_n(c.waves_n);
   return (c.path == FP8BS_PATH_DOT ? 8 : 16) * c.tiles_n * c.waves_n;
 }
 
@@ -149,7 +149,7 @@ int rows_per_workgroup(int64_t n, int num_cu) {
 
 size_t config_lds_bytes(const fp8bs_gemm_config& c, int m, int64_t n, int kbn, int num_cu,
                         bool swiglu = false) {
-  if (c.path == FP8BS_PATH_PREFILL) return (size_t)PF_LDS_BYTES;
+  if (c.path == FP8BS_PATH_PREFILL) return (size_t)pf_lds_bytes(c.waves_n);
   const int mt = m <= 16 ? 1 : 2;
   if (is_row_range(c.path)) {
     // weight scales of the row range first, then the kernel's own layout,
@@ -239,16 +239,21 @@ bool select_config(int64_t m, int64_t n, int64_t k, fp8bs_gemm_config* out, bool
   if (m < 0 || m > kMaxM || n < 0 || k < 0 || n % BLK || k % BLK) return false;
   if (swiglu && n % (2 * BLK)) return false;
   if (m > kMaxDecodeM && n > 0 && k > 0) {
-    // prefill sizes: the tiled kernel (2 x 2 waves, two LDS stages), with K
-    // split when the 128 x 128 output tiles alone cannot fill the compute
-    // units (each split keeps at least two K blocks)
-    const int64_t tiles = (n / PF_TILE) * ((m + PF_TILE - 1) / PF_TILE);
-    int64_t split = (kTableCUs + tiles - 1) / tiles;
+    // prefill sizes: the tiled kernel. 8 waves on 256 x 128 output tiles
+    // where n allows and those tiles fill the compute units at least once;
+    // otherwise 4 waves on 128 x 128 tiles (two workgroups per unit), with K
+    // split when the tiles alone cannot fill the units (each split keeps at
+    // least two K blocks). Measured on MI355X at m = 128 .. 8192.
+    const int64_t mtiles = (m + PF_TILE_M - 1) / PF_TILE_M;
+    const bool wide = n % pf_tile_n(4) == 0 && (n / pf_tile_n(4)) * mtiles >= kTableCUs;
+    const int wn = wide ? 4 : 2;
+    const int64_t tiles = (n / pf_tile_n(wn)) * mtiles;
+    int64_t split = wide ? 1 : (kTableCUs + tiles - 1) / tiles;
     const int64_t kblocks = k / BLK;
     const int64_t max_split = kblocks / 2 < 16 ? kblocks / 2 : 16;
     split = split < max_split ? split : max_split;
     split = split < 1 ? 1 : split;
-    *out = make_cfg(FP8BS_PATH_PREFILL, 1, 2, 2, 2, (int)split);
+    *out = make_cfg(FP8BS_PATH_PREFILL, 1, wn, 2, 1, (int)split);
     return true;
   }
   const int kbn = (int)(k / BLK);
@@ -476,9 +481,9 @@ fp8bs_status gemm_impl(const void* x_bf16, const uint8_t* x_fp8, const float* x_
     return FP8BS_ERR_CONFIG;
   dim3 block(64 * (is_row_range(c.path) ? 1 : c.waves_n) * c.waves_k);
   if (prefill) {
-    grid = dim3((unsigned)(n / PF_TILE), (unsigned)((m + PF_TILE - 1) / PF_TILE),
+    grid = dim3((unsigned)(n / pf_tile_n(c.waves_n)), (unsigned)((m + PF_TILE_M - 1) / PF_TILE_M),
                 (unsigned)c.split_k);
-    block = dim3(256);
+    block = dim3(128 * c.waves_n);
     p.part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
                                       (fused ? prefill_x_bytes(m, k) : 0));
     if (fused) {

@@ -1,9 +1,11 @@
-// The prefill-size GEMM kernel registered in the kernel table.
+// The prefill-size GEMM kernels registered in the kernel table: 4 waves on
+// 128 x 128 output tiles and 8 waves on 256 x 128 tiles.
 #include "fp8bs_prefill.h"
 #include "fp8bs_registry.h"
 
 namespace fp8bs {
 static KernelRegistrar reg_prefill({
-    {5, 1, 1, 2, 1, 2, 0, gemm_prefill_kernel<0>, 0},
+    {5, 1, 1, 2, 2, 1, 0, gemm_prefill_kernel<2>, 0},
+    {5, 1, 1, 4, 2, 1, 0, gemm_prefill_kernel<4>, 0},
 });
 }  // namespace fp8bs

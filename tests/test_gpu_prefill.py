@@ -56,6 +56,23 @@ def test_prefill_parity_full_output(fp8bs, m, n, k):
     assert np.array_equal(host_bits(y), host_bits(y_q)), "fused cast differs from quantize-then-multiply"
 
 
+@pytest.mark.parametrize("variant", [(2, 1), (4, 1)])
+@pytest.mark.parametrize("m,n,k,split", [(300, 512, 1280, 1), (129, 768, 2048, 3), (64, 256, 384, 1)])
+def test_prefill_every_variant(fp8bs, variant, m, n, k, split):
+    """Each compiled prefill kernel (4 or 8 waves), split and unsplit, full
+    output against the oracle."""
+    from fp8_block_scaled_fp8bs_amd import GemmConfig
+    wn, depth = variant
+    cfg = GemmConfig(fp8bs.PATH_PREFILL, 1, wn, 2, depth, split)
+    announce("prefill variant", cfg, m, n, k)
+    x_bits, wq, ws, wq_ref, ws_ref = _problem(fp8bs, m, n, k, 7400 + m + n + k)
+    y = fp8bs.gemm_ex(cfg, wq, ws, x=dev_bf16(x_bits))
+    torch.cuda.synchronize()
+    xq_ref, xs_ref = oracle.quantize_act_ref(x_bits)
+    rep = oracle.tolerance_report(host_bits(y), oracle.gemm_ref(xq_ref, xs_ref, wq_ref, ws_ref), **TOL)
+    assert rep["finite"] and rep["n_bad"] == 0, rep
+
+
 def test_prefill_run_to_run_identity(fp8bs):
     m, n, k = 777, 640, 1152
     x_bits, wq, ws, _, _ = _problem(fp8bs, m, n, k, 7100)
@@ -76,7 +93,7 @@ def test_prefill_explicit_config_rules(fp8bs):
     # the prefill kernel at decode sizes too (m = 1, 8, 32)
     xq_ref, xs_ref = oracle.quantize_act_ref(x_bits)
     for mm in (1, 8, 32):
-        y = fp8bs.gemm_ex(GemmConfig(5, 1, 2, 2, 2), wq, ws, x=x[:mm].contiguous())
+        y = fp8bs.gemm_ex(GemmConfig(5, 1, 2, 2, 1), wq, ws, x=x[:mm].contiguous())
         torch.cuda.synchronize()
         ref = oracle.gemm_ref(xq_ref[:mm], xs_ref[:mm], wq_ref, ws_ref)
         rep = oracle.tolerance_report(host_bits(y), ref, **TOL)
