@@ -126,7 +126,7 @@ const KernelEntry* find_kernel(const fp8bs_gemm_config& c, int m, bool fused,
   for (const KernelEntry& e : kernel_registry())
     if (e.path == c.path && e.mt == mt && e.tn == c.tiles_n && (rows || e.wn == c.waves_n) &&
         e.wk == c.waves_k && e.d == c.depth && e.fused == (int)fused &&
-        e.swiglu == (int)(swiglu && rows))
+        e.variant == (rows ? (swiglu ? 1 : (c.split_k > 1 ? 2 : 0)) : 0))
       return &e;
   return nullptr;
 }
@@ -154,12 +154,14 @@ size_t config_lds_bytes(const fp8bs_gemm_config& c, int m, int64_t n, int kbn, i
   if (is_row_range(c.path)) {
     // weight scales of the row range first, then the kernel's own layout,
     // then (SwiGLU epilogue) the staged outputs
+    // (split: the longest K range of a workgroup)
     const int rows = rows_per_workgroup(n, num_cu);
-    const size_t ws = (size_t)lds_wscale_bytes(rows, kbn);
+    const int nblk = (kbn + c.split_k - 1) / c.split_k;
+    const size_t ws = (size_t)lds_wscale_bytes(rows, nblk);
     const size_t ys = swiglu ? (size_t)lds_ystage_bytes(m, rows) : 0;
     if (c.path == FP8BS_PATH_MFMA_STREAM)
       return ws + (size_t)lds_stream_bytes(kbn, m, c.waves_k, mt) + ys;
-    return ws + (size_t)lds_act_bytes(kbn, m) + (size_t)2 * (c.waves_k - 1) * mt * 64 * 16 + ys;
+    return ws + (size_t)lds_act_bytes(nblk, m) + (size_t)2 * (c.waves_k - 1) * mt * 64 * 16 + ys;
   }
   const int nblk = (kbn + c.split_k - 1) / c.split_k;
   size_t red = 0;
@@ -412,7 +414,11 @@ fp8bs_status gemm_impl(const void* x_bf16, const uint8_t* x_fp8, const float* x_
   if (c.split_k < 1 || c.split_k > 64 || c.split_k > kbn) return FP8BS_ERR_CONFIG;
   if (c.path == FP8BS_PATH_PREFILL ? c.reduce != FP8BS_REDUCE_KERNEL : m > kMaxDecodeM)
     return FP8BS_ERR_CONFIG;
-  if (is_row_range(c.path) && (c.split_k != 1 || c.waves_n != 1)) return FP8BS_ERR_CONFIG;
+  // row-range paths: split only on MFMA_ROWS, with the reduce kernel
+  if (is_row_range(c.path) &&
+      (c.waves_n != 1 ||
+       (c.split_k != 1 && (c.path != FP8BS_PATH_MFMA_ROWS || c.reduce != FP8BS_REDUCE_KERNEL))))
+    return FP8BS_ERR_CONFIG;
   if (c.path == FP8BS_PATH_MFMA_STREAM && !stream_offsets_fit(m, k)) return FP8BS_ERR_CONFIG;
   if (c.reduce != FP8BS_REDUCE_KERNEL && c.reduce != FP8BS_REDUCE_LAST_ARRIVER)
     return FP8BS_ERR_CONFIG;
@@ -472,7 +478,7 @@ fp8bs_status gemm_impl(const void* x_bf16, const uint8_t* x_fp8, const float* x_
   dim3 grid((unsigned)(n / rows), (unsigned)c.split_k);
   if (is_row_range(c.path)) {
     p.rows_per_wg = rows_per_workgroup(n, dev.num_cu);
-    grid = dim3((unsigned)((n + p.rows_per_wg - 1) / p.rows_per_wg), 1);
+    grid = dim3((unsigned)((n + p.rows_per_wg - 1) / p.rows_per_wg), (unsigned)c.split_k);
   }
   // the SwiGLU epilogue arrives on each (side, 128-column block) pair of a
   // workgroup's range at once, one lane per pair

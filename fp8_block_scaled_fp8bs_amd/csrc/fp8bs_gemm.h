@@ -651,31 +651,40 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_mfma_kernel(GemmParams p) {
 // barrier per tile) and wave 0 writes the tile's outputs.
 // ====================================================================
 
-template <int MT, int WK, int D, int PRE, bool FUSED, bool SW = false>
+// OUTK selects the output: ROWS_OUT_BF16 (bf16 y), ROWS_OUT_SWIGLU (bf16 y
+// staged in LDS, then the in-GEMM SwiGLU epilogue), ROWS_OUT_PARTIAL (K split
+// over grid.y: fp32 partial tiles part[s][m][n], summed by the reduce kernel).
+enum { ROWS_OUT_BF16 = 0, ROWS_OUT_SWIGLU = 1, ROWS_OUT_PARTIAL = 2 };
+
+template <int MT, int WK, int D, int PRE, bool FUSED, int OUTK = ROWS_OUT_BF16>
 __global__ __launch_bounds__(64 * WK) void gemm_rows_kernel(GemmParams p) {
   constexpr int NT = 64 * WK;
   constexpr int CR = FUSED ? 3 : 1;
+  constexpr bool SW = OUTK == ROWS_OUT_SWIGLU;
   extern __shared__ __align__(16) uint8_t lds_all[];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wk = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int M = p.m;
-  const int kbn = p.kbn;
+  // this workgroup's K blocks: [kb0, kb0 + nblk) (all of K unless split)
+  int kb0 = 0, kb1 = p.kbn;
+  if constexpr (OUTK == ROWS_OUT_PARTIAL) split_range(blockIdx.y, p.split, p.kbn, kb0, kb1);
+  const int nblk = kb1 - kb0;
   const int r0 = blockIdx.x * p.rows_per_wg;
   const int r1 = r0 + p.rows_per_wg < p.n ? r0 + p.rows_per_wg : p.n;
   const int nrows = r1 - r0;
   const int ntile = (nrows + 15) >> 4;
-  const int njw = (kbn + WK - 1) / WK;  // blocks per tile per wave (same for every wave)
+  const int njw = (nblk + WK - 1) / WK;  // blocks per tile per wave (same for every wave)
   const int nitem = ntile * njw;
 
   const int nbf = r0 / BLK, nbr = (r1 - 1) / BLK - nbf + 1;
   float* wsl = reinterpret_cast<float*>(lds_all);
-  uint8_t* lds = lds_all + lds_wscale_bytes(p.rows_per_wg, kbn);
+  uint8_t* lds = lds_all + lds_wscale_bytes(p.rows_per_wg, nblk);
   uint8_t* act = lds;
-  float* act_s = reinterpret_cast<float*>(lds + kbn * M * ACT_STRIDE);
-  f32x4* red = reinterpret_cast<f32x4*>(lds + lds_act_bytes(kbn, M));
-  uint16_t* ystage = reinterpret_cast<uint16_t*>(lds + lds_act_bytes(kbn, M) +
+  float* act_s = reinterpret_cast<float*>(lds + nblk * M * ACT_STRIDE);
+  f32x4* red = reinterpret_cast<f32x4*>(lds + lds_act_bytes(nblk, M));
+  uint16_t* ystage = reinterpret_cast<uint16_t*>(lds + lds_act_bytes(nblk, M) +
                                                  2 * (WK - 1) * MT * 64 * 16);
 
   const int l16 = lane & 15, g16 = lane >> 4;
@@ -685,26 +694,26 @@ __global__ __launch_bounds__(64 * WK) void gemm_rows_kernel(GemmParams p) {
   // 1. activations beyond the first CR * NT quarters (a loop with its own
   //    waits, before any other load), then the weight-scale loads and the
   //    first CR * NT quarters' loads
-  stage_act_tail<NT, CR, FUSED>(p, 0, kbn, tid, act, act_s);
+  stage_act_tail<NT, CR, FUSED>(p, kb0, nblk, tid, act, act_s);
   ScaleFetch sf;
-  load_wscales<NT>(p, nbf, nbr, 0, kbn, tid, sf);
+  load_wscales<NT>(p, nbf, nbr, kb0, nblk, tid, sf);
   uint4 xr[CR][4];
-  if constexpr (FUSED) load_act_quarters<NT, CR>(p, 0, kbn * M * 4, tid, 0, xr);
+  if constexpr (FUSED) load_act_quarters<NT, CR>(p, kb0, nblk * M * 4, tid, 0, xr);
   __builtin_amdgcn_sched_barrier(0);  // activation loads stay ahead of the weight loads
 
-  // 2. weight prefetch. Item i = (tile i / njw, block wk + (i % njw) * WK).
-  //    Rows past the range and blocks past K are clamped to valid addresses
-  //    (their products are discarded).
+  // 2. weight prefetch. Item i = (tile i / njw, block wk + (i % njw) * WK of
+  //    the range). Rows past the range and blocks past it are clamped to
+  //    valid addresses (their products are discarded).
   TileLoad wb[D];
   auto load_item = [&](int d, int i) {
     i = i < nitem ? i : nitem - 1;
     const int t = i / njw, j = i - t * njw;
-    int kb = wk + j * WK;
-    kb = kb < kbn ? kb : kbn - 1;
+    int kbl = wk + j * WK;
+    kbl = kbl < nblk ? kbl : nblk - 1;
     int ra = 16 * t + l7, rb = 16 * t + 8 + l7;
     ra = ra < nrows ? ra : nrows - 1;
     rb = rb < nrows ? rb : nrows - 1;
-    const uint8_t* base = p.wq + (size_t)kb * BLK;
+    const uint8_t* base = p.wq + (size_t)(kb0 + kbl) * BLK;
     wb[d].p = load_stream16(base + (size_t)(r0 + ra) * (size_t)p.k + 16 * (2 * g16 + hb));
     wb[d].q = load_stream16(base + (size_t)(r0 + rb) * (size_t)p.k + 16 * (2 * g16 + 1 - hb));
   };
@@ -717,7 +726,7 @@ __global__ __launch_bounds__(64 * WK) void gemm_rows_kernel(GemmParams p) {
 
   // 3. stage activations in LDS, interleaved with the rest of the prefetch
   if constexpr (FUSED) {
-    const int G = kbn * M * 4;
+    const int G = nblk * M * 4;
 #pragma unroll
     for (int c = 0; c < CR; ++c) {
       cast_act_quarters<NT, 1>(G, tid, c * NT, reinterpret_cast<const uint4(&)[1][4]>(xr[c]),
@@ -727,11 +736,11 @@ __global__ __launch_bounds__(64 * WK) void gemm_rows_kernel(GemmParams p) {
 #pragma unroll
     for (int d = PRE + CR; d < D; ++d) load_item(d, d);
   } else {
-    copy_act<NT>(p, 0, kbn, tid, act, act_s);
+    copy_act<NT>(p, kb0, nblk, tid, act, act_s);
 #pragma unroll
     for (int d = PRE; d < D; ++d) load_item(d, d);
   }
-  store_wscales<NT>(p, nbf, nbr, 0, kbn, tid, sf, wsl);
+  store_wscales<NT>(p, nbf, nbr, kb0, nblk, tid, sf, wsl);
   lds_barrier();
 
   f32x4 acc[MT];
@@ -741,14 +750,14 @@ __global__ __launch_bounds__(64 * WK) void gemm_rows_kernel(GemmParams p) {
   auto compute = [&](int d, int i) {
     const int t = i / njw, j = i - t * njw;
     const int kb = wk + j * WK;
-    if (kb < kbn) {
+    if (kb < nblk) {
       // A 16-row tile may straddle two 128-row scale blocks (row ranges are
       // multiples of 4, not of 16); each lane's four output rows lie in one.
       // this lane's four output rows lie in one 128-row scale block (row
       // ranges are multiples of 4); lanes past the range read a valid entry
       int nbl = (r0 + 16 * t + 4 * g16) / BLK - nbf;
       nbl = nbl < nbr ? nbl : nbr - 1;
-      const float sw = wsl[nbl * kbn + kb];
+      const float sw = wsl[nbl * nblk + kb];
       const i32x8 aop = tile_operand(wb[d], lo8);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
@@ -791,6 +800,10 @@ __global__ __launch_bounds__(64 * WK) void gemm_rows_kernel(GemmParams p) {
             if constexpr (SW) {
               stage_y4(ystage, p.rows_per_wg, m, rl, acc[mt][0], acc[mt][1], acc[mt][2],
                        acc[mt][3]);
+            } else if constexpr (OUTK == ROWS_OUT_PARTIAL) {
+              *reinterpret_cast<float4*>(p.part + ((size_t)blockIdx.y * M + m) * (size_t)p.n +
+                                         r0 + rl) =
+                  make_float4(acc[mt][0], acc[mt][1], acc[mt][2], acc[mt][3]);
             } else {
               uint2* dst = reinterpret_cast<uint2*>(p.y + (size_t)m * (size_t)p.n + r0 + rl);
               *dst = make_uint2(pack_bf16x2(acc[mt][0], acc[mt][1]),

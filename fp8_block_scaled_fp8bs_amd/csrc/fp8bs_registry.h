@@ -16,7 +16,7 @@ struct KernelEntry {
   int wn, wk, d;
   int fused;   // activations cast in the kernel (1) or given as codes and scales (0)
   void (*fn)(GemmParams);
-  int swiglu = 0;  // row-range kernels with the SwiGLU epilogue (1)
+  int variant = 0;  // row-range kernels: 1 = SwiGLU epilogue, 2 = K split (fp32 partials)
 };
 
 std::vector<KernelEntry>& kernel_registry();
@@ -53,11 +53,19 @@ struct KernelRegistrar {
 
 // Row-range kernels with the SwiGLU epilogue, for the configurations the
 // fused up/gate call selects.
-#define FP8BS_ROWS_SWIGLU_ENTRY(WK, D, PRE)                                       \
-  {3, 1, PRE, 1, WK, D, 1, gemm_rows_kernel<1, WK, D, PRE, true, true>, 1},       \
-  {3, 2, PRE, 1, WK, D, 1, gemm_rows_kernel<2, WK, D, PRE, true, true>, 1},       \
-  {3, 1, PRE, 1, WK, D, 0, gemm_rows_kernel<1, WK, D, PRE, false, true>, 1},      \
-  {3, 2, PRE, 1, WK, D, 0, gemm_rows_kernel<2, WK, D, PRE, false, true>, 1},
+#define FP8BS_ROWS_SWIGLU_ENTRY(WK, D, PRE)                                            \
+  {3, 1, PRE, 1, WK, D, 1, gemm_rows_kernel<1, WK, D, PRE, true, ROWS_OUT_SWIGLU>, 1},   \
+  {3, 2, PRE, 1, WK, D, 1, gemm_rows_kernel<2, WK, D, PRE, true, ROWS_OUT_SWIGLU>, 1},   \
+  {3, 1, PRE, 1, WK, D, 0, gemm_rows_kernel<1, WK, D, PRE, false, ROWS_OUT_SWIGLU>, 1},  \
+  {3, 2, PRE, 1, WK, D, 0, gemm_rows_kernel<2, WK, D, PRE, false, ROWS_OUT_SWIGLU>, 1},
+
+// Row-range kernels with K split over grid.y (fp32 partials), for m where
+// one workgroup's activations of the whole K range do not fit in LDS.
+#define FP8BS_ROWS_SPLIT_ENTRY(WK, D, PRE)                                              \
+  {3, 1, PRE, 1, WK, D, 1, gemm_rows_kernel<1, WK, D, PRE, true, ROWS_OUT_PARTIAL>, 2},   \
+  {3, 2, PRE, 1, WK, D, 1, gemm_rows_kernel<2, WK, D, PRE, true, ROWS_OUT_PARTIAL>, 2},   \
+  {3, 1, PRE, 1, WK, D, 0, gemm_rows_kernel<1, WK, D, PRE, false, ROWS_OUT_PARTIAL>, 2},  \
+  {3, 2, PRE, 1, WK, D, 0, gemm_rows_kernel<2, WK, D, PRE, false, ROWS_OUT_PARTIAL>, 2},
 
 #define FP8BS_STREAM_SWIGLU_ENTRY(WK, D)                                          \
   {4, 1, 1, 1, WK, D, 1, gemm_stream_kernel<1, WK, D, true, true>, 1},           \

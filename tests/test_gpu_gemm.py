@@ -334,3 +334,22 @@ def test_errors_raise(fp8bs):
     with pytest.raises(fp8bs.Fp8bsError):
         bad = torch.zeros((40, 256), dtype=torch.bfloat16, device="cuda")
         fp8bs.gemm_ex(fp8bs.GemmConfig(1, 1, 1, 4, 5), pr.wq, pr.ws, x=bad)  # decode kernel, m > 32
+
+
+@pytest.mark.parametrize("rows_cfg", [(4, 8, 4), (1, 8, 3), (2, 8, 6), (2, 8, 4)])
+@pytest.mark.parametrize("m,n,k,split", [(32, 2048, 2560, 2), (20, 1536, 1664, 3), (9, 1024, 1280, 4)])
+def test_rows_split_parity(fp8bs, rows_cfg, m, n, k, split):
+    """Row-range kernels with K split over workgroups (fp32 partials summed in
+    split order by the reduce kernel): full output within tolerance, fused
+    cast equal to quantize-then-multiply, ragged K ranges."""
+    from fp8_block_scaled_fp8bs_amd import GemmConfig
+    pre, wk, d = rows_cfg
+    cfg = GemmConfig(fp8bs.PATH_MFMA_ROWS, pre, 1, wk, d, split)
+    announce("rows split", cfg, m, n, k)
+    pr = _random_problem(fp8bs, m, n, k, 9000 + m + n + k + split)
+    y = fp8bs.gemm_ex(cfg, pr.wq, pr.ws, x=pr.x)
+    xq, xs = fp8bs.quantize_act(pr.x)
+    yq = fp8bs.gemm_ex(cfg, pr.wq, pr.ws, x_q=xq, x_s=xs)
+    torch.cuda.synchronize()
+    _assert_close(host_bits(y), pr.ref, f"rows split {cfg}")
+    assert np.array_equal(host_bits(y), host_bits(yq))
