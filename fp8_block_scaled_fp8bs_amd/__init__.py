@@ -31,6 +31,7 @@ _LIB_PATH = os.path.join(_PKG, "libfp8bs.so")
 _LIB = None
 
 PATH_AUTO, PATH_MFMA, PATH_DOT, PATH_MFMA_ROWS, PATH_MFMA_STREAM, PATH_PREFILL = 0, 1, 2, 3, 4, 5
+PATH_MFMA_ROWS_REG = 6
 REDUCE_KERNEL, REDUCE_LAST_ARRIVER = 0, 1
 EPILOGUE_SEPARATE, EPILOGUE_IN_GEMM = 0, 1
 COUNTER = {"quant_weight": 0, "quant_act": 1, "gemm_mfma": 2, "gemm_dot": 3,

@@ -89,12 +89,13 @@ std::vector<KernelEntry>& kernel_registry() {
 
 namespace {
 
-constexpr int64_t kMaxDecodeM = 32;       // activation rows of the decode kernels (paths 1-4)
+constexpr int64_t kMaxDecodeM = 32;       // activation rows of the decode kernels (paths 1-4, 6)
 constexpr int64_t kMaxM = (int64_t)1 << 20;  // activation rows of the prefill path
 
 // Row-range paths: one workgroup per compute unit, n split over them.
 inline bool is_row_range(int path) {
-  return path == FP8BS_PATH_MFMA_ROWS || path == FP8BS_PATH_MFMA_STREAM;
+  return path == FP8BS_PATH_MFMA_ROWS || path == FP8BS_PATH_MFMA_STREAM ||
+         path == FP8BS_PATH_MFMA_ROWS_REG;
 }
 
 // The streaming kernel addresses activations with 32-bit buffer offsets
@@ -102,11 +103,18 @@ inline bool is_row_range(int path) {
 // activations must stay below that.
 inline bool stream_offsets_fit(int64_t m, int64_t k) { return m * k * 2 < ((int64_t)1 << 31); }
 
+// The register-activation row-range kernel holds depth K blocks per wave:
+// the K range must fit in waves_k * depth blocks, without a split.
+inline bool rows_reg_fits(const fp8bs_gemm_config& c, int kbn) {
+  return c.split_k == 1 && kbn <= c.waves_k * c.depth;
+}
+
 // swiglu: the row-range kernels instantiated with the SwiGLU epilogue.
 const KernelEntry* find_kernel(const fp8bs_gemm_config& c, int m, bool fused,
                                bool swiglu = false) {
   int mt;
-  if (c.path == FP8BS_PATH_MFMA || c.path == FP8BS_PATH_MFMA_ROWS) {
+  if (c.path == FP8BS_PATH_MFMA || c.path == FP8BS_PATH_MFMA_ROWS ||
+      c.path == FP8BS_PATH_MFMA_ROWS_REG) {
     mt = m <= 16 ? 1 : 2;
   } else if (c.path == FP8BS_PATH_MFMA_STREAM) {
     if (c.tiles_n != 1) return nullptr;
@@ -161,6 +169,9 @@ size_t config_lds_bytes(const fp8bs_gemm_config& c, int m, int64_t n, int kbn, i
     const size_t ys = swiglu ? (size_t)lds_ystage_bytes(m, rows) : 0;
     if (c.path == FP8BS_PATH_MFMA_STREAM)
       return ws + (size_t)lds_stream_bytes(kbn, m, c.waves_k, mt) + ys;
+    if (c.path == FP8BS_PATH_MFMA_ROWS_REG)  // m > 16: 16 rows at a time cast through LDS
+      return ws + (size_t)2 * (c.waves_k - 1) * mt * 64 * 16 +
+             (mt == 2 ? (size_t)lds_act_bytes(kbn, 16) : 0) + ys;
     return ws + (size_t)lds_act_bytes(nblk, m) + (size_t)2 * (c.waves_k - 1) * mt * 64 * 16 + ys;
   }
   const int nblk = (kbn + c.split_k - 1) / c.split_k;
@@ -201,6 +212,7 @@ constexpr int MF = FP8BS_PATH_MFMA;
 constexpr int DT = FP8BS_PATH_DOT;
 constexpr int RW = FP8BS_PATH_MFMA_ROWS;
 constexpr int ST = FP8BS_PATH_MFMA_STREAM;
+constexpr int RR = FP8BS_PATH_MFMA_ROWS_REG;
 constexpr int kTableCUs = 256;  // the configuration table assumes a full MI355X
 
 // Configurations the SwiGLU call accepts. With the separate epilogue:
@@ -222,6 +234,7 @@ bool candidate_fits(const Candidate& cd, int64_t m, int64_t n, int kbn, fp8bs_ge
   if (cd.path == DT && m > 4) return false;
   if (c.split_k > kbn) return false;
   if (cd.path == ST && !stream_offsets_fit(m, (int64_t)kbn * BLK)) return false;
+  if (cd.path == RR && !rows_reg_fits(c, kbn)) return false;
   if (kbn > 0 && config_lds_bytes(c, (int)m, n, kbn, kTableCUs) > kLdsLimit) return false;
   *out = c;
   return true;
@@ -234,7 +247,10 @@ bool candidate_fits(const Candidate& cd, int64_t m, int64_t n, int kbn, fp8bs_ge
 // candidates in order of preference, measured on MI355X with graph-replayed
 // launches over a rotating 1 GiB weight pool. The first candidate that fits
 // the shape (rows dividing n, split not above the number of K blocks,
-// staged activations within the LDS budget) is used; a fallback list with
+// staged activations within the LDS budget, the K range within the
+// registers of the register-activation kernel) is used; on wide shapes with
+// 17-32 rows the LDS row-range kernel fits up to about 22 rows at k = 5120
+// and the register-activation kernel takes the rest; a fallback list with
 // growing split catches everything else. The SwiGLU call (swiglu set) uses
 // the same choice with the separate epilogue, so its y equals fp8bs_gemm's.
 bool select_config(int64_t m, int64_t n, int64_t k, fp8bs_gemm_config* out, bool swiglu = false) {
@@ -291,14 +307,14 @@ bool select_config(int64_t m, int64_t n, int64_t k, fp8bs_gemm_config* out, bool
        {{{RW, 1, 1, 8, 3, 1, RK}, {RW, 2, 1, 8, 6, 1, RK}}, 2},
        {{{RW, 2, 1, 8, 6, 1, RK}, {RW, 1, 1, 8, 3, 1, RK}}, 2},
        {{{RW, 4, 1, 8, 4, 1, RK}, {RW, 2, 1, 8, 6, 1, RK}}, 2},
-       {{{MF, 1, 8, 1, 5, 4, RK}, {MF, 1, 4, 1, 5, 4, RK}}, 2}},
+       {{{RW, 2, 1, 8, 6, 1, RK}, {RR, 1, 1, 8, 5, 1, RK}, {MF, 1, 8, 1, 5, 4, RK}}, 3}},
       // vocabulary-wide N: n >= 65536
       {{{{MF, 1, 2, 4, 2, 1, RK}, {MF, 1, 2, 4, 5, 1, RK}}, 2},
        {{{MF, 1, 2, 4, 5, 1, RK}, {MF, 1, 1, 8, 5, 1, RK}}, 2},
        {{{MF, 4, 1, 4, 2, 1, RK}, {MF, 1, 8, 1, 5, 1, RK}}, 2},
        {{{ST, 1, 1, 8, 6, 1, RK}, {RW, 2, 1, 8, 6, 1, RK}}, 2},
        {{{RW, 1, 1, 8, 3, 1, RK}, {RW, 2, 1, 8, 6, 1, RK}}, 2},
-       {{{MF, 1, 8, 1, 5, 2, RK}, {MF, 1, 8, 2, 2, 2, RK}}, 2}}};
+       {{{RW, 2, 1, 8, 6, 1, RK}, {RR, 1, 1, 8, 5, 1, RK}, {MF, 1, 8, 1, 5, 2, RK}}, 3}}};
   static const Candidate fallback[] = {{MF, 1, 1, 4, 5, 1, RK}, {MF, 1, 1, 4, 5, 2, RK},
                                        {MF, 1, 1, 4, 5, 4, RK}, {MF, 1, 1, 4, 5, 8, RK},
                                        {MF, 1, 1, 4, 5, 16, RK}, {MF, 1, 1, 4, 5, 32, RK},
@@ -420,6 +436,7 @@ fp8bs_status gemm_impl(const void* x_bf16, const uint8_t* x_fp8, const float* x_
        (c.split_k != 1 && (c.path != FP8BS_PATH_MFMA_ROWS || c.reduce != FP8BS_REDUCE_KERNEL))))
     return FP8BS_ERR_CONFIG;
   if (c.path == FP8BS_PATH_MFMA_STREAM && !stream_offsets_fit(m, k)) return FP8BS_ERR_CONFIG;
+  if (c.path == FP8BS_PATH_MFMA_ROWS_REG && !rows_reg_fits(c, kbn)) return FP8BS_ERR_CONFIG;
   if (c.reduce != FP8BS_REDUCE_KERNEL && c.reduce != FP8BS_REDUCE_LAST_ARRIVER)
     return FP8BS_ERR_CONFIG;
   if (swiglu && !swiglu_supported(c, (int)m)) return FP8BS_ERR_CONFIG;

@@ -186,13 +186,9 @@ __device__ __forceinline__ float wave_max(float v) {
 
 // -------------------------------------------------- activation block cast ---
 
-// Cast one quarter (32 values) of a 1x128 activation block. The four
-// quarters of a block must sit in the four lanes of one DPP quad, quarter q
-// in lane q of the quad; the block amax is reduced across the quad.
-// xw: 16 dwords = 32 bf16 in K order. codes: 8 dwords = 32 codes in K order.
-// Returns the block scale fl32(amax / 448) (identical in the four lanes).
-__device__ __forceinline__ float cast_quarter(const uint4 (&xw)[4], uint32_t (&codes)[8]) {
-  float x[32];
+// One quarter (32 values) of a 1x128 activation block: xw holds 16 dwords =
+// 32 bf16 in K order. Unpacks them to x and returns their largest magnitude.
+__device__ __forceinline__ float quarter_unpack(const uint4 (&xw)[4], float (&x)[32]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint32_t w[4] = {xw[i].x, xw[i].y, xw[i].z, xw[i].w};
@@ -205,11 +201,63 @@ __device__ __forceinline__ float cast_quarter(const uint4 (&xw)[4], uint32_t (&c
   float am = 0.0f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) am = __builtin_fmaxf(am, __builtin_fabsf(x[i]));
-  am = quad_max(am);
+  return am;
+}
+
+// Codes (8 dwords = 32 codes in K order) of a quarter whose block has
+// largest magnitude am; returns the block scale fl32(am / 448).
+__device__ __forceinline__ float quarter_codes(float (&x)[32], float am, uint32_t (&codes)[8]) {
   const float s = am / 448.0f;
   block_quotients(x, am, s);
 #pragma unroll
   for (int i = 0; i < 8; ++i) codes[i] = e4m3x4(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
+  return s;
+}
+
+// Cast one quarter of a 1x128 activation block. The four quarters of a
+// block must sit in the four lanes of one DPP quad, quarter q in lane q of
+// the quad; the block amax is reduced across the quad.
+// Returns the block scale (identical in the four lanes).
+__device__ __forceinline__ float cast_quarter(const uint4 (&xw)[4], uint32_t (&codes)[8]) {
+  float x[32];
+  float am = quarter_unpack(xw, x);
+  am = quad_max(am);
+  return quarter_codes(x, am, codes);
+}
+
+// The same cast with the four quarters of a block in lanes l, l^16, l^32,
+// l^48 (quarter l/16: the K layout of an MFMA operand). The block amax is the
+// same maximum and each code the same per-element arithmetic, so scale and
+// codes equal cast_quarter's bit for bit. The quotients and codes are formed
+// 8 values at a time, which keeps few registers live in kernels that hold
+// many operands.
+__device__ __forceinline__ float cast_quarter_cols(const uint4 (&xw)[4], uint32_t (&codes)[8]) {
+  float am = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w[4] = {xw[i].x, xw[i].y, xw[i].z, xw[i].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      am = __builtin_fmaxf(am, __builtin_fmaxf(__builtin_fabsf(bf16_lo(w[j])),
+                                               __builtin_fabsf(bf16_hi(w[j]))));
+  }
+  am = __builtin_fmaxf(am, __shfl_xor(am, 16));
+  am = __builtin_fmaxf(am, __shfl_xor(am, 32));
+  const float s = am / 448.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w[4] = {xw[i].x, xw[i].y, xw[i].z, xw[i].w};
+    float x[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[2 * j] = bf16_lo(w[j]);
+      x[2 * j + 1] = bf16_hi(w[j]);
+    }
+    block_quotients(x, am, s);
+    codes[2 * i] = e4m3x4(x[0], x[1], x[2], x[3]);
+    codes[2 * i + 1] = e4m3x4(x[4], x[5], x[6], x[7]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   return s;
 }
 

@@ -22,6 +22,8 @@
 //   the same launch, by the workgroup of the row group that finishes last.
 #pragma once
 
+#include <type_traits>
+
 #include "fp8bs_device.h"
 
 namespace fp8bs {
@@ -830,6 +832,268 @@ __global__ __launch_bounds__(64 * WK) void gemm_rows_kernel(GemmParams p) {
     const int i = (ngrp - 1) * D + d;
     if (i < nitem) compute(d, i);
   }
+  if constexpr (SW) {
+    flush_ystage<NT>(p, ystage, r0, nrows, tid);
+    swiglu_arrive<NT>(p, r0, r1, p.rows_per_wg, gridDim.x, tid);
+  }
+}
+
+// ====================================================================
+// Row-range kernel with register-resident activations: the work split of
+// gemm_rows_kernel (one workgroup per compute unit, a contiguous range of
+// output columns over the whole K range, WK waves taking K blocks
+// wk, wk + WK, ...), but each wave keeps the activation operands of its own
+// NJ K blocks in VGPRs for the whole launch instead of reading them from
+// LDS: NJ * MT * 8 dwords per lane (80 at NJ = 5, m <= 32). The multiply
+// loop reads only weight scales and the cross-wave exchange area from LDS,
+// and the activations of a long K range never limit m. With m <= 16 (or
+// codes given) each wave loads and casts its own blocks straight into the
+// operand layout (quarter l/16 of row l%16 in lane l; the block amax is
+// taken across those four lanes); with 16 < m <= 32 and the cast fused, the
+// workgroup casts 16 rows at a time into LDS and each wave copies its
+// operands out. Either way the rule and arithmetic are those of every other
+// cast, so codes and scales equal fp8bs_quantize_act's. Requires
+// kbn <= NJ * WK; waves whose block index passes kbn skip it. Products are accumulated in the same
+// order as gemm_rows_kernel with the same WK, and summed across waves in
+// wave order.
+//
+// Weights: wave slot j holds block wk + j WK of the current 16-row tile; it
+// is refilled with the next tile's block as soon as it has been multiplied,
+// so NJ blocks per wave stay in flight. PRE of them are requested before
+// the activation cast.
+// ====================================================================
+
+template <int MT, int NJ>
+struct RegAct {
+  i32x8 op[NJ][MT];  // B operands (zero for rows past m)
+  float s[NJ][MT];   // activation scale of row l%16 + 16 mt (0 past m)
+};
+
+template <int MT, int WK, int NJ, int PRE, bool FUSED, bool SW = false>
+__global__ __launch_bounds__(64 * WK) void gemm_rows_reg_kernel(GemmParams p) {
+  constexpr int NT = 64 * WK;
+  extern __shared__ __align__(16) uint8_t lds_all[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wk = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int M = p.m;
+  const int nblk = p.kbn;
+  const int r0 = blockIdx.x * p.rows_per_wg;
+  const int r1 = r0 + p.rows_per_wg < p.n ? r0 + p.rows_per_wg : p.n;
+  const int nrows = r1 - r0;
+  const int ntile = (nrows + 15) >> 4;
+  const int nbf = r0 / BLK, nbr = (r1 - 1) / BLK - nbf + 1;
+  float* wsl = reinterpret_cast<float*>(lds_all);
+  f32x4* red = reinterpret_cast<f32x4*>(lds_all + lds_wscale_bytes(p.rows_per_wg, nblk));
+  // m > 16 with the cast fused: the 16-row cast area (lds_act_bytes(nblk, 16))
+  uint8_t* act = reinterpret_cast<uint8_t*>(red) + 2 * (WK - 1) * MT * 64 * 16;
+  // SwiGLU epilogue: bf16 outputs staged after the other areas
+  uint16_t* ystage =
+      reinterpret_cast<uint16_t*>(act + (FUSED && MT == 2 ? lds_act_bytes(nblk, 16) : 0));
+
+  const int l16 = lane & 15, g16 = lane >> 4;
+  const int l7 = lane & 7, hb = (lane >> 3) & 1;
+  const bool lo8 = hb == 0;
+
+  // block of slot j (clamped for the address; the multiply is skipped)
+  auto slot_block = [&](int j) {
+    const int kb = wk + j * WK;
+    return kb < nblk ? kb : nblk - 1;
+  };
+  auto act_row = [&](int mt) {
+    const int m = l16 + 16 * mt;
+    return m < M ? m : M - 1;
+  };
+
+  TileLoad wb[NJ];
+  auto load_slot = [&](int j, int t) {
+    t = t < ntile ? t : ntile - 1;
+    int ra = 16 * t + l7, rb = 16 * t + 8 + l7;
+    ra = ra < nrows ? ra : nrows - 1;
+    rb = rb < nrows ? rb : nrows - 1;
+    const uint8_t* base = p.wq + (size_t)slot_block(j) * BLK;
+    wb[j].p = load_stream16(base + (size_t)(r0 + ra) * (size_t)p.k + 16 * (2 * g16 + hb));
+    wb[j].q = load_stream16(base + (size_t)(r0 + rb) * (size_t)p.k + 16 * (2 * g16 + 1 - hb));
+  };
+  RegAct<MT, NJ> xa;
+  ScaleFetch sf;
+
+  if constexpr (FUSED && MT == 2) {
+    // Activations cast cooperatively through LDS, 16 rows at a time (the
+    // bf16 values of a wave's own blocks would not fit in registers next to
+    // the operands): quarter g of a half is (block g / 64, row (g / 4) % 16,
+    // quarter g % 4), in the quad layout cast_quarter takes. A thread holds
+    // at most NJ quarters per half (kbn <= NJ WK). Both halves are loaded
+    // before the first weight slot is requested.
+    float* act_s = reinterpret_cast<float*>(act + nblk * 16 * ACT_STRIDE);
+    const int G = nblk * 64;
+    uint4 xh[2][NJ][4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < NJ; ++i) {
+        int g = tid + i * NT;
+        g = g < G ? g : G - 1;
+        const int bm = g >> 2;
+        int m = 16 * h + (bm & 15);
+        m = m < M ? m : M - 1;
+        const uint4* src = reinterpret_cast<const uint4*>(
+            p.x + (size_t)m * (size_t)p.k + (size_t)(bm >> 4) * BLK + 32 * (g & 3));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) xh[h][i][q] = src[q];
+      }
+    load_wscales<NT>(p, nbf, nbr, 0, nblk, tid, sf);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < PRE && j < NJ; ++j) load_slot(j, 0);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (h == 1) lds_barrier();  // every wave has read the first half
+#pragma unroll
+      for (int i = 0; i < NJ; ++i) {
+        const int g = tid + i * NT;
+        uint32_t c[8];
+        const float sc = cast_quarter(xh[h][i], c);  // the whole quad takes part
+        if (g < G) {  // G is a multiple of 4: the four lanes of a quad agree
+          const int bm = g >> 2;
+          uint4* d = reinterpret_cast<uint4*>(act + bm * ACT_STRIDE + (g & 3) * 32);
+          d[0] = make_uint4(c[0], c[1], c[2], c[3]);
+          d[1] = make_uint4(c[4], c[5], c[6], c[7]);
+          if ((g & 3) == 0) act_s[bm] = sc;
+        }
+        if (h == 0 && PRE + i < NJ) load_slot(PRE + i, 0);
+      }
+      lds_barrier();
+      const bool live = 16 * h + l16 < M;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int bm = slot_block(j) * 16 + l16;
+        const uint4* a = reinterpret_cast<const uint4*>(act + bm * ACT_STRIDE + 32 * g16);
+        const uint4 lo = a[0], hi = a[1];
+        xa.op[j][h] = live ? i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                                   (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w}
+                           : i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+        xa.s[j][h] = live ? act_s[bm] : 0.0f;
+      }
+    }
+  } else {
+    // Each wave loads (and casts) the operands of its own blocks straight
+    // into registers: quarter l/16 of row l%16 of each block; the activation
+    // loads come before any weight load, so each cast waits for activation
+    // loads only.
+    uint4 xr[NJ][MT][4];
+    float xsr[NJ][MT];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int kb = slot_block(j);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int m = act_row(mt);
+        if constexpr (FUSED) {
+          const uint4* src = reinterpret_cast<const uint4*>(p.x + (size_t)m * (size_t)p.k +
+                                                            (size_t)kb * BLK + 32 * g16);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) xr[j][mt][i] = src[i];
+        } else {
+          const uint4* src = reinterpret_cast<const uint4*>(p.xq + (size_t)m * (size_t)p.k +
+                                                            (size_t)kb * BLK + 32 * g16);
+          xr[j][mt][0] = src[0];
+          xr[j][mt][1] = src[1];
+          xsr[j][mt] = p.xs[(size_t)m * (size_t)p.kbn + kb];
+        }
+      }
+    }
+    load_wscales<NT>(p, nbf, nbr, 0, nblk, tid, sf);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < PRE && j < NJ; ++j) load_slot(j, 0);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const bool live = l16 + 16 * mt < M;
+        uint32_t c[8];
+        float sc;
+        if constexpr (FUSED) {
+          sc = cast_quarter_cols(xr[j][mt], c);  // every lane takes part in the shuffles
+        } else {
+          const uint4 lo = xr[j][mt][0], hi = xr[j][mt][1];
+          c[0] = lo.x; c[1] = lo.y; c[2] = lo.z; c[3] = lo.w;
+          c[4] = hi.x; c[5] = hi.y; c[6] = hi.z; c[7] = hi.w;
+          sc = xsr[j][mt];
+        }
+        xa.op[j][mt] = live ? i32x8{(int)c[0], (int)c[1], (int)c[2], (int)c[3], (int)c[4],
+                                    (int)c[5], (int)c[6], (int)c[7]}
+                            : i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+        xa.s[j][mt] = live ? sc : 0.0f;
+      }
+      if (PRE + j < NJ) load_slot(PRE + j, 0);
+    }
+  }
+  store_wscales<NT>(p, nbf, nbr, 0, nblk, tid, sf, wsl);
+  lds_barrier();
+
+  // 4. tiles: multiply slot j, refill it with the next tile's block
+  f32x4 acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto multiply_tile = [&](int t, auto refill) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int kb = wk + j * WK;
+      if (kb < nblk) {
+        // this lane's four output rows lie in one 128-row scale block
+        int nbl = (r0 + 16 * t + 4 * g16) / BLK - nbf;
+        nbl = nbl < nbr ? nbl : nbr - 1;
+        const float sw = wsl[nbl * nblk + kb];
+        const i32x8 aop = tile_operand(wb[j], lo8);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+          const f32x4 pb = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              aop, xa.op[j][mt], z, 0, 0, 0, 0, 0, 0);
+          const float sc = xa.s[j][mt] * sw;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[mt][q] = __builtin_fmaf(pb[q], sc, acc[mt][q]);
+        }
+      }
+      if constexpr (decltype(refill)::value) load_slot(j, t + 1);
+    }
+    // partial sums of waves 1..WK-1 through LDS, summed in wave order
+    f32x4* rt = red + (t & 1) * (WK - 1) * MT * 64;
+    if (wk > 0) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) rt[((wk - 1) * MT + mt) * 64 + lane] = acc[mt];
+    }
+    lds_barrier();
+    if (wk == 0) {
+      for (int w = 1; w < WK; ++w)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[mt] += rt[((w - 1) * MT + mt) * 64 + lane];
+      const int rl = 16 * t + 4 * g16;  // first of this lane's four rows
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int m = l16 + 16 * mt;
+        if (m < M && rl < nrows) {
+          if constexpr (SW) {
+            stage_y4(ystage, p.rows_per_wg, m, rl, acc[mt][0], acc[mt][1], acc[mt][2],
+                     acc[mt][3]);
+          } else {
+            uint2* dst = reinterpret_cast<uint2*>(p.y + (size_t)m * (size_t)p.n + r0 + rl);
+            *dst = make_uint2(pack_bf16x2(acc[mt][0], acc[mt][1]),
+                              pack_bf16x2(acc[mt][2], acc[mt][3]));
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+
+  for (int t = 0; t + 1 < ntile; ++t) multiply_tile(t, std::true_type{});
+  multiply_tile(ntile - 1, std::false_type{});
   if constexpr (SW) {
     flush_ystage<NT>(p, ystage, r0, nrows, tid);
     swiglu_arrive<NT>(p, r0, r1, p.rows_per_wg, gridDim.x, tid);

@@ -10,7 +10,8 @@ namespace fp8bs {
 
 struct KernelEntry {
   int path;    // 1 = MFMA grid, 2 = DOT grid, 3 = MFMA row range (one workgroup per CU),
-               // 4 = MFMA streaming row range, 5 = prefill-size tiled MFMA GEMM
+               // 4 = MFMA streaming row range, 5 = prefill-size tiled MFMA GEMM,
+               // 6 = MFMA row range with register-resident activations
   int mt;      // MFMA: 16-row activation tiles (1: m <= 16, 2: m <= 32); DOT: max m
   int tn;      // MFMA: 16-row weight tiles per wave; DOT: 8-row groups per wave
   int wn, wk, d;
@@ -66,6 +67,21 @@ struct KernelRegistrar {
   {3, 2, PRE, 1, WK, D, 1, gemm_rows_kernel<2, WK, D, PRE, true, ROWS_OUT_PARTIAL>, 2},   \
   {3, 1, PRE, 1, WK, D, 0, gemm_rows_kernel<1, WK, D, PRE, false, ROWS_OUT_PARTIAL>, 2},  \
   {3, 2, PRE, 1, WK, D, 0, gemm_rows_kernel<2, WK, D, PRE, false, ROWS_OUT_PARTIAL>, 2},
+
+// Row-range kernel with register-resident activations: (waves along K,
+// K blocks per wave, weight slots requested before the cast). The config's
+// depth field holds the blocks per wave, tiles_n the pre-cast count.
+#define FP8BS_ROWS_REG_ENTRY(WK, NJ, PRE)                                    \
+  {6, 1, PRE, 1, WK, NJ, 1, gemm_rows_reg_kernel<1, WK, NJ, PRE, true>},     \
+  {6, 2, PRE, 1, WK, NJ, 1, gemm_rows_reg_kernel<2, WK, NJ, PRE, true>},     \
+  {6, 1, PRE, 1, WK, NJ, 0, gemm_rows_reg_kernel<1, WK, NJ, PRE, false>},    \
+  {6, 2, PRE, 1, WK, NJ, 0, gemm_rows_reg_kernel<2, WK, NJ, PRE, false>},
+
+#define FP8BS_ROWS_REG_SWIGLU_ENTRY(WK, NJ, PRE)                                        \
+  {6, 1, PRE, 1, WK, NJ, 1, gemm_rows_reg_kernel<1, WK, NJ, PRE, true, true>, 1},        \
+  {6, 2, PRE, 1, WK, NJ, 1, gemm_rows_reg_kernel<2, WK, NJ, PRE, true, true>, 1},        \
+  {6, 1, PRE, 1, WK, NJ, 0, gemm_rows_reg_kernel<1, WK, NJ, PRE, false, true>, 1},       \
+  {6, 2, PRE, 1, WK, NJ, 0, gemm_rows_reg_kernel<2, WK, NJ, PRE, false, true>, 1},
 
 #define FP8BS_STREAM_SWIGLU_ENTRY(WK, D)                                          \
   {4, 1, 1, 1, WK, D, 1, gemm_stream_kernel<1, WK, D, true, true>, 1},           \

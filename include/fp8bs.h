@@ -134,7 +134,8 @@ enum {
   FP8BS_PATH_DOT = 2,
   FP8BS_PATH_MFMA_ROWS = 3,
   FP8BS_PATH_MFMA_STREAM = 4,
-  FP8BS_PATH_PREFILL = 5
+  FP8BS_PATH_PREFILL = 5,
+  FP8BS_PATH_MFMA_ROWS_REG = 6
 };
 enum { FP8BS_REDUCE_KERNEL = 0, FP8BS_REDUCE_LAST_ARRIVER = 1 };
 enum { FP8BS_EPILOGUE_SEPARATE = 0, FP8BS_EPILOGUE_IN_GEMM = 1 };
@@ -152,8 +153,14 @@ enum { FP8BS_EPILOGUE_SEPARATE = 0, FP8BS_EPILOGUE_IN_GEMM = 1 };
  *             tiles_n, waves_n and split_k must be 1; needs m*k*2 < 2^31), or
  *             PREFILL (any m: workgroups of 4 waves own 128 x 128 output
  *             tiles and step through K in 128-deep blocks staged in LDS;
- *             split_k must be 1, the other fields are not used). Paths 1-4
- *             take m <= 32.
+ *             split_k must be 1, the other fields are not used), or
+ *             MFMA_ROWS_REG (the work split of MFMA_ROWS with each wave's
+ *             activation operands held in registers instead of LDS, so m up
+ *             to 32 runs unsplit at any K the registers hold: depth is the
+ *             number of K blocks per wave and k / 128 must not exceed
+ *             waves_k * depth; tiles_n gives how many weight blocks are
+ *             requested before the cast; waves_n and split_k must be 1).
+ *             Paths 1-4 and 6 take m <= 32.
  *   tiles_n   MFMA: 16-row tiles per wave (1, 2, 4); DOT: 8-row groups per wave (1, 2, 4)
  *   waves_n   waves side by side along N in one workgroup (1, 2, 4)
  *   waves_k   waves splitting a workgroup's K range (1, 2, 4, 8); their
@@ -251,8 +258,9 @@ fp8bs_status fp8bs_gemm_swiglu(const void* x_bf16, int64_t m, const uint8_t* w_f
  * the fused cast, otherwise x_fp8 / x_scale). Accepted with
  * FP8BS_EPILOGUE_SEPARATE: every configuration fp8bs_gemm_ex accepts except
  * the last-arriver reduce. With FP8BS_EPILOGUE_IN_GEMM: split_k == 1 on the
- * MFMA path, or on the MFMA_ROWS / MFMA_STREAM paths for the compiled
- * shapes (waves_k 8 with depth 3, 4 or 6 and, MFMA_STREAM, depth 4 or 6).
+ * MFMA path, or on the MFMA_ROWS / MFMA_STREAM / MFMA_ROWS_REG paths for
+ * the compiled shapes (waves_k 8 with depth 3, 4 or 6; MFMA_STREAM, depth 4
+ * or 6; MFMA_ROWS_REG, depth 5 with tiles_n 1).
  * Anything else is FP8BS_ERR_CONFIG.                                        */
 fp8bs_status fp8bs_gemm_swiglu_ex(const void* x_bf16, const uint8_t* x_fp8, const float* x_scale,
                                   int64_t m, const uint8_t* w_fp8, const float* w_scale,

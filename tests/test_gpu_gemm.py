@@ -230,6 +230,38 @@ def test_row_range_kernel_uneven_ranges(fp8bs, m, n, k, wk, d, pre):
     assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
 
 
+ROWS_REG_SHAPES = [(8, 5, 1), (8, 5, 2), (8, 4, 2)]  # (waves_k, K blocks per wave, pre-cast slots)
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 384, 640), (8, 4224, 5120), (16, 2048, 4096), (17, 640, 5120),
+                                   (20, 1152, 1280), (23, 1536, 3968), (32, 4224, 5120),
+                                   (32, 256, 128)])
+@pytest.mark.parametrize("wk,nj,pre", ROWS_REG_SHAPES)
+def test_rows_reg_kernel(fp8bs, m, n, k, wk, nj, pre):
+    """Row-range kernel with register-resident activations: short last
+    ranges, partial 16-row tiles, K blocks not a multiple of the waves (waves
+    with fewer blocks, one block in all), m on both sides of 16 (per-wave
+    cast and, fused above 16 rows, the cast through LDS); the pre-quantized
+    route gives the same bits. A K range beyond waves_k * depth blocks is a
+    configuration error."""
+    from fp8_block_scaled_fp8bs_amd import Fp8bsError, GemmConfig
+    c = GemmConfig(fp8bs.PATH_MFMA_ROWS_REG, pre, 1, wk, nj)
+    announce("rows reg", c, "m", m, "n", n, "k", k)
+    pr = _random_problem(fp8bs, m, n, k, 13 * m + n + k + wk + nj + pre)
+    if k // 128 > wk * nj:
+        with pytest.raises(Fp8bsError):
+            fp8bs.gemm_ex(c, pr.wq, pr.ws, x=pr.x)
+        return
+    y = fp8bs.gemm_ex(c, pr.wq, pr.ws, x=pr.x)
+    torch.cuda.synchronize()
+    _assert_close(host_bits(y), pr.ref, f"rows reg {wk},{nj},{pre} m={m} n={n} k={k}")
+    xq, xs = fp8bs.quantize_act(pr.x)
+    y2 = fp8bs.gemm_ex(c, pr.wq, pr.ws, x_q=xq, x_s=xs)
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16))
+    with pytest.raises(Fp8bsError):  # no K split on this path
+        fp8bs.gemm_ex(GemmConfig(fp8bs.PATH_MFMA_ROWS_REG, pre, 1, wk, nj, 2), pr.wq, pr.ws, x=pr.x)
+
+
 @pytest.mark.parametrize("m,n,k", [(8, 384, 640), (3, 1152, 1920), (12, 2048, 5120),
                                    (32, 640, 1024), (16, 5120, 2048)])
 @pytest.mark.parametrize("wk,d", STREAM_SHAPES)

@@ -216,6 +216,9 @@ FUSED_CASES = [
     (32, 384, 640, (3, 1, 1, 8, 3, 1, 0, 1)),
     (8, 640, 1024, (4, 1, 1, 8, 6, 1, 0, 1)),    # streaming row-range kernel
     (1, 1280, 512, (4, 1, 1, 8, 4, 1, 0, 1)),
+    (8, 640, 1024, (6, 1, 1, 8, 5, 1, 0, 1)),    # register-activation row-range kernel
+    (24, 1280, 5120, (6, 1, 1, 8, 5, 1, 0, 1)),
+    (32, 384, 640, (6, 1, 1, 8, 5, 1, 0, 0)),
     (8, 640, 1024, (1, 1, 5, 1, 5, 4, 0, 0)),    # split sum carrying the epilogue
     (32, 1280, 2048, (1, 1, 8, 1, 5, 4, 0, 0)),
     (4, 640, 1024, (2, 2, 1, 8, 5, 3, 0, 0)),    # DOT with split
