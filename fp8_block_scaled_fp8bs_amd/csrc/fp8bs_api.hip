@@ -157,7 +157,8 @@ int rows_per_workgroup(int64_t n, int num_cu) {
 
 size_t config_lds_bytes(const fp8bs_gemm_config& c, int m, int64_t n, int kbn, int num_cu,
                         bool swiglu = false) {
-  if (c.path == FP8BS_PATH_PREFILL) return (size_t)pf_lds_bytes(c.waves_n);
+  if (c.path == FP8BS_PATH_PREFILL)
+    return (size_t)(c.depth > 1 ? pf_dma_lds_bytes(c.waves_n, c.depth) : pf_lds_bytes(c.waves_n));
   const int mt = m <= 16 ? 1 : 2;
   if (is_row_range(c.path)) {
     // weight scales of the row range first, then the kernel's own layout,
@@ -257,21 +258,21 @@ bool select_config(int64_t m, int64_t n, int64_t k, fp8bs_gemm_config* out, bool
   if (m < 0 || m > kMaxM || n < 0 || k < 0 || n % BLK || k % BLK) return false;
   if (swiglu && n % (2 * BLK)) return false;
   if (m > kMaxDecodeM && n > 0 && k > 0) {
-    // prefill sizes: the tiled kernel. 8 waves on 256 x 128 output tiles
-    // where n allows and those tiles fill the compute units at least once;
-    // otherwise 4 waves on 128 x 128 tiles (two workgroups per unit), with K
-    // split when the tiles alone cannot fill the units (each split keeps at
-    // least two K blocks). Measured on MI355X at m = 128 .. 8192.
+    // prefill sizes: the tiled kernel with 4 waves on 128 x 128 output tiles
+    // and two LDS stages filled by direct loads (two workgroups per compute
+    // unit), with K split when the tiles alone cannot fill the compute units
+    // (each split keeps at least two K blocks). Measured on MI355X at
+    // m = 512 .. 8192 against the register-pipelined kernels and deeper
+    // stage rings (one workgroup per unit), which it beats at every size.
     const int64_t mtiles = (m + PF_TILE_M - 1) / PF_TILE_M;
-    const bool wide = n % pf_tile_n(4) == 0 && (n / pf_tile_n(4)) * mtiles >= kTableCUs;
-    const int wn = wide ? 4 : 2;
+    const int wn = 2;
     const int64_t tiles = (n / pf_tile_n(wn)) * mtiles;
-    int64_t split = wide ? 1 : (kTableCUs + tiles - 1) / tiles;
+    int64_t split = (kTableCUs + tiles - 1) / tiles;
     const int64_t kblocks = k / BLK;
     const int64_t max_split = kblocks / 2 < 16 ? kblocks / 2 : 16;
     split = split < max_split ? split : max_split;
     split = split < 1 ? 1 : split;
-    *out = make_cfg(FP8BS_PATH_PREFILL, 1, wn, 2, 1, (int)split);
+    *out = make_cfg(FP8BS_PATH_PREFILL, 1, wn, 2, 2, (int)split);
     return true;
   }
   const int kbn = (int)(k / BLK);

@@ -56,21 +56,32 @@ def test_prefill_parity_full_output(fp8bs, m, n, k):
     assert np.array_equal(host_bits(y), host_bits(y_q)), "fused cast differs from quantize-then-multiply"
 
 
-@pytest.mark.parametrize("variant", [(2, 1), (4, 1)])
-@pytest.mark.parametrize("m,n,k,split", [(300, 512, 1280, 1), (129, 768, 2048, 3), (64, 256, 384, 1)])
+@pytest.mark.parametrize("variant", [(2, 1), (4, 1), (2, 2), (2, 4), (4, 2), (4, 3)])
+@pytest.mark.parametrize("m,n,k,split", [(300, 512, 1280, 1), (129, 768, 2048, 3), (64, 256, 384, 1),
+                                         (33, 1024, 128, 1), (520, 256, 2560, 2)])
 def test_prefill_every_variant(fp8bs, variant, m, n, k, split):
-    """Each compiled prefill kernel (4 or 8 waves), split and unsplit, full
-    output against the oracle."""
-    from fp8_block_scaled_fp8bs_amd import GemmConfig
+    """Each compiled prefill kernel (4 or 8 waves; register pipeline, or a
+    ring of 2-4 LDS stages filled by direct loads), split and unsplit, one K
+    block (fewer blocks than stages), ragged m tails: full output against
+    the oracle."""
+    from fp8_block_scaled_fp8bs_amd import Fp8bsError, GemmConfig
     wn, depth = variant
     cfg = GemmConfig(fp8bs.PATH_PREFILL, 1, wn, 2, depth, split)
     announce("prefill variant", cfg, m, n, k)
     x_bits, wq, ws, wq_ref, ws_ref = _problem(fp8bs, m, n, k, 7400 + m + n + k)
+    if n % (64 * wn):
+        with pytest.raises(Fp8bsError):
+            fp8bs.gemm_ex(cfg, wq, ws, x=dev_bf16(x_bits))
+        return
     y = fp8bs.gemm_ex(cfg, wq, ws, x=dev_bf16(x_bits))
     torch.cuda.synchronize()
     xq_ref, xs_ref = oracle.quantize_act_ref(x_bits)
     rep = oracle.tolerance_report(host_bits(y), oracle.gemm_ref(xq_ref, xs_ref, wq_ref, ws_ref), **TOL)
     assert rep["finite"] and rep["n_bad"] == 0, rep
+    # run to run: the same bits again
+    y2 = fp8bs.gemm_ex(cfg, wq, ws, x=dev_bf16(x_bits))
+    torch.cuda.synchronize()
+    assert np.array_equal(host_bits(y), host_bits(y2))
 
 
 def test_prefill_run_to_run_identity(fp8bs):
