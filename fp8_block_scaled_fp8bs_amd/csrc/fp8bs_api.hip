@@ -125,7 +125,9 @@ const KernelEntry* find_kernel(const fp8bs_gemm_config& c, int m, bool fused,
   } else if (c.path == FP8BS_PATH_PREFILL) {
     // one kernel; it reads activation codes (the fused call casts them first)
     for (const KernelEntry& e : kernel_registry())
-      if (e.path == FP8BS_PATH_PREFILL && !swiglu && e.wn == c.waves_n && e.d == c.depth) return &e;
+      if (e.path == FP8BS_PATH_PREFILL && !swiglu && e.wn == c.waves_n && e.d == c.depth &&
+          e.tn == c.tiles_n)
+        return &e;
     return nullptr;
   } else {
     return nullptr;

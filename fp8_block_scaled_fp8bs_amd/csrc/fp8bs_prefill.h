@@ -331,9 +331,14 @@ __device__ __forceinline__ void pf_ring_tail(int kb, int last, F& f) {
 
 // grid: (n / (64 WN), ceil(m / 128), split); 128 WN threads;
 // pf_dma_lds_bytes(WN, S) of dynamic LDS. Otherwise as gemm_prefill_kernel.
-template <int WN, int S>
+//
+// EARLY: a stage is refilled as soon as every wave has copied the block's
+// operands into registers (a second barrier right after those reads),
+// with the block S later, instead of when the next block starts: S blocks
+// are then in flight while one is multiplied, from the same LDS.
+template <int WN, int S, bool EARLY = false>
 __global__ __launch_bounds__(128 * WN, WN == 2 ? 2 : 1) void gemm_prefill_dma_kernel(GemmParams p) {
-  static_assert(S >= 2 && (S - 2) * pf_dma_per_stage(WN) <= 63, "vmcnt range");
+  static_assert(S >= 2 && (S - 1) * pf_dma_per_stage(WN) <= 63, "vmcnt range");
   extern __shared__ __align__(16) uint8_t lds_all[];
   constexpr int STAGE = pf_dma_stage_bytes(WN);
   constexpr int WROWS = pf_tile_n(WN);
@@ -391,7 +396,7 @@ __global__ __launch_bounds__(128 * WN, WN == 2 ? 2 : 1) void gemm_prefill_dma_ke
     for (int j = 0; j < 4; ++j) acc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll
-  for (int s = 0; s < S - 1; ++s) issue(kb0 + s, s);
+  for (int s = 0; s < (EARLY ? S : S - 1); ++s) issue(kb0 + s, s);
 
   // One K block out of stage ST (a compile-time ring position, so every
   // LDS address is a lane base plus an immediate): all operands first, then
@@ -399,8 +404,8 @@ __global__ __launch_bounds__(128 * WN, WN == 2 ? 2 : 1) void gemm_prefill_dma_ke
   // products later, so no product waits on the one before it.
   auto block = [&](int kb, auto stc) {
     constexpr int ST = decltype(stc)::value;
-    wait_loads_then_barrier<(S - 2) * pf_dma_per_stage(WN)>();
-    issue(kb + S - 1, (ST + S - 1) % S);
+    wait_loads_then_barrier<(EARLY ? S - 1 : S - 2) * pf_dma_per_stage(WN)>();
+    if constexpr (!EARLY) issue(kb + S - 1, (ST + S - 1) % S);
     const uint8_t* st = lds_all + ST * STAGE;
     const uint8_t* wl = st;
     const uint8_t* xl = st + WROWS * BLK;
@@ -414,6 +419,11 @@ __global__ __launch_bounds__(128 * WN, WN == 2 ? 2 : 1) void gemm_prefill_dma_ke
       bop[j] = pf_swz_operand(xl, mr, g);
       aop[j] = pf_swz_operand(wl, 64 * wn + 16 * j + l16, g);
       sc[j] = sl[mr] * sw;
+    }
+    if constexpr (EARLY) {
+      // every wave holds this block's operands: refill the stage
+      lds_barrier();
+      issue(kb + S, ST);
     }
     f32x4 pb[4][4];
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};

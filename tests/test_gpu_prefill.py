@@ -56,17 +56,19 @@ def test_prefill_parity_full_output(fp8bs, m, n, k):
     assert np.array_equal(host_bits(y), host_bits(y_q)), "fused cast differs from quantize-then-multiply"
 
 
-@pytest.mark.parametrize("variant", [(2, 1), (4, 1), (2, 2), (2, 4), (4, 2), (4, 3)])
+@pytest.mark.parametrize("variant", [(2, 1, 1), (4, 1, 1), (2, 2, 1), (2, 4, 1), (4, 2, 1), (4, 3, 1),
+                                     (2, 2, 2), (4, 2, 2), (4, 3, 2)])
 @pytest.mark.parametrize("m,n,k,split", [(300, 512, 1280, 1), (129, 768, 2048, 3), (64, 256, 384, 1),
                                          (33, 1024, 128, 1), (520, 256, 2560, 2)])
 def test_prefill_every_variant(fp8bs, variant, m, n, k, split):
     """Each compiled prefill kernel (4 or 8 waves; register pipeline, or a
-    ring of 2-4 LDS stages filled by direct loads), split and unsplit, one K
-    block (fewer blocks than stages), ragged m tails: full output against
-    the oracle."""
+    ring of 2-4 LDS stages filled by direct loads, refilled when the next
+    block starts or as soon as a block's operands are in registers), split
+    and unsplit, one K block (fewer blocks than stages), ragged m tails: full
+    output against the oracle."""
     from fp8_block_scaled_fp8bs_amd import Fp8bsError, GemmConfig
-    wn, depth = variant
-    cfg = GemmConfig(fp8bs.PATH_PREFILL, 1, wn, 2, depth, split)
+    wn, depth, tn = variant
+    cfg = GemmConfig(fp8bs.PATH_PREFILL, tn, wn, 2, depth, split)
     announce("prefill variant", cfg, m, n, k)
     x_bits, wq, ws, wq_ref, ws_ref = _problem(fp8bs, m, n, k, 7400 + m + n + k)
     if n % (64 * wn):
@@ -82,6 +84,27 @@ def test_prefill_every_variant(fp8bs, variant, m, n, k, split):
     y2 = fp8bs.gemm_ex(cfg, wq, ws, x=dev_bf16(x_bits))
     torch.cuda.synchronize()
     assert np.array_equal(host_bits(y), host_bits(y2))
+
+
+@pytest.mark.parametrize("m,n,k", [(300, 8192, 256), (1000, 16384, 128), (129, 8320, 256)])
+def test_prefill_wide_grid_tile_order(fp8bs, m, n, k):
+    """Wide unsplit grids (64 or more 128-column tiles) take the tile order
+    remapped per XCD when the tile count is a multiple of 8 (the first two
+    shapes) and the plain order otherwise (65 x 2 tiles): full output
+    against the oracle, fused cast equal to quantize-then-multiply."""
+    cfg = fp8bs.select_config(m, n, k)
+    announce("prefill wide grid", m, n, k, cfg)
+    assert cfg.path == fp8bs.PATH_PREFILL and cfg.split_k == 1
+    x_bits, wq, ws, wq_ref, ws_ref = _problem(fp8bs, m, n, k, 7500 + m + n + k)
+    x = dev_bf16(x_bits)
+    y = fp8bs.gemm(x, wq, ws)
+    xq, xs = fp8bs.quantize_act(x)
+    y_q = fp8bs.gemm_q(xq, xs, wq, ws)
+    torch.cuda.synchronize()
+    xq_ref, xs_ref = oracle.quantize_act_ref(x_bits)
+    rep = oracle.tolerance_report(host_bits(y), oracle.gemm_ref(xq_ref, xs_ref, wq_ref, ws_ref), **TOL)
+    assert rep["finite"] and rep["n_bad"] == 0, rep
+    assert np.array_equal(host_bits(y), host_bits(y_q))
 
 
 def test_prefill_run_to_run_identity(fp8bs):
