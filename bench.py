@@ -56,9 +56,9 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def stored_traffic(workload: str, m: int) -> dict | None:
+def stored_traffic(workload: str, m: int, layout: str) -> dict | None:
     """HBM traffic per launch from the committed rocprofv3 counter summary,
-    if it was taken on the current kernel sources."""
+    if it was taken on the current kernel sources and weight layout."""
     path = os.path.join(ROOT, "profiles", f"gemm_{workload}_m{m}_pmc.txt")
     if not os.path.exists(path):
         return None
@@ -69,6 +69,8 @@ def stored_traffic(workload: str, m: int) -> dict | None:
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
     if vals.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    if vals.get("weight_layout", "rows") != layout:
         return None
     try:
         return {"bytes_per_launch": float(vals["hbm_bytes_per_launch"]),
@@ -121,6 +123,7 @@ def step_mix(args, fp8bs, dev) -> int:
     from workloads import STEP_SHAPES, WORKLOADS, step_order
 
     order = step_order(256, 0)
+    gemm = fp8bs.gemm_tiles if args.weight_layout == "tiles" else fp8bs.gemm
     pools = {}
     gen = torch.Generator(device=dev)
     gen.manual_seed(1400)
@@ -130,8 +133,10 @@ def step_mix(args, fp8bs, dev) -> int:
         pool = []
         for _ in range(count):
             w = (torch.randn((wl.n, wl.k), generator=gen, device=dev, dtype=torch.float32) * 0.02).to(torch.bfloat16)
-            pool.append(fp8bs.quantize_weight(w))
+            wq, wsc = fp8bs.quantize_weight(w)
             del w
+            pool.append((fp8bs.pack_weight(wq), wsc) if args.weight_layout == "tiles" else (wq, wsc))
+            del wq
         pools[name] = pool
     torch.cuda.synchronize()
     for m in [int(v) for v in args.step_m.split(",")]:
@@ -148,7 +153,7 @@ def step_mix(args, fp8bs, dev) -> int:
                 pool = pools[name]
                 wq, wsc = pool[cursor[name] % len(pool)]
                 cursor[name] += 1
-                fp8bs.gemm(xs[name], wq, wsc, out=ys[name], workspace=workspace)
+                gemm(xs[name], wq, wsc, out=ys[name], workspace=workspace)
 
         for _ in range(2):
             one_step()
@@ -420,6 +425,9 @@ def main() -> int:
     ap.add_argument("--prefill-m", default="128,512,2048,8192", help="m values of --prefill")
     ap.add_argument("--prefill-shapes", default="square,mlp_up,mlp_down",
                     help="weight shapes of --prefill")
+    ap.add_argument("--weight-layout", default="tiles", choices=("tiles", "rows"),
+                    help="weight codes for the GEMM and step-mix modes: the tile layout "
+                         "(fp8bs_pack_weight, rearranged once before timing) or row-major")
     ap.add_argument("--mlp-swiglu", action="store_true",
                     help="MLP up/gate projection with the SwiGLU epilogue at every M; "
                          "prints one JSON line per M")
@@ -477,16 +485,25 @@ def main() -> int:
     x = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
     code_bytes = n * k
     pool_n = max(1, math.ceil(args.pool_gib * (1 << 30) / code_bytes))
-    pool = [fp8bs.quantize_weight(w0)]
+    tiles = args.weight_layout == "tiles" and m <= 32  # the tile layout serves decode sizes
+    layout = "tiles" if tiles else "rows"
+
+    def prepared(w):
+        # quantized once; in the tile layout, rearranged once (neither is timed)
+        wq, wsc = fp8bs.quantize_weight(w)
+        return (fp8bs.pack_weight(wq), wsc) if tiles else (wq, wsc)
+
+    pool = [prepared(w0)]
     del w0
     gen = torch.Generator(device=dev)
     gen.manual_seed(1400)
     for _ in range(pool_n - 1):
         wi = (torch.randn((n, k), generator=gen, device=dev, dtype=torch.float32) * 0.02).to(torch.bfloat16)
-        pool.append(fp8bs.quantize_weight(wi))
+        pool.append(prepared(wi))
         del wi
     torch.cuda.synchronize()
-    cfg = fp8bs.select_config(m, n, k)
+    cfg = fp8bs.tiles_select_config(m, n, k) if tiles else fp8bs.select_config(m, n, k)
+    gemm = fp8bs.gemm_tiles if tiles else fp8bs.gemm
     ws_bytes = fp8bs.workspace_bytes(m, n, k)
     workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
@@ -495,7 +512,7 @@ def main() -> int:
 
     def step(i):
         wq, wsc = pool[i % pool_n]
-        fp8bs.gemm(x, wq, wsc, out=y, workspace=workspace)
+        gemm(x, wq, wsc, out=y, workspace=workspace)
 
     launches0 = fp8bs.launch_count("gemm_mfma") + fp8bs.launch_count("gemm_dot")
     for i in range(args.warmup):
@@ -564,7 +581,7 @@ def main() -> int:
     step_ms = graph_ms if graph_ms is not None else eager_ms
     us = step_ms * 1e3
     gbps = alg_bytes / (us * 1e3)
-    traffic = stored_traffic(args.workload, m)
+    traffic = stored_traffic(args.workload, m, layout)
     roofline = {
         "bound": "hbm",
         "achieved": round(gbps, 1),
@@ -596,6 +613,7 @@ def main() -> int:
                        "waves_n": cfg.waves_n, "waves_k": cfg.waves_k, "depth": cfg.depth,
                        "split_k": cfg.split_k,
                        "launches_per_gemm": 2 if cfg.split_k > 1 and cfg.reduce == 0 else 1},
+            "weight_layout": layout,
             "timing": "hip graph of the steps, replayed" if graph_ms is not None else "stream launches",
         },
         "us_per_gemm": round(us, 3),

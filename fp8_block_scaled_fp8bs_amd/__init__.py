@@ -18,12 +18,14 @@ import torch  # loaded first so that libfp8bs binds to the HIP runtime torch use
 __all__ = [
     "Fp8bsError", "GemmConfig", "load", "library_path",
     "quantize_weight", "quantize_act", "gemm", "gemm_q", "gemm_ex",
+    "pack_weight", "gemm_tiles", "gemm_q_tiles", "tiles_select_config",
     "workspace_bytes", "config_workspace_bytes", "select_config",
     "swiglu_quant", "gemm_swiglu", "gemm_swiglu_ex", "swiglu_select_config",
     "swiglu_workspace_bytes",
     "encode_e4m3", "launch_count", "build_info", "diag_read", "diag_copy",
     "hip_runtime_mappings", "PATH_MFMA", "PATH_DOT", "REDUCE_KERNEL",
-    "REDUCE_LAST_ARRIVER", "EPILOGUE_SEPARATE", "EPILOGUE_IN_GEMM", "COUNTER",
+    "REDUCE_LAST_ARRIVER", "EPILOGUE_SEPARATE", "EPILOGUE_IN_GEMM", "LAYOUT_ROWS",
+    "LAYOUT_TILES", "COUNTER",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -34,8 +36,9 @@ PATH_AUTO, PATH_MFMA, PATH_DOT, PATH_MFMA_ROWS, PATH_MFMA_STREAM, PATH_PREFILL =
 PATH_MFMA_ROWS_REG = 6
 REDUCE_KERNEL, REDUCE_LAST_ARRIVER = 0, 1
 EPILOGUE_SEPARATE, EPILOGUE_IN_GEMM = 0, 1
+LAYOUT_ROWS, LAYOUT_TILES = 0, 1
 COUNTER = {"quant_weight": 0, "quant_act": 1, "gemm_mfma": 2, "gemm_dot": 3,
-           "split_reduce": 4, "encode": 5, "diag": 6, "swiglu": 7}
+           "split_reduce": 4, "encode": 5, "diag": 6, "swiglu": 7, "pack": 8}
 
 
 class Fp8bsError(RuntimeError):
@@ -49,7 +52,7 @@ class Fp8bsError(RuntimeError):
 class _Config(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int32) for name in
                 ("path", "tiles_n", "waves_n", "waves_k", "depth", "split_k", "reduce",
-                 "epilogue")]
+                 "epilogue", "weight_layout")]
 
 
 @dataclass(frozen=True)
@@ -63,15 +66,16 @@ class GemmConfig:
     split_k: int = 1
     reduce: int = REDUCE_KERNEL
     epilogue: int = EPILOGUE_SEPARATE
+    weight_layout: int = LAYOUT_ROWS
 
     def _c(self) -> _Config:
         return _Config(self.path, self.tiles_n, self.waves_n, self.waves_k, self.depth,
-                       self.split_k, self.reduce, self.epilogue)
+                       self.split_k, self.reduce, self.epilogue, self.weight_layout)
 
     @staticmethod
     def _from_c(c: _Config) -> "GemmConfig":
         return GemmConfig(c.path, c.tiles_n, c.waves_n, c.waves_k, c.depth, c.split_k, c.reduce,
-                          c.epilogue)
+                          c.epilogue, c.weight_layout)
 
 
 def library_path() -> str:
@@ -98,6 +102,10 @@ def load() -> ctypes.CDLL:
         "fp8bs_gemm_config_workspace_bytes": (sz, [ctypes.POINTER(_Config), i64, i64, i64]),
         "fp8bs_gemm_ex": (i32, [vp, vp, vp, i64, vp, vp, i64, i64, vp, vp, sz,
                                 ctypes.POINTER(_Config), vp]),
+        "fp8bs_pack_weight": (i32, [vp, i64, i64, vp, vp]),
+        "fp8bs_gemm_tiles": (i32, [vp, i64, vp, vp, i64, i64, vp, vp, sz, vp]),
+        "fp8bs_gemm_q_tiles": (i32, [vp, vp, i64, vp, vp, i64, i64, vp, vp, sz, vp]),
+        "fp8bs_gemm_tiles_select_config": (i32, [i64, i64, i64, ctypes.POINTER(_Config)]),
         "fp8bs_swiglu_quant": (i32, [vp, i64, i64, vp, vp, vp]),
         "fp8bs_gemm_swiglu": (i32, [vp, i64, vp, vp, i64, i64, vp, vp, vp, vp, sz, vp]),
         "fp8bs_gemm_swiglu_ex": (i32, [vp, vp, vp, i64, vp, vp, i64, i64, vp, vp, vp, vp, sz,
@@ -226,6 +234,52 @@ def gemm_q(x_q: torch.Tensor, x_s: torch.Tensor, w_q: torch.Tensor, w_s: torch.T
                                m, _dev(w_q, torch.uint8, "w_fp8", 2),
                                _dev(w_s, torch.float32, "w_scale", 2), n, k,
                                _dev(y, torch.bfloat16, "y", 2), ws, wl, _stream(stream)))
+    _done(wst, stream)
+    return y
+
+
+def pack_weight(w_q: torch.Tensor, out=None, stream=None) -> torch.Tensor:
+    """Weight codes [n][k] (row-major) rearranged into the tile layout the
+    *_tiles GEMM calls read (include/fp8bs.h); returned as a uint8 [n][k]
+    tensor whose bytes are in that layout."""
+    n, k = w_q.shape
+    t = out if out is not None else torch.empty((n, k), dtype=torch.uint8, device=w_q.device)
+    _check(load().fp8bs_pack_weight(_dev(w_q, torch.uint8, "w_fp8", 2), n, k,
+                                    _dev(t, torch.uint8, "w_tiles", 2), _stream(stream)))
+    return t
+
+
+def tiles_select_config(m: int, n: int, k: int) -> GemmConfig:
+    c = _Config()
+    _check(load().fp8bs_gemm_tiles_select_config(m, n, k, ctypes.byref(c)))
+    return GemmConfig._from_c(c)
+
+
+def gemm_tiles(x: torch.Tensor, w_t: torch.Tensor, w_s: torch.Tensor, out=None, workspace=None,
+               stream=None) -> torch.Tensor:
+    """gemm() on weights in the tile layout (pack_weight), m <= 32."""
+    m, k = x.shape
+    n = w_t.shape[0]
+    y, wst, ws, wl = _out_ws(m, n, x.device, out, workspace, workspace_bytes(m, n, k))
+    _check(load().fp8bs_gemm_tiles(_dev(x, torch.bfloat16, "x", 2), m,
+                                   _dev(w_t, torch.uint8, "w_tiles", 2),
+                                   _dev(w_s, torch.float32, "w_scale", 2), n, k,
+                                   _dev(y, torch.bfloat16, "y", 2), ws, wl, _stream(stream)))
+    _done(wst, stream)
+    return y
+
+
+def gemm_q_tiles(x_q: torch.Tensor, x_s: torch.Tensor, w_t: torch.Tensor, w_s: torch.Tensor,
+                 out=None, workspace=None, stream=None) -> torch.Tensor:
+    """gemm_q() on weights in the tile layout, m <= 32."""
+    m, k = x_q.shape
+    n = w_t.shape[0]
+    y, wst, ws, wl = _out_ws(m, n, x_q.device, out, workspace, workspace_bytes(m, n, k))
+    _check(load().fp8bs_gemm_q_tiles(_dev(x_q, torch.uint8, "x_fp8", 2),
+                                     _dev(x_s, torch.float32, "x_scale", 2), m,
+                                     _dev(w_t, torch.uint8, "w_tiles", 2),
+                                     _dev(w_s, torch.float32, "w_scale", 2), n, k,
+                                     _dev(y, torch.bfloat16, "y", 2), ws, wl, _stream(stream)))
     _done(wst, stream)
     return y
 

@@ -17,12 +17,12 @@ using namespace fp8bs;
 
 namespace {
 
-std::atomic<uint64_t> g_counts[8];
+std::atomic<uint64_t> g_counts[9];
 std::atomic<uint64_t> g_epoch{1};  // launch tags for the last-arriver counters (never 0)
 
 enum {
   CNT_QW = 0, CNT_QA = 1, CNT_MFMA = 2, CNT_DOT = 3, CNT_RED = 4, CNT_ENC = 5, CNT_DIAG = 6,
-  CNT_SWIGLU = 7
+  CNT_SWIGLU = 7, CNT_PACK = 8
 };
 
 constexpr int kMaxDevices = 64;
@@ -126,7 +126,7 @@ const KernelEntry* find_kernel(const fp8bs_gemm_config& c, int m, bool fused,
     // one kernel; it reads activation codes (the fused call casts them first)
     for (const KernelEntry& e : kernel_registry())
       if (e.path == FP8BS_PATH_PREFILL && !swiglu && e.wn == c.waves_n && e.d == c.depth &&
-          e.tn == c.tiles_n)
+          e.tn == c.tiles_n && e.layout == c.weight_layout)
         return &e;
     return nullptr;
   } else {
@@ -136,7 +136,8 @@ const KernelEntry* find_kernel(const fp8bs_gemm_config& c, int m, bool fused,
   for (const KernelEntry& e : kernel_registry())
     if (e.path == c.path && e.mt == mt && e.tn == c.tiles_n && (rows || e.wn == c.waves_n) &&
         e.wk == c.waves_k && e.d == c.depth && e.fused == (int)fused &&
-        e.variant == (rows ? (swiglu ? 1 : (c.split_k > 1 ? 2 : 0)) : 0))
+        e.variant == (rows ? (swiglu ? 1 : (c.split_k > 1 ? 2 : 0)) : 0) &&
+        e.layout == c.weight_layout)
       return &e;
   return nullptr;
 }
@@ -151,10 +152,13 @@ int config_rows(const fp8bs_gemm_config& c) {
 
 // Row range per workgroup of the row-range path: n split over the compute
 // units, rounded up to a multiple of 4 (the last workgroup may get fewer).
-int rows_per_workgroup(int64_t n, int num_cu) {
+// On tile-layout weights the ranges start on 16-row tiles (a multiple of
+// 16), so no 2 KB tile is fetched in two parts by two workgroups.
+int rows_per_workgroup(int64_t n, int num_cu, int layout = FP8BS_LAYOUT_ROWS) {
   const int64_t cu = num_cu > 0 ? num_cu : 1;
   const int64_t r = (n + cu - 1) / cu;
-  return (int)((r + 3) / 4 * 4);
+  const int64_t a = layout == FP8BS_LAYOUT_TILES ? 16 : 4;
+  return (int)((r + a - 1) / a * a);
 }
 
 size_t config_lds_bytes(const fp8bs_gemm_config& c, int m, int64_t n, int kbn, int num_cu,
@@ -166,7 +170,7 @@ size_t config_lds_bytes(const fp8bs_gemm_config& c, int m, int64_t n, int kbn, i
     // weight scales of the row range first, then the kernel's own layout,
     // then (SwiGLU epilogue) the staged outputs
     // (split: the longest K range of a workgroup)
-    const int rows = rows_per_workgroup(n, num_cu);
+    const int rows = rows_per_workgroup(n, num_cu, c.weight_layout);
     const int nblk = (kbn + c.split_k - 1) / c.split_k;
     const size_t ws = (size_t)lds_wscale_bytes(rows, nblk);
     const size_t ys = swiglu ? (size_t)lds_ystage_bytes(m, rows) : 0;
@@ -230,9 +234,13 @@ bool swiglu_supported(const fp8bs_gemm_config& c, int m) {
   return c.path == FP8BS_PATH_MFMA;
 }
 
-bool candidate_fits(const Candidate& cd, int64_t m, int64_t n, int kbn, fp8bs_gemm_config* out) {
+bool candidate_fits(const Candidate& cd, int64_t m, int64_t n, int kbn, fp8bs_gemm_config* out,
+                    int layout = FP8BS_LAYOUT_ROWS) {
   fp8bs_gemm_config c = make_cfg(cd.path, cd.tn, cd.wn, cd.wk, cd.d, cd.split);
   c.reduce = cd.split > 1 ? cd.reduce : RK;
+  c.weight_layout = layout;
+  // the tile layout is compiled for the kernels the table selects with it
+  if (layout != FP8BS_LAYOUT_ROWS && !find_kernel(c, (int)m, true)) return false;
   if (n % config_rows(c) != 0) return false;
   if (cd.path == DT && m > 4) return false;
   if (c.split_k > kbn) return false;
@@ -256,9 +264,19 @@ bool candidate_fits(const Candidate& cd, int64_t m, int64_t n, int kbn, fp8bs_ge
 // and the register-activation kernel takes the rest; a fallback list with
 // growing split catches everything else. The SwiGLU call (swiglu set) uses
 // the same choice with the separate epilogue, so its y equals fp8bs_gemm's.
-bool select_config(int64_t m, int64_t n, int64_t k, fp8bs_gemm_config* out, bool swiglu = false) {
+//
+// With the tile layout (layout = FP8BS_LAYOUT_TILES) a second table of the
+// same classes applies, measured the same way on tile-layout weights. The
+// grid kernels stream that layout faster than row-major weights (each load
+// instruction reads one contiguous KB), while the one-workgroup-per-CU
+// kernels on long row ranges do not, so this table takes the grid kernels
+// wherever they win; candidates without a tile-layout kernel are passed
+// over. The tile layout serves m <= 32.
+bool select_config(int64_t m, int64_t n, int64_t k, fp8bs_gemm_config* out, bool swiglu = false,
+                   int layout = FP8BS_LAYOUT_ROWS) {
   if (m < 0 || m > kMaxM || n < 0 || k < 0 || n % BLK || k % BLK) return false;
   if (swiglu && n % (2 * BLK)) return false;
+  if (layout != FP8BS_LAYOUT_ROWS && (swiglu || m > kMaxDecodeM)) return false;
   if (m > kMaxDecodeM && n > 0 && k > 0) {
     // prefill sizes: the tiled kernel with 4 waves on 128 x 128 output tiles
     // and two LDS stages filled by direct loads (two workgroups per compute
@@ -281,6 +299,7 @@ bool select_config(int64_t m, int64_t n, int64_t k, fp8bs_gemm_config* out, bool
   const int64_t nbn = n / BLK;
   if (m == 0 || n == 0 || kbn == 0) {
     *out = make_cfg(MF, 1, 1, 4, 5, 1);
+    out->weight_layout = layout;
     return true;
   }
   struct Cell {
@@ -322,13 +341,42 @@ bool select_config(int64_t m, int64_t n, int64_t k, fp8bs_gemm_config* out, bool
                                        {MF, 1, 1, 4, 5, 4, RK}, {MF, 1, 1, 4, 5, 8, RK},
                                        {MF, 1, 1, 4, 5, 16, RK}, {MF, 1, 1, 4, 5, 32, RK},
                                        {MF, 1, 1, 4, 5, 64, RK}};
+  static const Cell table_tiles[4][6] = {
+      // square-like
+      {{{{MF, 1, 2, 4, 5, 1, RK}}, 1},
+       {{{MF, 1, 2, 4, 5, 1, RK}}, 1},
+       {{{MF, 1, 2, 4, 5, 1, RK}, {MF, 1, 5, 1, 5, 4, RK}}, 2},
+       {{{MF, 1, 2, 4, 5, 1, RK}, {MF, 1, 5, 1, 5, 4, RK}}, 2},
+       {{{MF, 1, 8, 1, 5, 4, RK}, {MF, 1, 5, 1, 5, 4, RK}}, 2},
+       {{{MF, 1, 8, 1, 5, 4, RK}, {MF, 1, 5, 2, 5, 4, RK}}, 2}},
+      // deep K
+      {{{{MF, 1, 5, 2, 2, 4, RK}, {MF, 1, 5, 1, 5, 4, RK}}, 2},
+       {{{MF, 1, 5, 1, 5, 4, RK}, {MF, 1, 5, 2, 2, 4, RK}}, 2},
+       {{{MF, 1, 5, 1, 5, 4, RK}, {MF, 1, 5, 2, 2, 4, RK}}, 2},
+       {{{MF, 1, 8, 1, 5, 4, RK}, {MF, 1, 5, 2, 2, 4, RK}}, 2},
+       {{{MF, 1, 8, 1, 5, 4, RK}, {MF, 2, 5, 1, 5, 8, RK}}, 2},
+       {{{MF, 2, 5, 1, 5, 8, RK}, {MF, 1, 8, 1, 5, 4, RK}}, 2}},
+      // wide N
+      {{{{MF, 1, 1, 4, 5, 1, RK}, {MF, 1, 1, 8, 5, 1, RK}}, 2},
+       {{{MF, 1, 1, 8, 5, 1, RK}, {MF, 1, 1, 4, 5, 1, RK}}, 2},
+       {{{MF, 1, 1, 8, 5, 1, RK}, {RW, 1, 1, 8, 3, 1, RK}}, 2},
+       {{{RW, 1, 1, 8, 3, 1, RK}, {RW, 2, 1, 8, 6, 1, RK}}, 2},
+       {{{RW, 1, 1, 8, 3, 1, RK}, {RW, 2, 1, 8, 6, 1, RK}}, 2},
+       {{{RW, 2, 1, 8, 6, 1, RK}, {RR, 1, 1, 8, 5, 1, RK}, {MF, 1, 8, 1, 5, 4, RK}}, 3}},
+      // vocabulary-wide N
+      {{{{MF, 1, 1, 8, 5, 1, RK}, {MF, 1, 2, 4, 2, 1, RK}}, 2},
+       {{{MF, 1, 2, 4, 2, 1, RK}, {MF, 1, 1, 8, 5, 1, RK}}, 2},
+       {{{MF, 1, 2, 4, 2, 1, RK}, {MF, 1, 2, 4, 5, 1, RK}}, 2},
+       {{{MF, 1, 8, 1, 5, 1, RK}, {MF, 1, 2, 4, 5, 1, RK}}, 2},
+       {{{RW, 1, 1, 8, 3, 1, RK}, {MF, 1, 8, 1, 5, 1, RK}}, 2},
+       {{{RW, 1, 1, 8, 3, 1, RK}, {RR, 1, 1, 8, 5, 1, RK}, {MF, 1, 8, 1, 5, 2, RK}}, 3}}};
   const int shape = nbn >= 512 ? 3 : (nbn >= 200 ? 2 : (kbn > 48 ? 1 : 0));
   const int mc = m == 1 ? 0 : (m == 2 ? 1 : (m <= 4 ? 2 : (m <= 8 ? 3 : (m <= 16 ? 4 : 5))));
-  const Cell& cell = table[shape][mc];
+  const Cell& cell = layout == FP8BS_LAYOUT_ROWS ? table[shape][mc] : table_tiles[shape][mc];
   for (int i = 0; i < cell.n; ++i)
-    if (candidate_fits(cell.c[i], m, n, kbn, out)) return true;
+    if (candidate_fits(cell.c[i], m, n, kbn, out, layout)) return true;
   for (const Candidate& cd : fallback)
-    if (candidate_fits(cd, m, n, kbn, out)) return true;
+    if (candidate_fits(cd, m, n, kbn, out, layout)) return true;
   return false;
 }
 
@@ -386,7 +434,8 @@ fp8bs_status gemm_impl(const void* x_bf16, const uint8_t* x_fp8, const float* x_
                        const uint8_t* w_fp8, const float* w_scale, int64_t n, int64_t k,
                        void* y_bf16, void* workspace, size_t workspace_bytes,
                        const fp8bs_gemm_config* cfg_in, void* stream, bool swiglu = false,
-                       uint8_t* h_fp8 = nullptr, float* h_scale = nullptr) {
+                       uint8_t* h_fp8 = nullptr, float* h_scale = nullptr,
+                       int layout = FP8BS_LAYOUT_ROWS) {
   // shapes
   if (m < 0 || m > kMaxM || n < 0 || k < 0 || n % BLK || k % BLK) return FP8BS_ERR_SHAPE;
   if (n / BLK > (int64_t)1 << 24 || k / BLK > (int64_t)1 << 20) return FP8BS_ERR_SHAPE;
@@ -427,9 +476,12 @@ fp8bs_status gemm_impl(const void* x_bf16, const uint8_t* x_fp8, const float* x_
   fp8bs_gemm_config c;
   if (cfg_in) {
     c = *cfg_in;
-  } else if (!select_config(m, n, k, &c, swiglu)) {
+  } else if (!select_config(m, n, k, &c, swiglu, layout)) {
     return FP8BS_ERR_SHAPE;
   }
+  if (c.weight_layout != FP8BS_LAYOUT_ROWS &&
+      (c.weight_layout != FP8BS_LAYOUT_TILES || swiglu || c.path == FP8BS_PATH_PREFILL))
+    return FP8BS_ERR_CONFIG;
   if (c.split_k < 1 || c.split_k > 64 || c.split_k > kbn) return FP8BS_ERR_CONFIG;
   if (c.path == FP8BS_PATH_PREFILL ? c.reduce != FP8BS_REDUCE_KERNEL : m > kMaxDecodeM)
     return FP8BS_ERR_CONFIG;
@@ -497,7 +549,7 @@ fp8bs_status gemm_impl(const void* x_bf16, const uint8_t* x_fp8, const float* x_
   void* args[] = {&p};
   dim3 grid((unsigned)(n / rows), (unsigned)c.split_k);
   if (is_row_range(c.path)) {
-    p.rows_per_wg = rows_per_workgroup(n, dev.num_cu);
+    p.rows_per_wg = rows_per_workgroup(n, dev.num_cu, c.weight_layout);
     grid = dim3((unsigned)((n + p.rows_per_wg - 1) / p.rows_per_wg), (unsigned)c.split_k);
   }
   // the SwiGLU epilogue arrives on each (side, 128-column block) pair of a
@@ -614,7 +666,13 @@ size_t fp8bs_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k) {
   fp8bs_gemm_config c;
   if (!select_config(m, n, k, &c)) return 0;
   if (m == 0 || n == 0 || k == 0) return 0;
-  return cfg_workspace(c, m, n, k, true);
+  size_t need = cfg_workspace(c, m, n, k, true);
+  // enough for the tile-layout calls as well (they may select a split grid)
+  if (select_config(m, n, k, &c, false, FP8BS_LAYOUT_TILES)) {
+    const size_t t = cfg_workspace(c, m, n, k, true);
+    need = t > need ? t : need;
+  }
+  return need;
 }
 
 fp8bs_status fp8bs_gemm_select_config(int64_t m, int64_t n, int64_t k, fp8bs_gemm_config* out) {
@@ -636,6 +694,49 @@ fp8bs_status fp8bs_gemm_ex(const void* x_bf16, const uint8_t* x_fp8, const float
   if (!cfg) return FP8BS_ERR_NULL;
   return gemm_impl(x_bf16, x_fp8, x_scale, m, w_fp8, w_scale, n, k, y_bf16, workspace,
                    workspace_bytes, cfg, stream);
+}
+
+fp8bs_status fp8bs_pack_weight(const uint8_t* w_fp8, int64_t n, int64_t k, uint8_t* w_tiles,
+                               void* stream) {
+  if (n < 0 || k < 0 || n % BLK || k % BLK) return FP8BS_ERR_SHAPE;
+  if (n / BLK > (int64_t)1 << 24 || k / BLK > (int64_t)1 << 20) return FP8BS_ERR_SHAPE;
+  if (n == 0 || k == 0) return FP8BS_OK;
+  if (!w_fp8 || !w_tiles) return FP8BS_ERR_NULL;
+  if (!aligned(w_fp8, 16) || !aligned(w_tiles, 16)) return FP8BS_ERR_ALIGN;
+  const fp8bs_status st = current_device(nullptr);
+  if (st != FP8BS_OK) return st;
+  const uint4* src = reinterpret_cast<const uint4*>(w_fp8);
+  uint4* dst = reinterpret_cast<uint4*>(w_tiles);
+  int64_t chunks = n * k / 16, kc = k / 16, kbn = k / BLK;
+  void* args[] = {&src, &chunks, &kc, &kbn, &dst};
+  g_counts[CNT_PACK]++;
+  return launch(reinterpret_cast<const void*>(pack_weight_kernel),
+                dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, stream, args);
+}
+
+fp8bs_status fp8bs_gemm_tiles(const void* x_bf16, int64_t m, const uint8_t* w_tiles,
+                              const float* w_scale, int64_t n, int64_t k, void* y_bf16,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (m < 0 || m > kMaxDecodeM || n < 0 || k < 0 || n % BLK || k % BLK) return FP8BS_ERR_SHAPE;
+  if (!x_bf16 && m > 0 && n > 0 && k > 0) return FP8BS_ERR_NULL;
+  return gemm_impl(x_bf16, nullptr, nullptr, m, w_tiles, w_scale, n, k, y_bf16, workspace,
+                   workspace_bytes, nullptr, stream, false, nullptr, nullptr, FP8BS_LAYOUT_TILES);
+}
+
+fp8bs_status fp8bs_gemm_q_tiles(const uint8_t* x_fp8, const float* x_scale, int64_t m,
+                                const uint8_t* w_tiles, const float* w_scale, int64_t n,
+                                int64_t k, void* y_bf16, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+  if (m < 0 || m > kMaxDecodeM || n < 0 || k < 0 || n % BLK || k % BLK) return FP8BS_ERR_SHAPE;
+  return gemm_impl(nullptr, x_fp8, x_scale, m, w_tiles, w_scale, n, k, y_bf16, workspace,
+                   workspace_bytes, nullptr, stream, false, nullptr, nullptr, FP8BS_LAYOUT_TILES);
+}
+
+fp8bs_status fp8bs_gemm_tiles_select_config(int64_t m, int64_t n, int64_t k,
+                                            fp8bs_gemm_config* out) {
+  if (!out) return FP8BS_ERR_NULL;
+  if (!select_config(m, n, k, out, false, FP8BS_LAYOUT_TILES)) return FP8BS_ERR_SHAPE;
+  return FP8BS_OK;
 }
 
 fp8bs_status fp8bs_swiglu_quant(const void* y_bf16, int64_t m, int64_t inter, uint8_t* h_fp8,
@@ -721,7 +822,7 @@ const char* fp8bs_status_string(fp8bs_status s) {
 }
 
 uint64_t fp8bs_launch_count(int32_t which) {
-  if (which < 0 || which >= 8) return 0;
+  if (which < 0 || which >= 9) return 0;
   return g_counts[which].load();
 }
 

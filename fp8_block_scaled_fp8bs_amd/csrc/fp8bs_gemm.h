@@ -447,8 +447,33 @@ __device__ __forceinline__ i32x8 tile_operand(const TileLoad& t, bool lo8) {
   return r;
 }
 
+// Tile layout of the weight codes (written by fp8bs_pack_weight): the codes
+// of 16 rows x 128 columns (one MFMA A operand per K block) are 2 KB of
+// consecutive bytes, tile (R/16, kb) at byte ((R/16) * kbn + kb) * 2048.
+// Inside a tile, half h (columns 16h .. 16h+15 of each 32-column quarter)
+// fills the h-th KB, and lane 16g + R%16 of a wave (row R%16, quarter g,
+// the operand's lane order) owns the 16 bytes at (16g + R%16) * 16 of it.
+// One 16-byte load per lane and half then reads each half of an operand as
+// one contiguous KB, and the loaded registers are the operand as they are.
+// Returns the offset of W[R][128kb + 32g .. +15] (half 0; half 1 is +1024).
+__device__ __forceinline__ size_t tile_layout_off(int R, int kb, int kbn, int g) {
+  return ((size_t)(R >> 4) * (size_t)kbn + (size_t)kb) * 2048u +
+         (size_t)((16 * g + (R & 15)) * 16);
+}
+
+// The MFMA A operand of a loaded weight tile in either layout.
+template <bool PK>
+__device__ __forceinline__ i32x8 weight_operand(const TileLoad& t, bool lo8) {
+  if constexpr (PK) {
+    return i32x8{(int)t.p.x, (int)t.p.y, (int)t.p.z, (int)t.p.w,
+                 (int)t.q.x, (int)t.q.y, (int)t.q.z, (int)t.q.w};
+  } else {
+    return tile_operand(t, lo8);
+  }
+}
+
 // Body of the grid kernel for CR activation-load rounds per thread.
-template <int MT, int TN, int WN, int WK, int D, bool FUSED, int CR>
+template <int MT, int TN, int WN, int WK, int D, bool FUSED, int CR, bool PK>
 __device__ __forceinline__ void gemm_mfma_body(const GemmParams& p, uint8_t* lds_all) {
   constexpr int NT = 64 * WN * WK;
   constexpr int ROWS = 16 * TN * WN;
@@ -472,8 +497,12 @@ __device__ __forceinline__ void gemm_mfma_body(const GemmParams& p, uint8_t* lds
   const int l16 = lane & 15, g16 = lane >> 4;
   const int l7 = lane & 7, hb = (lane >> 3) & 1;
   const bool lo8 = hb == 0;
-  const uint8_t* wp = p.wq + (size_t)(row0 + l7) * (size_t)p.k + 16 * (2 * g16 + hb);
-  const uint8_t* wqp = p.wq + (size_t)(row0 + 8 + l7) * (size_t)p.k + 16 * (2 * g16 + 1 - hb);
+  // row-major: load P takes rows 0-7 of a tile, load Q rows 8-15 (see above);
+  // tile layout: lane l loads both halves of its own operand row l%16
+  const uint8_t* wp = PK ? p.wq + tile_layout_off(row0 + l16, 0, p.kbn, g16)
+                         : p.wq + (size_t)(row0 + l7) * (size_t)p.k + 16 * (2 * g16 + hb);
+  const uint8_t* wqp =
+      PK ? wp + 1024 : p.wq + (size_t)(row0 + 8 + l7) * (size_t)p.k + 16 * (2 * g16 + 1 - hb);
   const int nj = nblk > wk ? (nblk - wk + WK - 1) / WK : 0;  // this wave's K blocks
 
   // 1. activation bf16 loads first (so waiting for them does not wait on weights)
@@ -493,7 +522,8 @@ __device__ __forceinline__ void gemm_mfma_body(const GemmParams& p, uint8_t* lds
     kb = kb < p.kbn ? kb : p.kbn - 1;
 #pragma unroll
     for (int t = 0; t < TN; ++t) {
-      const size_t off = (size_t)t * 16 * (size_t)p.k + (size_t)kb * BLK;
+      const size_t off = PK ? ((size_t)t * (size_t)p.kbn + (size_t)kb) * 2048u
+                            : (size_t)t * 16 * (size_t)p.k + (size_t)kb * BLK;
       wb[d][t].p = load_stream16(wp + off);
       wb[d][t].q = load_stream16(wqp + off);
     }
@@ -540,7 +570,7 @@ __device__ __forceinline__ void gemm_mfma_body(const GemmParams& p, uint8_t* lds
     for (int t = 0; t < TN; ++t) {
       const int nb = (row0 + 16 * t) / BLK;
       const float sw = load_invariant(p.ws, (size_t)nb * (size_t)p.kbn + kb);
-      const i32x8 aop = tile_operand(wb[d][t], lo8);
+      const i32x8 aop = weight_operand<PK>(wb[d][t], lo8);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
@@ -621,7 +651,7 @@ __device__ __forceinline__ int act_rounds(int G, int NT) {
   return r < 1 ? 1 : (r > 3 ? 3 : r);
 }
 
-template <int MT, int TN, int WN, int WK, int D, bool FUSED>
+template <int MT, int TN, int WN, int WK, int D, bool FUSED, bool PK = false>
 __global__ __launch_bounds__(64 * WN * WK) void gemm_mfma_kernel(GemmParams p) {
   constexpr int NT = 64 * WN * WK;
   extern __shared__ __align__(16) uint8_t lds_all[];
@@ -630,13 +660,13 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_mfma_kernel(GemmParams p) {
     split_range(blockIdx.y, p.split, p.kbn, kb0, kb1);
     const int rounds = act_rounds((kb1 - kb0) * p.m * 4, NT);
     if (rounds == 1)
-      gemm_mfma_body<MT, TN, WN, WK, D, true, 1>(p, lds_all);
+      gemm_mfma_body<MT, TN, WN, WK, D, true, 1, PK>(p, lds_all);
     else if (rounds == 2)
-      gemm_mfma_body<MT, TN, WN, WK, D, true, 2>(p, lds_all);
+      gemm_mfma_body<MT, TN, WN, WK, D, true, 2, PK>(p, lds_all);
     else
-      gemm_mfma_body<MT, TN, WN, WK, D, true, 3>(p, lds_all);
+      gemm_mfma_body<MT, TN, WN, WK, D, true, 3, PK>(p, lds_all);
   } else {
-    gemm_mfma_body<MT, TN, WN, WK, D, false, 1>(p, lds_all);
+    gemm_mfma_body<MT, TN, WN, WK, D, false, 1, PK>(p, lds_all);
   }
 }
 
@@ -658,7 +688,7 @@ __global__ __launch_bounds__(64 * WN * WK) void gemm_mfma_kernel(GemmParams p) {
 // over grid.y: fp32 partial tiles part[s][m][n], summed by the reduce kernel).
 enum { ROWS_OUT_BF16 = 0, ROWS_OUT_SWIGLU = 1, ROWS_OUT_PARTIAL = 2 };
 
-template <int MT, int WK, int D, int PRE, bool FUSED, int OUTK = ROWS_OUT_BF16>
+template <int MT, int WK, int D, int PRE, bool FUSED, int OUTK = ROWS_OUT_BF16, bool PK = false>
 __global__ __launch_bounds__(64 * WK) void gemm_rows_kernel(GemmParams p) {
   constexpr int NT = 64 * WK;
   constexpr int CR = FUSED ? 3 : 1;
@@ -712,12 +742,21 @@ __global__ __launch_bounds__(64 * WK) void gemm_rows_kernel(GemmParams p) {
     const int t = i / njw, j = i - t * njw;
     int kbl = wk + j * WK;
     kbl = kbl < nblk ? kbl : nblk - 1;
-    int ra = 16 * t + l7, rb = 16 * t + 8 + l7;
-    ra = ra < nrows ? ra : nrows - 1;
-    rb = rb < nrows ? rb : nrows - 1;
-    const uint8_t* base = p.wq + (size_t)(kb0 + kbl) * BLK;
-    wb[d].p = load_stream16(base + (size_t)(r0 + ra) * (size_t)p.k + 16 * (2 * g16 + hb));
-    wb[d].q = load_stream16(base + (size_t)(r0 + rb) * (size_t)p.k + 16 * (2 * g16 + 1 - hb));
+    if constexpr (PK) {
+      // the range need not start on a 16-row tile: each lane addresses its row
+      int ra = 16 * t + l16;
+      ra = ra < nrows ? ra : nrows - 1;
+      const uint8_t* a = p.wq + tile_layout_off(r0 + ra, kb0 + kbl, p.kbn, g16);
+      wb[d].p = load_stream16(a);
+      wb[d].q = load_stream16(a + 1024);
+    } else {
+      int ra = 16 * t + l7, rb = 16 * t + 8 + l7;
+      ra = ra < nrows ? ra : nrows - 1;
+      rb = rb < nrows ? rb : nrows - 1;
+      const uint8_t* base = p.wq + (size_t)(kb0 + kbl) * BLK;
+      wb[d].p = load_stream16(base + (size_t)(r0 + ra) * (size_t)p.k + 16 * (2 * g16 + hb));
+      wb[d].q = load_stream16(base + (size_t)(r0 + rb) * (size_t)p.k + 16 * (2 * g16 + 1 - hb));
+    }
   };
   // Only PRE items are issued before the cast: a wave stalls at issue once
   // the memory queue is full, and the cast must not wait behind the whole
@@ -760,7 +799,7 @@ __global__ __launch_bounds__(64 * WK) void gemm_rows_kernel(GemmParams p) {
       int nbl = (r0 + 16 * t + 4 * g16) / BLK - nbf;
       nbl = nbl < nbr ? nbl : nbr - 1;
       const float sw = wsl[nbl * nblk + kb];
-      const i32x8 aop = tile_operand(wb[d], lo8);
+      const i32x8 aop = weight_operand<PK>(wb[d], lo8);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const int m = l16 + 16 * mt;
@@ -869,7 +908,7 @@ struct RegAct {
   float s[NJ][MT];   // activation scale of row l%16 + 16 mt (0 past m)
 };
 
-template <int MT, int WK, int NJ, int PRE, bool FUSED, bool SW = false>
+template <int MT, int WK, int NJ, int PRE, bool FUSED, bool SW = false, bool PK = false>
 __global__ __launch_bounds__(64 * WK) void gemm_rows_reg_kernel(GemmParams p) {
   constexpr int NT = 64 * WK;
   extern __shared__ __align__(16) uint8_t lds_all[];
@@ -909,12 +948,20 @@ __global__ __launch_bounds__(64 * WK) void gemm_rows_reg_kernel(GemmParams p) {
   TileLoad wb[NJ];
   auto load_slot = [&](int j, int t) {
     t = t < ntile ? t : ntile - 1;
-    int ra = 16 * t + l7, rb = 16 * t + 8 + l7;
-    ra = ra < nrows ? ra : nrows - 1;
-    rb = rb < nrows ? rb : nrows - 1;
-    const uint8_t* base = p.wq + (size_t)slot_block(j) * BLK;
-    wb[j].p = load_stream16(base + (size_t)(r0 + ra) * (size_t)p.k + 16 * (2 * g16 + hb));
-    wb[j].q = load_stream16(base + (size_t)(r0 + rb) * (size_t)p.k + 16 * (2 * g16 + 1 - hb));
+    if constexpr (PK) {
+      int ra = 16 * t + l16;
+      ra = ra < nrows ? ra : nrows - 1;
+      const uint8_t* a = p.wq + tile_layout_off(r0 + ra, slot_block(j), p.kbn, g16);
+      wb[j].p = load_stream16(a);
+      wb[j].q = load_stream16(a + 1024);
+    } else {
+      int ra = 16 * t + l7, rb = 16 * t + 8 + l7;
+      ra = ra < nrows ? ra : nrows - 1;
+      rb = rb < nrows ? rb : nrows - 1;
+      const uint8_t* base = p.wq + (size_t)slot_block(j) * BLK;
+      wb[j].p = load_stream16(base + (size_t)(r0 + ra) * (size_t)p.k + 16 * (2 * g16 + hb));
+      wb[j].q = load_stream16(base + (size_t)(r0 + rb) * (size_t)p.k + 16 * (2 * g16 + 1 - hb));
+    }
   };
   RegAct<MT, NJ> xa;
   ScaleFetch sf;
@@ -1048,7 +1095,7 @@ __global__ __launch_bounds__(64 * WK) void gemm_rows_reg_kernel(GemmParams p) {
         int nbl = (r0 + 16 * t + 4 * g16) / BLK - nbf;
         nbl = nbl < nbr ? nbl : nbr - 1;
         const float sw = wsl[nbl * nblk + kb];
-        const i32x8 aop = tile_operand(wb[j], lo8);
+        const i32x8 aop = weight_operand<PK>(wb[j], lo8);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           const f32x4 z = {0.f, 0.f, 0.f, 0.f};
@@ -1160,7 +1207,7 @@ struct ActFetch {
 };
 
 // XP = staging passes (1, 2, 4): 8 * XP >= m activation rows.
-template <int XP, int WK, int D, bool FUSED, bool SW = false>
+template <int XP, int WK, int D, bool FUSED, bool SW = false, bool PK = false>
 __global__ __launch_bounds__(64 * WK) void gemm_stream_kernel(GemmParams p) {
   constexpr int MT = XP > 2 ? 2 : 1;  // 16-row activation tiles of the MFMA B operand
   extern __shared__ __align__(16) uint8_t lds_all[];
@@ -1203,12 +1250,20 @@ __global__ __launch_bounds__(64 * WK) void gemm_stream_kernel(GemmParams p) {
     int kb = wk + j * WK;
     const bool stage = t == 0 && kb < kbn;
     kb = kb < kbn ? kb : kbn - 1;
-    int ra = 16 * t + l7, rb = 16 * t + 8 + l7;
-    ra = ra < nrows ? ra : nrows - 1;
-    rb = rb < nrows ? rb : nrows - 1;
-    const uint8_t* base = p.wq + (size_t)kb * BLK;
-    wb[d].p = load_stream16(base + (size_t)(r0 + ra) * (size_t)p.k + 16 * (2 * g16 + hb));
-    wb[d].q = load_stream16(base + (size_t)(r0 + rb) * (size_t)p.k + 16 * (2 * g16 + 1 - hb));
+    if constexpr (PK) {
+      int ra = 16 * t + l16;
+      ra = ra < nrows ? ra : nrows - 1;
+      const uint8_t* a = p.wq + tile_layout_off(r0 + ra, kb, kbn, g16);
+      wb[d].p = load_stream16(a);
+      wb[d].q = load_stream16(a + 1024);
+    } else {
+      int ra = 16 * t + l7, rb = 16 * t + 8 + l7;
+      ra = ra < nrows ? ra : nrows - 1;
+      rb = rb < nrows ? rb : nrows - 1;
+      const uint8_t* base = p.wq + (size_t)kb * BLK;
+      wb[d].p = load_stream16(base + (size_t)(r0 + ra) * (size_t)p.k + 16 * (2 * g16 + hb));
+      wb[d].q = load_stream16(base + (size_t)(r0 + rb) * (size_t)p.k + 16 * (2 * g16 + 1 - hb));
+    }
 #pragma unroll
     for (int c = 0; c < XP; ++c) {
       const int task = 64 * c + lane;
@@ -1293,7 +1348,7 @@ __global__ __launch_bounds__(64 * WK) void gemm_stream_kernel(GemmParams p) {
       int nbl = (r0 + 16 * t + 4 * g16) / BLK - nbf;
       nbl = nbl < nbr ? nbl : nbr - 1;
       const float sw = wsl[nbl * kbn + kb];
-      const i32x8 aop = tile_operand(wb[d], lo8);
+      const i32x8 aop = weight_operand<PK>(wb[d], lo8);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const int m = l16 + 16 * mt;

@@ -6,6 +6,23 @@
 
 namespace fp8bs {
 
+// Weight codes from row-major [n][k] to the tile layout the GEMM kernels
+// read with FP8BS_LAYOUT_TILES (tile_layout_off in fp8bs_gemm.h): 16-row x
+// 128-column tiles of 2 KB, each half of a wave's MFMA A operand one
+// contiguous KB. One thread per 16-byte chunk W[R][128kb + 32g + 16h ..]:
+// consecutive threads read consecutive chunks; the chunk goes to tile
+// (R/16, kb), half h, lane slot 16g + R%16.
+__global__ __launch_bounds__(256) void pack_weight_kernel(const uint4* __restrict__ src,
+                                                          int64_t chunks, int64_t kc, int64_t kbn,
+                                                          uint4* __restrict__ dst) {
+  const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= chunks) return;
+  const int64_t r = c / kc;
+  const int rem = (int)(c - r * kc);
+  const int kb = rem >> 3, g = (rem >> 1) & 3, h = rem & 1;
+  dst[((r >> 4) * kbn + kb) * 128 + h * 64 + 16 * g + (r & 15)] = src[c];
+}
+
 // One workgroup of 256 threads per 128x128 weight block. Thread t handles
 // half a block row: row t/2, columns 64*(t%2) .. +63 (128 contiguous bytes of
 // bf16 in, 64 contiguous bytes of codes out).

@@ -18,6 +18,7 @@ struct KernelEntry {
   int fused;   // activations cast in the kernel (1) or given as codes and scales (0)
   void (*fn)(GemmParams);
   int variant = 0;  // row-range kernels: 1 = SwiGLU epilogue, 2 = K split (fp32 partials)
+  int layout = 0;   // weight codes: 0 = row-major [n][k], 1 = tile layout (fp8bs_pack_weight)
 };
 
 std::vector<KernelEntry>& kernel_registry();
@@ -36,6 +37,13 @@ struct KernelRegistrar {
   {1, 1, TN, WN, WK, D, 0, gemm_mfma_kernel<1, TN, WN, WK, D, false>},    \
   {1, 2, TN, WN, WK, D, 0, gemm_mfma_kernel<2, TN, WN, WK, D, false>},
 
+// The same kernels reading weights in the tile layout.
+#define FP8BS_MFMA_TILES_ENTRY(TN, WN, WK, D)                                            \
+  {1, 1, TN, WN, WK, D, 1, gemm_mfma_kernel<1, TN, WN, WK, D, true, true>, 0, 1},        \
+  {1, 2, TN, WN, WK, D, 1, gemm_mfma_kernel<2, TN, WN, WK, D, true, true>, 0, 1},        \
+  {1, 1, TN, WN, WK, D, 0, gemm_mfma_kernel<1, TN, WN, WK, D, false, true>, 0, 1},       \
+  {1, 2, TN, WN, WK, D, 0, gemm_mfma_kernel<2, TN, WN, WK, D, false, true>, 0, 1},
+
 #define FP8BS_DOT_ENTRY(RT, WN, WK, D)                                    \
   {2, 1, RT, WN, WK, D, 1, gemm_dot_kernel<1, RT, WN, WK, D, true>},      \
   {2, 2, RT, WN, WK, D, 1, gemm_dot_kernel<2, RT, WN, WK, D, true>},      \
@@ -51,6 +59,12 @@ struct KernelRegistrar {
   {3, 2, PRE, 1, WK, D, 1, gemm_rows_kernel<2, WK, D, PRE, true>},           \
   {3, 1, PRE, 1, WK, D, 0, gemm_rows_kernel<1, WK, D, PRE, false>},          \
   {3, 2, PRE, 1, WK, D, 0, gemm_rows_kernel<2, WK, D, PRE, false>},
+
+#define FP8BS_ROWS_TILES_ENTRY(WK, D, PRE)                                                      \
+  {3, 1, PRE, 1, WK, D, 1, gemm_rows_kernel<1, WK, D, PRE, true, ROWS_OUT_BF16, true>, 0, 1},   \
+  {3, 2, PRE, 1, WK, D, 1, gemm_rows_kernel<2, WK, D, PRE, true, ROWS_OUT_BF16, true>, 0, 1},   \
+  {3, 1, PRE, 1, WK, D, 0, gemm_rows_kernel<1, WK, D, PRE, false, ROWS_OUT_BF16, true>, 0, 1},  \
+  {3, 2, PRE, 1, WK, D, 0, gemm_rows_kernel<2, WK, D, PRE, false, ROWS_OUT_BF16, true>, 0, 1},
 
 // Row-range kernels with the SwiGLU epilogue, for the configurations the
 // fused up/gate call selects.
@@ -101,3 +115,17 @@ struct KernelRegistrar {
   {4, 2, 1, 1, WK, D, 0, gemm_stream_kernel<2, WK, D, false>},               \
   {4, 4, 1, 1, WK, D, 0, gemm_stream_kernel<4, WK, D, false>},
 
+
+#define FP8BS_STREAM_TILES_ENTRY(WK, D)                                                  \
+  {4, 1, 1, 1, WK, D, 1, gemm_stream_kernel<1, WK, D, true, false, true>, 0, 1},        \
+  {4, 2, 1, 1, WK, D, 1, gemm_stream_kernel<2, WK, D, true, false, true>, 0, 1},        \
+  {4, 4, 1, 1, WK, D, 1, gemm_stream_kernel<4, WK, D, true, false, true>, 0, 1},        \
+  {4, 1, 1, 1, WK, D, 0, gemm_stream_kernel<1, WK, D, false, false, true>, 0, 1},       \
+  {4, 2, 1, 1, WK, D, 0, gemm_stream_kernel<2, WK, D, false, false, true>, 0, 1},       \
+  {4, 4, 1, 1, WK, D, 0, gemm_stream_kernel<4, WK, D, false, false, true>, 0, 1},
+
+#define FP8BS_ROWS_REG_TILES_ENTRY(WK, NJ, PRE)                                             \
+  {6, 1, PRE, 1, WK, NJ, 1, gemm_rows_reg_kernel<1, WK, NJ, PRE, true, false, true>, 0, 1},  \
+  {6, 2, PRE, 1, WK, NJ, 1, gemm_rows_reg_kernel<2, WK, NJ, PRE, true, false, true>, 0, 1},  \
+  {6, 1, PRE, 1, WK, NJ, 0, gemm_rows_reg_kernel<1, WK, NJ, PRE, false, false, true>, 0, 1}, \
+  {6, 2, PRE, 1, WK, NJ, 0, gemm_rows_reg_kernel<2, WK, NJ, PRE, false, false, true>, 0, 1},

@@ -122,7 +122,8 @@ fp8bs_status fp8bs_gemm_q(const uint8_t* x_fp8, const float* x_scale, int64_t m,
                           void* stream);
 
 /* Workspace bytes the automatically selected configuration needs (0 when
- * the K dimension is not split across workgroups). Returns 0 for shapes
+ * the K dimension is not split across workgroups), enough for both weight
+ * layouts (fp8bs_gemm* and fp8bs_gemm*_tiles). Returns 0 for shapes
  * fp8bs_gemm would reject.                                                  */
 size_t fp8bs_gemm_workspace_bytes(int64_t m, int64_t n, int64_t k);
 
@@ -139,6 +140,7 @@ enum {
 };
 enum { FP8BS_REDUCE_KERNEL = 0, FP8BS_REDUCE_LAST_ARRIVER = 1 };
 enum { FP8BS_EPILOGUE_SEPARATE = 0, FP8BS_EPILOGUE_IN_GEMM = 1 };
+enum { FP8BS_LAYOUT_ROWS = 0, FP8BS_LAYOUT_TILES = 1 };
 
 /* How one GEMM is laid out on the GPU.
  *   path      MFMA (16x16x128 FP8 matrix instructions, a grid of row
@@ -184,7 +186,12 @@ enum { FP8BS_EPILOGUE_SEPARATE = 0, FP8BS_EPILOGUE_IN_GEMM = 1 };
  *             FP8BS_EPILOGUE_IN_GEMM = (split_k == 1, MFMA grid or row-range
  *             paths) inside the GEMM launch: the workgroup that completes
  *             the outputs of a 128-column block of h, found with one 64-bit
- *             arrival counter per block in the workspace, applies it.     */
+ *             arrival counter per block in the workspace, applies it.
+ *   weight_layout  how w_fp8 is stored: FP8BS_LAYOUT_ROWS (row-major
+ *             [n][k], every path) or FP8BS_LAYOUT_TILES (the tile layout of
+ *             fp8bs_pack_weight; MFMA, MFMA_ROWS, MFMA_STREAM and
+ *             MFMA_ROWS_REG paths, for the kernel shapes the tile-layout
+ *             table selects; not with the SwiGLU calls, DOT or PREFILL).   */
 typedef struct {
   int32_t path;
   int32_t tiles_n;
@@ -194,6 +201,7 @@ typedef struct {
   int32_t split_k;
   int32_t reduce;
   int32_t epilogue;
+  int32_t weight_layout;
 } fp8bs_gemm_config;
 
 /* The configuration fp8bs_gemm uses for this shape (a fixed table: the same
@@ -213,6 +221,47 @@ fp8bs_status fp8bs_gemm_ex(const void* x_bf16, const uint8_t* x_fp8, const float
                            const uint8_t* w_fp8, const float* w_scale, int64_t n, int64_t k,
                            void* y_bf16, void* workspace, size_t workspace_bytes,
                            const fp8bs_gemm_config* cfg, void* stream);
+
+/* ---- tile layout of the weight codes -------------------------------------
+ * The same E4M3 codes and scales as above, stored so that the decode GEMM
+ * streams them with contiguous loads: the codes of 16 rows x 128 columns
+ * (one K block of one 16-row matrix-core tile) are 2 KB of consecutive
+ * bytes, tile (r/16, kb) at byte ((r/16) * (k/128) + kb) * 2048. Inside a
+ * tile, bytes 0..1023 hold columns 32g + 0..15 and bytes 1024..2047 columns
+ * 32g + 16..31 of each 32-column quarter g; within each KB the 16 bytes of
+ * row r%16, quarter g sit at (16g + r%16) * 16. The layout is a property of
+ * the storage only: the GEMM computes the product defined at the top of this
+ * header on the same codes, and with the same kernel configuration the
+ * result is bit-identical to the row-major call. Weights are rearranged
+ * once, like the quantization itself. The weight scales keep their layout.
+ * The tile layout serves the decode kernels: 0 <= m <= 32.                  */
+
+/* Rearrange row-major codes w_fp8 [n][k] into the tile layout (n*k bytes at
+ * w_tiles, which must not overlap w_fp8). Both pointers 16-byte aligned.   */
+fp8bs_status fp8bs_pack_weight(const uint8_t* w_fp8, int64_t n, int64_t k, uint8_t* w_tiles,
+                               void* stream);
+
+/* fp8bs_gemm on tile-layout weights (activation cast fused), 0 <= m <= 32;
+ * m > 32 is FP8BS_ERR_SHAPE. Workspace as for fp8bs_gemm
+ * (fp8bs_gemm_workspace_bytes covers both layouts).                         */
+fp8bs_status fp8bs_gemm_tiles(const void* x_bf16, int64_t m, const uint8_t* w_tiles,
+                              const float* w_scale, int64_t n, int64_t k, void* y_bf16,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* fp8bs_gemm_q on tile-layout weights; the same configuration as
+ * fp8bs_gemm_tiles, so fp8bs_gemm_tiles(x) == fp8bs_gemm_q_tiles(
+ * fp8bs_quantize_act(x)) bit for bit.                                       */
+fp8bs_status fp8bs_gemm_q_tiles(const uint8_t* x_fp8, const float* x_scale, int64_t m,
+                                const uint8_t* w_tiles, const float* w_scale, int64_t n,
+                                int64_t k, void* y_bf16, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/* The configuration fp8bs_gemm_tiles uses for this shape (weight_layout =
+ * FP8BS_LAYOUT_TILES): a fixed table of the same shape and m classes as
+ * fp8bs_gemm_select_config's, measured on tile-layout weights (the MFMA
+ * grid kernels gain most from the layout, so it takes them more often).    */
+fp8bs_status fp8bs_gemm_tiles_select_config(int64_t m, int64_t n, int64_t k,
+                                            fp8bs_gemm_config* out);
 
 /* ---- MLP epilogue: SwiGLU and the FP8 cast of its output ------------------
  * Fusing the element-wise steps between the matmuls of a transformer layer
@@ -293,7 +342,8 @@ const char* fp8bs_status_string(fp8bs_status s);
 /* Host-side count of launches of each kernel family since load: 0 = weight
  * quantizer, 1 = activation quantizer, 2 = MFMA GEMM, 3 = DOT GEMM,
  * 4 = split reduce (plain or with the SwiGLU epilogue), 5 = encoder utility,
- * 6 = read/copy diagnostics, 7 = standalone SwiGLU epilogue.
+ * 6 = read/copy diagnostics, 7 = standalone SwiGLU epilogue,
+ * 8 = weight rearrangement into the tile layout.
  * Lets a caller check that the kernels it benchmarks actually ran.          */
 uint64_t fp8bs_launch_count(int32_t which);
 

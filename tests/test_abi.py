@@ -218,3 +218,61 @@ def test_swiglu_config_rules(lib):
             assert fp8bs.swiglu_workspace_bytes(m, n, k, cin) >= (n // 256) * 8
     with pytest.raises(fp8bs.Fp8bsError):
         fp8bs.swiglu_select_config(8, 384, 128)
+
+
+def test_tile_layout_argument_errors(lib):
+    """Weight rearrangement and the tile-layout GEMM calls check their
+    arguments before any launch; the tile layout serves m <= 32 only."""
+    assert lib.fp8bs_pack_weight(P, 100, 128, P, None) == E_SHAPE
+    assert lib.fp8bs_pack_weight(P, 128, 130, P, None) == E_SHAPE
+    assert lib.fp8bs_pack_weight(None, 128, 128, P, None) == E_NULL
+    assert lib.fp8bs_pack_weight(P, 128, 128, None, None) == E_NULL
+    assert lib.fp8bs_pack_weight(P + 8, 128, 128, P, None) == E_ALIGN
+    assert lib.fp8bs_pack_weight(P, 128, 128, P + 4, None) == E_ALIGN
+    assert lib.fp8bs_pack_weight(None, 0, 128, None, None) == OK
+    g = lib.fp8bs_gemm_tiles
+    assert g(P, 33, P, P, 512, 1024, P, P, 1 << 20, None) == E_SHAPE
+    assert g(P, 8, P, P, 500, 1024, P, P, 1 << 20, None) == E_SHAPE
+    assert g(None, 8, P, P, 512, 1024, P, P, 1 << 20, None) == E_NULL
+    assert g(P, 8, P + 8, P, 512, 1024, P, P, 1 << 20, None) == E_ALIGN
+    assert lib.fp8bs_gemm_q_tiles(P, P, 33, P, P, 512, 1024, P, P, 1 << 20, None) == E_SHAPE
+    assert lib.fp8bs_gemm_q_tiles(P, None, 8, P, P, 512, 1024, P, P, 1 << 20, None) == E_NULL
+    import torch
+    if not torch.cuda.is_available():
+        assert lib.fp8bs_pack_weight(P, 128, 128, P, None) == E_DEV
+        assert g(P, 8, P, P, 512, 1024, P, P, 1 << 20, None) == E_DEV
+
+
+def test_tile_layout_config_rules(lib):
+    """The tile-layout table picks a kernel with a tile-layout build for
+    every decode m, as a pure function of the shape; SwiGLU and prefill
+    configurations reject the tile layout; the workspace query covers both
+    layouts."""
+    import fp8_block_scaled_fp8bs_amd as fp8bs
+    from fp8_block_scaled_fp8bs_amd import GemmConfig
+    for (n, k) in ((512, 1024), (5120, 5120), (34816, 5120), (5120, 17408), (248320, 5120)):
+        for m in range(1, 33):
+            t = fp8bs.tiles_select_config(m, n, k)
+            r = fp8bs.select_config(m, n, k)
+            assert t.weight_layout == fp8bs.LAYOUT_TILES and r.weight_layout == fp8bs.LAYOUT_ROWS
+            assert t.path in (fp8bs.PATH_MFMA, 3, 4, 6)
+            assert t == fp8bs.tiles_select_config(m, n, k)
+            assert 1 <= t.split_k <= k // 128
+            if t.path == fp8bs.PATH_MFMA:
+                assert n % (16 * t.tiles_n * t.waves_n) == 0
+            assert fp8bs.workspace_bytes(m, n, k) >= fp8bs.config_workspace_bytes(t, m, n, k)
+    with pytest.raises(fp8bs.Fp8bsError):
+        fp8bs.tiles_select_config(33, 5120, 5120)
+    c = GemmConfig(1, 1, 1, 4, 5, weight_layout=fp8bs.LAYOUT_TILES)._c()
+    r = lib.fp8bs_gemm_swiglu_ex(P, None, None, 8, P, P, 1024, 1024, P, P, P, P, 1 << 20,
+                                 ctypes.byref(c), None)
+    assert r == E_CFG
+    c = GemmConfig(5, 1, 2, 2, 2, weight_layout=fp8bs.LAYOUT_TILES)._c()
+    r = lib.fp8bs_gemm_ex(P, None, None, 64, P, P, 512, 1024, P, P, 1 << 24, ctypes.byref(c), None)
+    assert r == E_CFG
+    c = GemmConfig(1, 1, 1, 4, 5, weight_layout=2)._c()
+    r = lib.fp8bs_gemm_ex(P, None, None, 8, P, P, 512, 1024, P, None, 0, ctypes.byref(c), None)
+    assert r == E_CFG
+    c = GemmConfig(2, 2, 2, 4, 4, weight_layout=fp8bs.LAYOUT_TILES)._c()  # no DOT tile build
+    r = lib.fp8bs_gemm_ex(P, None, None, 1, P, P, 512, 1024, P, None, 0, ctypes.byref(c), None)
+    assert r == E_CFG
