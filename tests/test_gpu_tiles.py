@@ -95,7 +95,8 @@ def _random_problem(fp8bs, m, n, k, seed):
 @pytest.fixture(scope="module")
 def ragged(fp8bs):
     # K = 13 blocks (not a multiple of any waves_k, depth or split); N = 1280:
-    # the row-range kernels give each workgroup one 16-row tile
+    # the row-range kernels give each workgroup 8 rows (16-row ranges would
+    # idle most compute units), so ranges start in the middle of 16-row tiles
     return _random_problem(fp8bs, 32, 1280, 13 * 128, 4242)
 
 
@@ -218,3 +219,34 @@ def test_tiles_rejects_prefill_sizes(fp8bs, ragged):
     with pytest.raises(fp8bs.Fp8bsError):
         x = torch.zeros((33, ragged.x.shape[1]), dtype=torch.bfloat16, device="cuda")
         fp8bs.gemm_tiles(x, ragged.wt, ragged.ws)
+
+
+def test_tiles_graph_replays_match_eager(fp8bs, full):
+    """A tile-layout split configuration (fp32 partials in the workspace and
+    the reduce kernel) captured in a HIP graph: every replay, with eager work
+    and synchronizations between replays, equals the eager result."""
+    pr = full["mlp_down"]
+    x = pr.x[:8].contiguous()
+    n, k = pr.wq.shape
+    cfg = fp8bs.tiles_select_config(8, n, k)
+    assert cfg.split_k > 1
+    ws = torch.empty(fp8bs.workspace_bytes(8, n, k), dtype=torch.uint8, device="cuda")
+    y = torch.empty((8, n), dtype=torch.bfloat16, device="cuda")
+    eager = fp8bs.gemm_tiles(x, pr.wt, pr.ws)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        fp8bs.gemm_tiles(x, pr.wt, pr.ws, out=y, workspace=ws)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            fp8bs.gemm_tiles(x, pr.wt, pr.ws, out=y, workspace=ws)
+    torch.cuda.synchronize()
+    for i in range(4):
+        y.zero_()
+        ws.fill_(0x5A)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert _bits_equal(y, eager), f"replay {i}"
+        fp8bs.gemm_tiles(x, pr.wt, pr.ws)  # eager work between replays
