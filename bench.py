@@ -237,8 +237,9 @@ def mlp_swiglu(args, fp8bs, dev) -> int:
     5120 -> 34816 shape (inter 17408) with a rotating weight pool of at least
     --pool-gib GiB. Timed beside it, with the same launches in captured
     graphs: the plain GEMM alone, the GEMM followed by the standalone
-    epilogue call, and the epilogue inside the GEMM launch. One JSON line per
-    M. Algorithmic bytes of the fused call: weight codes and scales, bf16 X,
+    epilogue call, the epilogue inside the GEMM launch, and the fused call on
+    the same weights in the tile layout (fp8bs_gemm_swiglu_tiles). One JSON
+    line per M. Algorithmic bytes of the fused call: weight codes and scales, bf16 X,
     bf16 y (gate and up), h codes and h scales."""
     import dataclasses
 
@@ -257,6 +258,7 @@ def mlp_swiglu(args, fp8bs, dev) -> int:
         w = (torch.randn((n, k), generator=gen, device=dev, dtype=torch.float32) * 0.02).to(torch.bfloat16)
         pool.append(fp8bs.quantize_weight(w))
         del w
+    tiles = [fp8bs.pack_weight(wq) for wq, _ in pool]
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
@@ -292,7 +294,8 @@ def mlp_swiglu(args, fp8bs, dev) -> int:
         hs = torch.empty((m, inter // 128), dtype=torch.float32, device=dev)
         cfg = fp8bs.swiglu_select_config(m, n, k)
         inside = dataclasses.replace(cfg, epilogue=fp8bs.EPILOGUE_IN_GEMM) if cfg.split_k == 1 else None
-        ws_bytes = max(fp8bs.swiglu_workspace_bytes(m, n, k, c) for c in (cfg, inside) if c)
+        ws_bytes = max(max(fp8bs.swiglu_workspace_bytes(m, n, k, c) for c in (cfg, inside) if c),
+                       fp8bs.workspace_bytes(m, n, k))
         work = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
         P = len(pool)
         fused = timed(lambda i: fp8bs.gemm_swiglu(x, pool[i % P][0], pool[i % P][1], out=y,
@@ -304,6 +307,9 @@ def mlp_swiglu(args, fp8bs, dev) -> int:
         in_gemm = (timed(lambda i: fp8bs.gemm_swiglu_ex(inside, pool[i % P][0], pool[i % P][1], x=x,
                                                         out=y, h=(hq, hs), workspace=work), steps)
                    if inside is not None else None)
+        fused_tiles = (timed(lambda i: fp8bs.gemm_swiglu_tiles(x, tiles[i % P], pool[i % P][1], out=y,
+                                                               h=(hq, hs), workspace=work), steps)
+                       if m <= 32 else None)
         nbytes = (n * k + 4 * (n // 128) * (k // 128) + 2 * m * k + 2 * m * n + m * inter
                   + 4 * m * (inter // 128))
         print(json.dumps({
@@ -315,6 +321,8 @@ def mlp_swiglu(args, fp8bs, dev) -> int:
             "us_plain_gemm": round(plain, 3),
             "us_gemm_then_epilogue_call": round(two, 3),
             "us_epilogue_in_gemm": round(in_gemm, 3) if in_gemm is not None else None,
+            "us_fused_call_tiles": round(fused_tiles, 3) if fused_tiles is not None else None,
+            "config_tiles": dataclasses.asdict(fp8bs.tiles_select_config(m, n, k)) if m <= 32 else None,
             "timing": f"captured graph of {steps} calls over a {P}-weight pool, best of 3 replays"}),
             flush=True)
         del x, y, hq, hs, work

@@ -18,7 +18,7 @@ import torch  # loaded first so that libfp8bs binds to the HIP runtime torch use
 __all__ = [
     "Fp8bsError", "GemmConfig", "load", "library_path",
     "quantize_weight", "quantize_act", "gemm", "gemm_q", "gemm_ex",
-    "pack_weight", "gemm_tiles", "gemm_q_tiles", "tiles_select_config",
+    "pack_weight", "gemm_tiles", "gemm_q_tiles", "tiles_select_config", "gemm_swiglu_tiles",
     "workspace_bytes", "config_workspace_bytes", "select_config",
     "swiglu_quant", "gemm_swiglu", "gemm_swiglu_ex", "swiglu_select_config",
     "swiglu_workspace_bytes",
@@ -106,6 +106,7 @@ def load() -> ctypes.CDLL:
         "fp8bs_gemm_tiles": (i32, [vp, i64, vp, vp, i64, i64, vp, vp, sz, vp]),
         "fp8bs_gemm_q_tiles": (i32, [vp, vp, i64, vp, vp, i64, i64, vp, vp, sz, vp]),
         "fp8bs_gemm_tiles_select_config": (i32, [i64, i64, i64, ctypes.POINTER(_Config)]),
+        "fp8bs_gemm_swiglu_tiles": (i32, [vp, i64, vp, vp, i64, i64, vp, vp, vp, vp, sz, vp]),
         "fp8bs_swiglu_quant": (i32, [vp, i64, i64, vp, vp, vp]),
         "fp8bs_gemm_swiglu": (i32, [vp, i64, vp, vp, i64, i64, vp, vp, vp, vp, sz, vp]),
         "fp8bs_gemm_swiglu_ex": (i32, [vp, vp, vp, i64, vp, vp, i64, i64, vp, vp, vp, vp, sz,
@@ -355,6 +356,25 @@ def gemm_swiglu(x: torch.Tensor, w_q: torch.Tensor, w_s: torch.Tensor, out=None,
                                     _dev(hq, torch.uint8, "h_fp8", 2),
                                     _dev(hs, torch.float32, "h_scale", 2), ws, wl,
                                     _stream(stream)))
+    _done(wst, stream)
+    return y, hq, hs
+
+
+def gemm_swiglu_tiles(x: torch.Tensor, w_t: torch.Tensor, w_s: torch.Tensor, out=None, h=None,
+                      workspace=None, stream=None):
+    """gemm_swiglu() on weights in the tile layout (pack_weight), m <= 32:
+    y as gemm_tiles() gives it, h as swiglu_quant(y)."""
+    m, k = x.shape
+    n = w_t.shape[0]
+    y, wst, ws, wl = _out_ws(m, n, x.device, out, workspace, workspace_bytes(m, n, k))
+    hq, hs = _h_out(m, n // 2, x.device, h)
+    _check(load().fp8bs_gemm_swiglu_tiles(_dev(x, torch.bfloat16, "x", 2), m,
+                                          _dev(w_t, torch.uint8, "w_tiles", 2),
+                                          _dev(w_s, torch.float32, "w_scale", 2), n, k,
+                                          _dev(y, torch.bfloat16, "y", 2),
+                                          _dev(hq, torch.uint8, "h_fp8", 2),
+                                          _dev(hs, torch.float32, "h_scale", 2), ws, wl,
+                                          _stream(stream)))
     _done(wst, stream)
     return y, hq, hs
 

@@ -283,7 +283,7 @@ bool select_config(int64_t m, int64_t n, int64_t k, fp8bs_gemm_config* out, bool
                    int layout = FP8BS_LAYOUT_ROWS) {
   if (m < 0 || m > kMaxM || n < 0 || k < 0 || n % BLK || k % BLK) return false;
   if (swiglu && n % (2 * BLK)) return false;
-  if (layout != FP8BS_LAYOUT_ROWS && (swiglu || m > kMaxDecodeM)) return false;
+  if (layout != FP8BS_LAYOUT_ROWS && m > kMaxDecodeM) return false;
   if (m > kMaxDecodeM && n > 0 && k > 0) {
     // prefill sizes: the tiled kernel with 4 waves on 128 x 128 output tiles
     // and two LDS stages filled by direct loads (two workgroups per compute
@@ -486,8 +486,11 @@ fp8bs_status gemm_impl(const void* x_bf16, const uint8_t* x_fp8, const float* x_
   } else if (!select_config(m, n, k, &c, swiglu, layout)) {
     return FP8BS_ERR_SHAPE;
   }
+  // tile layout: plain kernels only (the SwiGLU epilogue runs after the split
+  // sum or in a second kernel), no prefill path
   if (c.weight_layout != FP8BS_LAYOUT_ROWS &&
-      (c.weight_layout != FP8BS_LAYOUT_TILES || swiglu || c.path == FP8BS_PATH_PREFILL))
+      (c.weight_layout != FP8BS_LAYOUT_TILES || c.path == FP8BS_PATH_PREFILL ||
+       (swiglu && c.epilogue != FP8BS_EPILOGUE_SEPARATE)))
     return FP8BS_ERR_CONFIG;
   if (c.split_k < 1 || c.split_k > 64 || c.split_k > kbn) return FP8BS_ERR_CONFIG;
   if (c.path == FP8BS_PATH_PREFILL ? c.reduce != FP8BS_REDUCE_KERNEL : m > kMaxDecodeM)
@@ -768,6 +771,17 @@ fp8bs_status fp8bs_gemm_swiglu(const void* x_bf16, int64_t m, const uint8_t* w_f
   }
   return gemm_impl(x_bf16, nullptr, nullptr, m, w_fp8, w_scale, n, k, y_bf16, workspace,
                    workspace_bytes, nullptr, stream, true, h_fp8, h_scale);
+}
+
+fp8bs_status fp8bs_gemm_swiglu_tiles(const void* x_bf16, int64_t m, const uint8_t* w_tiles,
+                                     const float* w_scale, int64_t n, int64_t k, void* y_bf16,
+                                     uint8_t* h_fp8, float* h_scale, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  if (m < 0 || m > kMaxDecodeM || n < 0 || k < 0 || n % (2 * BLK) || k % BLK)
+    return FP8BS_ERR_SHAPE;
+  if (!x_bf16 && m > 0 && n > 0 && k > 0) return FP8BS_ERR_NULL;
+  return gemm_impl(x_bf16, nullptr, nullptr, m, w_tiles, w_scale, n, k, y_bf16, workspace,
+                   workspace_bytes, nullptr, stream, true, h_fp8, h_scale, FP8BS_LAYOUT_TILES);
 }
 
 fp8bs_status fp8bs_gemm_swiglu_ex(const void* x_bf16, const uint8_t* x_fp8, const float* x_scale,

@@ -191,7 +191,8 @@ enum { FP8BS_LAYOUT_ROWS = 0, FP8BS_LAYOUT_TILES = 1 };
  *             [n][k], every path) or FP8BS_LAYOUT_TILES (the tile layout of
  *             fp8bs_pack_weight; MFMA, MFMA_ROWS, MFMA_STREAM and
  *             MFMA_ROWS_REG paths, for the kernel shapes the tile-layout
- *             table selects; not with the SwiGLU calls, DOT or PREFILL).   */
+ *             table selects; not with DOT or PREFILL, nor with the SwiGLU
+ *             epilogue inside the GEMM).                                   */
 typedef struct {
   int32_t path;
   int32_t tiles_n;
@@ -234,7 +235,8 @@ fp8bs_status fp8bs_gemm_ex(const void* x_bf16, const uint8_t* x_fp8, const float
  * header on the same codes, and with the same kernel configuration the
  * result is bit-identical to the row-major call. Weights are rearranged
  * once, like the quantization itself. The weight scales keep their layout.
- * The tile layout serves the decode kernels: 0 <= m <= 32.                  */
+ * The tile layout serves the decode kernels: 0 <= m <= 32 (the plain GEMM
+ * calls below and fp8bs_gemm_swiglu_tiles).                                 */
 
 /* Rearrange row-major codes w_fp8 [n][k] into the tile layout (n*k bytes at
  * w_tiles, which must not overlap w_fp8). Both pointers 16-byte aligned.   */
@@ -302,6 +304,16 @@ fp8bs_status fp8bs_gemm_swiglu(const void* x_bf16, int64_t m, const uint8_t* w_f
                                const float* w_scale, int64_t n, int64_t k, void* y_bf16,
                                uint8_t* h_fp8, float* h_scale, void* workspace,
                                size_t workspace_bytes, void* stream);
+
+/* fp8bs_gemm_swiglu on tile-layout weights (fp8bs_pack_weight), 0 <= m <= 32:
+ * y bit-identical to fp8bs_gemm_tiles on the same inputs, h as
+ * fp8bs_swiglu_quant(y). The epilogue runs after the split sum or in a
+ * second kernel (FP8BS_EPILOGUE_SEPARATE); workspace as for
+ * fp8bs_gemm_tiles (fp8bs_gemm_workspace_bytes covers it).                  */
+fp8bs_status fp8bs_gemm_swiglu_tiles(const void* x_bf16, int64_t m, const uint8_t* w_tiles,
+                                     const float* w_scale, int64_t n, int64_t k, void* y_bf16,
+                                     uint8_t* h_fp8, float* h_scale, void* workspace,
+                                     size_t workspace_bytes, void* stream);
 
 /* Same with an explicit configuration (cfg != NULL; x_bf16 != NULL selects
  * the fused cast, otherwise x_fp8 / x_scale). Accepted with

@@ -245,9 +245,9 @@ def test_tile_layout_argument_errors(lib):
 
 def test_tile_layout_config_rules(lib):
     """The tile-layout table picks a kernel with a tile-layout build for
-    every decode m, as a pure function of the shape; SwiGLU and prefill
-    configurations reject the tile layout; the workspace query covers both
-    layouts."""
+    every decode m, as a pure function of the shape; the in-GEMM SwiGLU
+    epilogue and prefill configurations reject the tile layout; the
+    workspace query covers both layouts."""
     import fp8_block_scaled_fp8bs_amd as fp8bs
     from fp8_block_scaled_fp8bs_amd import GemmConfig
     for (n, k) in ((512, 1024), (5120, 5120), (34816, 5120), (5120, 17408), (248320, 5120)):
@@ -263,10 +263,20 @@ def test_tile_layout_config_rules(lib):
             assert fp8bs.workspace_bytes(m, n, k) >= fp8bs.config_workspace_bytes(t, m, n, k)
     with pytest.raises(fp8bs.Fp8bsError):
         fp8bs.tiles_select_config(33, 5120, 5120)
-    c = GemmConfig(1, 1, 1, 4, 5, weight_layout=fp8bs.LAYOUT_TILES)._c()
+    c = GemmConfig(1, 1, 1, 4, 5, epilogue=1, weight_layout=fp8bs.LAYOUT_TILES)._c()
     r = lib.fp8bs_gemm_swiglu_ex(P, None, None, 8, P, P, 1024, 1024, P, P, P, P, 1 << 20,
                                  ctypes.byref(c), None)
-    assert r == E_CFG
+    assert r == E_CFG  # the epilogue inside the GEMM has no tile-layout build
+    assert lib.fp8bs_gemm_swiglu_tiles(P, 33, P, P, 1024, 1024, P, P, P, P, 1 << 20, None) == E_SHAPE
+    assert lib.fp8bs_gemm_swiglu_tiles(P, 8, P, P, 1152, 1024, P, P, P, P, 1 << 20, None) == E_SHAPE
+    assert lib.fp8bs_gemm_swiglu_tiles(None, 8, P, P, 1024, 1024, P, P, P, P, 1 << 20, None) == E_NULL
+    import torch
+    if not torch.cuda.is_available():
+        c = GemmConfig(1, 1, 1, 4, 5, weight_layout=fp8bs.LAYOUT_TILES)._c()
+        r = lib.fp8bs_gemm_swiglu_ex(P, None, None, 8, P, P, 1024, 1024, P, P, P, P, 1 << 20,
+                                     ctypes.byref(c), None)
+        assert r == E_DEV
+        assert lib.fp8bs_gemm_swiglu_tiles(P, 8, P, P, 1024, 1024, P, P, P, P, 1 << 20, None) == E_DEV
     c = GemmConfig(5, 1, 2, 2, 2, weight_layout=fp8bs.LAYOUT_TILES)._c()
     r = lib.fp8bs_gemm_ex(P, None, None, 64, P, P, 512, 1024, P, P, 1 << 24, ctypes.byref(c), None)
     assert r == E_CFG

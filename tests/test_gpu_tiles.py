@@ -250,3 +250,21 @@ def test_tiles_graph_replays_match_eager(fp8bs, full):
         torch.cuda.synchronize()
         assert _bits_equal(y, eager), f"replay {i}"
         fp8bs.gemm_tiles(x, pr.wt, pr.ws)  # eager work between replays
+
+
+@pytest.mark.parametrize("m", [1, 2, 4, 8, 16, 32])
+def test_swiglu_tiles(fp8bs, full, m):
+    """The up/gate projection with the SwiGLU epilogue on tile-layout
+    weights: y equals the plain tile-layout GEMM bit for bit, and h equals
+    the standalone epilogue applied to that y (itself checked against the
+    oracle in the SwiGLU tests)."""
+    pr = full["mlp_up"]
+    x = pr.x[:m].contiguous()
+    announce("swiglu tiles", m, fp8bs.tiles_select_config(m, *pr.wq.shape))
+    y, hq, hs = fp8bs.gemm_swiglu_tiles(x, pr.wt, pr.ws)
+    y_plain = fp8bs.gemm_tiles(x, pr.wt, pr.ws)
+    hq2, hs2 = fp8bs.swiglu_quant(y)
+    torch.cuda.synchronize()
+    assert _bits_equal(y, y_plain)
+    assert torch.equal(hq, hq2)
+    assert same_bits_f32(hs.cpu().numpy(), hs2.cpu().numpy())
