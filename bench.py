@@ -381,6 +381,7 @@ def prefill(args, fp8bs, dev) -> int:
             w = (torch.randn((n, k), generator=gen, device=dev, dtype=torch.float32) * 0.02).to(torch.bfloat16)
             pool.append(fp8bs.quantize_weight(w))
             del w
+        tiles = [fp8bs.pack_weight(wq) for wq, _ in pool]
         wbf = (torch.randn((n, k), generator=gen, device=dev, dtype=torch.float32) * 0.02).to(torch.bfloat16)
         P = len(pool)
         for m in [int(v) for v in args.prefill_m.split(",")]:
@@ -393,6 +394,8 @@ def prefill(args, fp8bs, dev) -> int:
             t_fused = timed(lambda i: fp8bs.gemm(x, pool[i % P][0], pool[i % P][1], out=y,
                                                  workspace=work), steps)
             t_q = timed(lambda i: fp8bs.gemm_q(xq, xs, pool[i % P][0], pool[i % P][1], out=y), steps)
+            t_qt = timed(lambda i: fp8bs.gemm_q_tiles(xq, xs, tiles[i % P], pool[i % P][1], out=y,
+                                                      workspace=work), steps)
             t_lib = timed(lambda i: torch.nn.functional.linear(x, wbf), steps)
             cfg = fp8bs.select_config(m, n, k)
             print(json.dumps({
@@ -401,11 +404,12 @@ def prefill(args, fp8bs, dev) -> int:
                 "us_fused_call": round(t_fused, 2), "TFLOPs_fused_call": round(flop / (t_fused * 1e6), 1),
                 "us_gemm_q": round(t_q, 2), "TFLOPs_gemm_q": round(flop / (t_q * 1e6), 1),
                 "pct_of_fp8_peak_gemm_q": round(100 * flop / (t_q * 1e6) / MFMA_FP8_PEAK_TFLOPS, 2),
+                "us_gemm_q_tiles": round(t_qt, 2), "TFLOPs_gemm_q_tiles": round(flop / (t_qt * 1e6), 1),
                 "bf16_library_us": round(t_lib, 2), "bf16_library_TFLOPs": round(flop / (t_lib * 1e6), 1),
                 "timing": f"captured graph of {steps} calls over a {P}-weight pool, best of 3 replays"}),
                 flush=True)
             del x, xq, xs, y, work
-        del pool, wbf
+        del pool, tiles, wbf
     return 0
 
 

@@ -258,7 +258,7 @@ def tiles_select_config(m: int, n: int, k: int) -> GemmConfig:
 
 def gemm_tiles(x: torch.Tensor, w_t: torch.Tensor, w_s: torch.Tensor, out=None, workspace=None,
                stream=None) -> torch.Tensor:
-    """gemm() on weights in the tile layout (pack_weight), m <= 32."""
+    """gemm() on weights in the tile layout (pack_weight)."""
     m, k = x.shape
     n = w_t.shape[0]
     y, wst, ws, wl = _out_ws(m, n, x.device, out, workspace, workspace_bytes(m, n, k))
@@ -272,7 +272,7 @@ def gemm_tiles(x: torch.Tensor, w_t: torch.Tensor, w_s: torch.Tensor, out=None, 
 
 def gemm_q_tiles(x_q: torch.Tensor, x_s: torch.Tensor, w_t: torch.Tensor, w_s: torch.Tensor,
                  out=None, workspace=None, stream=None) -> torch.Tensor:
-    """gemm_q() on weights in the tile layout, m <= 32."""
+    """gemm_q() on weights in the tile layout."""
     m, k = x_q.shape
     n = w_t.shape[0]
     y, wst, ws, wl = _out_ws(m, n, x_q.device, out, workspace, workspace_bytes(m, n, k))
@@ -362,8 +362,8 @@ def gemm_swiglu(x: torch.Tensor, w_q: torch.Tensor, w_s: torch.Tensor, out=None,
 
 def gemm_swiglu_tiles(x: torch.Tensor, w_t: torch.Tensor, w_s: torch.Tensor, out=None, h=None,
                       workspace=None, stream=None):
-    """gemm_swiglu() on weights in the tile layout (pack_weight), m <= 32:
-    y as gemm_tiles() gives it, h as swiglu_quant(y)."""
+    """gemm_swiglu() on weights in the tile layout (pack_weight): y as
+    gemm_tiles() gives it, h as swiglu_quant(y)."""
     m, k = x.shape
     n = w_t.shape[0]
     y, wst, ws, wl = _out_ws(m, n, x.device, out, workspace, workspace_bytes(m, n, k))

@@ -278,12 +278,11 @@ bool candidate_fits(const Candidate& cd, int64_t m, int64_t n, int kbn, fp8bs_ge
 // instruction reads one contiguous KB), while the one-workgroup-per-CU
 // kernels on long row ranges do not, so this table takes the grid kernels
 // wherever they win; candidates without a tile-layout kernel are passed
-// over. The tile layout serves m <= 32.
+// over. Prefill sizes take the direct-load kernel in either layout.
 bool select_config(int64_t m, int64_t n, int64_t k, fp8bs_gemm_config* out, bool swiglu = false,
                    int layout = FP8BS_LAYOUT_ROWS) {
   if (m < 0 || m > kMaxM || n < 0 || k < 0 || n % BLK || k % BLK) return false;
   if (swiglu && n % (2 * BLK)) return false;
-  if (layout != FP8BS_LAYOUT_ROWS && m > kMaxDecodeM) return false;
   if (m > kMaxDecodeM && n > 0 && k > 0) {
     // prefill sizes: the tiled kernel with 4 waves on 128 x 128 output tiles
     // and two LDS stages filled by direct loads (two workgroups per compute
@@ -300,6 +299,7 @@ bool select_config(int64_t m, int64_t n, int64_t k, fp8bs_gemm_config* out, bool
     split = split < max_split ? split : max_split;
     split = split < 1 ? 1 : split;
     *out = make_cfg(FP8BS_PATH_PREFILL, 1, wn, 2, 2, (int)split);
+    out->weight_layout = layout;
     return true;
   }
   const int kbn = (int)(k / BLK);
@@ -487,11 +487,15 @@ fp8bs_status gemm_impl(const void* x_bf16, const uint8_t* x_fp8, const float* x_
     return FP8BS_ERR_SHAPE;
   }
   // tile layout: plain kernels only (the SwiGLU epilogue runs after the split
-  // sum or in a second kernel), no prefill path
+  // sum or in a second kernel)
   if (c.weight_layout != FP8BS_LAYOUT_ROWS &&
-      (c.weight_layout != FP8BS_LAYOUT_TILES || c.path == FP8BS_PATH_PREFILL ||
-       (swiglu && c.epilogue != FP8BS_EPILOGUE_SEPARATE)))
+      (c.weight_layout != FP8BS_LAYOUT_TILES || (swiglu && c.epilogue != FP8BS_EPILOGUE_SEPARATE)))
     return FP8BS_ERR_CONFIG;
+  // the prefill kernel forms its per-lane weight offsets in 32 bits (up to
+  // 256 rows times k, or 16 tiles times k/128 times 2 KB): larger k is
+  // rejected before anything is launched
+  if (c.path == FP8BS_PATH_PREFILL && (int64_t)256 * k >= ((int64_t)1 << 32))
+    return FP8BS_ERR_SHAPE;
   if (c.split_k < 1 || c.split_k > 64 || c.split_k > kbn) return FP8BS_ERR_CONFIG;
   if (c.path == FP8BS_PATH_PREFILL ? c.reduce != FP8BS_REDUCE_KERNEL : m > kMaxDecodeM)
     return FP8BS_ERR_CONFIG;
@@ -727,7 +731,7 @@ fp8bs_status fp8bs_pack_weight(const uint8_t* w_fp8, int64_t n, int64_t k, uint8
 fp8bs_status fp8bs_gemm_tiles(const void* x_bf16, int64_t m, const uint8_t* w_tiles,
                               const float* w_scale, int64_t n, int64_t k, void* y_bf16,
                               void* workspace, size_t workspace_bytes, void* stream) {
-  if (m < 0 || m > kMaxDecodeM || n < 0 || k < 0 || n % BLK || k % BLK) return FP8BS_ERR_SHAPE;
+  if (m < 0 || m > kMaxM || n < 0 || k < 0 || n % BLK || k % BLK) return FP8BS_ERR_SHAPE;
   if (!x_bf16 && m > 0 && n > 0 && k > 0) return FP8BS_ERR_NULL;
   return gemm_impl(x_bf16, nullptr, nullptr, m, w_tiles, w_scale, n, k, y_bf16, workspace,
                    workspace_bytes, nullptr, stream, false, nullptr, nullptr, FP8BS_LAYOUT_TILES);
@@ -737,7 +741,7 @@ fp8bs_status fp8bs_gemm_q_tiles(const uint8_t* x_fp8, const float* x_scale, int6
                                 const uint8_t* w_tiles, const float* w_scale, int64_t n,
                                 int64_t k, void* y_bf16, void* workspace, size_t workspace_bytes,
                                 void* stream) {
-  if (m < 0 || m > kMaxDecodeM || n < 0 || k < 0 || n % BLK || k % BLK) return FP8BS_ERR_SHAPE;
+  if (m < 0 || m > kMaxM || n < 0 || k < 0 || n % BLK || k % BLK) return FP8BS_ERR_SHAPE;
   return gemm_impl(nullptr, x_fp8, x_scale, m, w_tiles, w_scale, n, k, y_bf16, workspace,
                    workspace_bytes, nullptr, stream, false, nullptr, nullptr, FP8BS_LAYOUT_TILES);
 }
@@ -777,8 +781,7 @@ fp8bs_status fp8bs_gemm_swiglu_tiles(const void* x_bf16, int64_t m, const uint8_
                                      const float* w_scale, int64_t n, int64_t k, void* y_bf16,
                                      uint8_t* h_fp8, float* h_scale, void* workspace,
                                      size_t workspace_bytes, void* stream) {
-  if (m < 0 || m > kMaxDecodeM || n < 0 || k < 0 || n % (2 * BLK) || k % BLK)
-    return FP8BS_ERR_SHAPE;
+  if (m < 0 || m > 65535 || n < 0 || k < 0 || n % (2 * BLK) || k % BLK) return FP8BS_ERR_SHAPE;
   if (!x_bf16 && m > 0 && n > 0 && k > 0) return FP8BS_ERR_NULL;
   return gemm_impl(x_bf16, nullptr, nullptr, m, w_tiles, w_scale, n, k, y_bf16, workspace,
                    workspace_bytes, nullptr, stream, true, h_fp8, h_scale, FP8BS_LAYOUT_TILES);

@@ -336,7 +336,19 @@ __device__ __forceinline__ void pf_ring_tail(int kb, int last, F& f) {
 // operands into registers (a second barrier right after those reads),
 // with the block S later, instead of when the next block starts: S blocks
 // are then in flight while one is multiplied, from the same LDS.
-template <int WN, int S, bool EARLY = false>
+// Tile-layout weights (PK): a stage's weight rows are 4 WN whole 16-row
+// tiles of 2 KB (the tile layout of the codes, see tile_layout_off); load
+// instruction q of the stage copies KB q (tile q/2, half q%2) as it is, so
+// the stage holds the tiles in operand order and lane l reads the two
+// 16-byte halves of its A operand at t*2048 + 16l and t*2048 + 1024 + 16l
+// (consecutive lanes, consecutive bytes: no bank conflicts, no swizzle).
+__device__ __forceinline__ i32x8 pf_tile_operand(const uint8_t* rows, int t, int lane) {
+  const uint4 lo = *reinterpret_cast<const uint4*>(rows + t * 2048 + 16 * lane);
+  const uint4 hi = *reinterpret_cast<const uint4*>(rows + t * 2048 + 1024 + 16 * lane);
+  return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+}
+
+template <int WN, int S, bool EARLY = false, bool PK = false>
 __global__ __launch_bounds__(128 * WN, WN == 2 ? 2 : 1) void gemm_prefill_dma_kernel(GemmParams p) {
   static_assert(S >= 2 && (S - 1) * pf_dma_per_stage(WN) <= 63, "vmcnt range");
   extern __shared__ __align__(16) uint8_t lds_all[];
@@ -360,8 +372,14 @@ __global__ __launch_bounds__(128 * WN, WN == 2 ? 2 : 1) void gemm_prefill_dma_ke
   uint32_t wo[4], xo[XI];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int r = 8 * (4 * wave + i) + (lane >> 3);
-    wo[i] = (uint32_t)r * (uint32_t)p.k + 16u * (uint32_t)((lane & 7) ^ pf_swz(r));
+    if constexpr (PK) {
+      const int q = 4 * wave + i;
+      wo[i] = (uint32_t)(q >> 1) * (uint32_t)p.kbn * 2048u + (uint32_t)(q & 1) * 1024u +
+              16u * (uint32_t)lane;
+    } else {
+      const int r = 8 * (4 * wave + i) + (lane >> 3);
+      wo[i] = (uint32_t)r * (uint32_t)p.k + 16u * (uint32_t)((lane & 7) ^ pf_swz(r));
+    }
   }
 #pragma unroll
   for (int i = 0; i < XI; ++i) {
@@ -371,14 +389,17 @@ __global__ __launch_bounds__(128 * WN, WN == 2 ? 2 : 1) void gemm_prefill_dma_ke
   }
   const int sr = 64 * (wave & 1) + lane;  // scale row of this lane
   const uint32_t so = (uint32_t)(m0 + sr < p.m ? sr : p.m - 1 - m0) * (uint32_t)p.kbn * 4u;
-  const uint8_t* wbase = p.wq + (size_t)n0 * (size_t)p.k;
+  // row-major: row n0, the block's K offset added per block; tile layout:
+  // tile n0/16 of K block 0, the block's 2 KB step added per block
+  const uint8_t* wbase = PK ? p.wq + (size_t)(n0 >> 4) * (size_t)p.kbn * 2048u
+                            : p.wq + (size_t)n0 * (size_t)p.k;
   const uint8_t* xbase = p.xq + (size_t)m0 * (size_t)p.k;
   const float* sbase = p.xs + (size_t)m0 * (size_t)p.kbn;
 
   auto issue = [&](int kb, int stage) {
     kb = kb < last ? kb : last;
     const uint32_t st = lds0 + (uint32_t)(stage * STAGE);
-    const uint8_t* wb = wbase + (size_t)kb * BLK;
+    const uint8_t* wb = wbase + (size_t)kb * (PK ? 2048u : (size_t)BLK);
     const uint8_t* xb = xbase + (size_t)kb * BLK;
 #pragma unroll
     for (int i = 0; i < 4; ++i) dma16(st + (uint32_t)(4 * wave + i) * 1024u, wb, wo[i]);
@@ -417,7 +438,10 @@ __global__ __launch_bounds__(128 * WN, WN == 2 ? 2 : 1) void gemm_prefill_dma_ke
     for (int j = 0; j < 4; ++j) {
       const int mr = 64 * wm + 16 * j + l16;
       bop[j] = pf_swz_operand(xl, mr, g);
-      aop[j] = pf_swz_operand(wl, 64 * wn + 16 * j + l16, g);
+      if constexpr (PK)
+        aop[j] = pf_tile_operand(wl, 4 * wn + j, lane);
+      else
+        aop[j] = pf_swz_operand(wl, 64 * wn + 16 * j + l16, g);
       sc[j] = sl[mr] * sw;
     }
     if constexpr (EARLY) {

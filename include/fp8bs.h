@@ -99,7 +99,9 @@ fp8bs_status fp8bs_quantize_act(const void* x_bf16, int64_t m, int64_t k,
  * Training", section "Start with the bound: memory or compute") runs the
  * tiled matrix-core kernel: the activations are first cast into the
  * workspace (m*k code bytes, padded to 256, then m*k/128 fp32 scales), with
- * the same rule as fp8bs_quantize_act.
+ * the same rule as fp8bs_quantize_act. That kernel forms 32-bit offsets
+ * within a 256-row slab of W, so m > 32 needs k < 2^24 (else
+ * FP8BS_ERR_SHAPE).
  *   x_bf16  [m][k] bf16; w_fp8 [n][k] codes; w_scale [n/128][k/128] fp32;
  *   y_bf16  [m][n] bf16, out.
  *   workspace: device scratch of at least fp8bs_gemm_workspace_bytes(m,n,k)
@@ -191,8 +193,9 @@ enum { FP8BS_LAYOUT_ROWS = 0, FP8BS_LAYOUT_TILES = 1 };
  *             [n][k], every path) or FP8BS_LAYOUT_TILES (the tile layout of
  *             fp8bs_pack_weight; MFMA, MFMA_ROWS, MFMA_STREAM and
  *             MFMA_ROWS_REG paths, for the kernel shapes the tile-layout
- *             table selects; not with DOT or PREFILL, nor with the SwiGLU
- *             epilogue inside the GEMM).                                   */
+ *             table selects, and PREFILL with the direct-load kernel of 2
+ *             stages; not with DOT, nor with the SwiGLU epilogue inside
+ *             the GEMM).                                                   */
 typedef struct {
   int32_t path;
   int32_t tiles_n;
@@ -235,17 +238,17 @@ fp8bs_status fp8bs_gemm_ex(const void* x_bf16, const uint8_t* x_fp8, const float
  * header on the same codes, and with the same kernel configuration the
  * result is bit-identical to the row-major call. Weights are rearranged
  * once, like the quantization itself. The weight scales keep their layout.
- * The tile layout serves the decode kernels: 0 <= m <= 32 (the plain GEMM
- * calls below and fp8bs_gemm_swiglu_tiles).                                 */
+ * Every m the row-major calls take is served: the decode kernels (m <= 32)
+ * and the prefill kernel (m > 32) both have tile-layout builds.             */
 
 /* Rearrange row-major codes w_fp8 [n][k] into the tile layout (n*k bytes at
  * w_tiles, which must not overlap w_fp8). Both pointers 16-byte aligned.   */
 fp8bs_status fp8bs_pack_weight(const uint8_t* w_fp8, int64_t n, int64_t k, uint8_t* w_tiles,
                                void* stream);
 
-/* fp8bs_gemm on tile-layout weights (activation cast fused), 0 <= m <= 32;
- * m > 32 is FP8BS_ERR_SHAPE. Workspace as for fp8bs_gemm
- * (fp8bs_gemm_workspace_bytes covers both layouts).                         */
+/* fp8bs_gemm on tile-layout weights (activation cast fused), 0 <= m <= 2^20.
+ * Workspace as for fp8bs_gemm (fp8bs_gemm_workspace_bytes covers both
+ * layouts).                                                                 */
 fp8bs_status fp8bs_gemm_tiles(const void* x_bf16, int64_t m, const uint8_t* w_tiles,
                               const float* w_scale, int64_t n, int64_t k, void* y_bf16,
                               void* workspace, size_t workspace_bytes, void* stream);
@@ -305,7 +308,7 @@ fp8bs_status fp8bs_gemm_swiglu(const void* x_bf16, int64_t m, const uint8_t* w_f
                                uint8_t* h_fp8, float* h_scale, void* workspace,
                                size_t workspace_bytes, void* stream);
 
-/* fp8bs_gemm_swiglu on tile-layout weights (fp8bs_pack_weight), 0 <= m <= 32:
+/* fp8bs_gemm_swiglu on tile-layout weights (fp8bs_pack_weight), 0 <= m <= 65535:
  * y bit-identical to fp8bs_gemm_tiles on the same inputs, h as
  * fp8bs_swiglu_quant(y). The epilogue runs after the split sum or in a
  * second kernel (FP8BS_EPILOGUE_SEPARATE); workspace as for

@@ -222,7 +222,7 @@ def test_swiglu_config_rules(lib):
 
 def test_tile_layout_argument_errors(lib):
     """Weight rearrangement and the tile-layout GEMM calls check their
-    arguments before any launch; the tile layout serves m <= 32 only."""
+    arguments before any launch."""
     assert lib.fp8bs_pack_weight(P, 100, 128, P, None) == E_SHAPE
     assert lib.fp8bs_pack_weight(P, 128, 130, P, None) == E_SHAPE
     assert lib.fp8bs_pack_weight(None, 128, 128, P, None) == E_NULL
@@ -231,11 +231,12 @@ def test_tile_layout_argument_errors(lib):
     assert lib.fp8bs_pack_weight(P, 128, 128, P + 4, None) == E_ALIGN
     assert lib.fp8bs_pack_weight(None, 0, 128, None, None) == OK
     g = lib.fp8bs_gemm_tiles
-    assert g(P, 33, P, P, 512, 1024, P, P, 1 << 20, None) == E_SHAPE
+    assert g(P, (1 << 20) + 1, P, P, 512, 1024, P, P, 1 << 20, None) == E_SHAPE
+    assert g(P, 33, P, P, 512, 1024, P, None, 0, None) == E_WS  # prefill casts X into it
     assert g(P, 8, P, P, 500, 1024, P, P, 1 << 20, None) == E_SHAPE
     assert g(None, 8, P, P, 512, 1024, P, P, 1 << 20, None) == E_NULL
     assert g(P, 8, P + 8, P, 512, 1024, P, P, 1 << 20, None) == E_ALIGN
-    assert lib.fp8bs_gemm_q_tiles(P, P, 33, P, P, 512, 1024, P, P, 1 << 20, None) == E_SHAPE
+    assert lib.fp8bs_gemm_q_tiles(P, P, -1, P, P, 512, 1024, P, P, 1 << 20, None) == E_SHAPE
     assert lib.fp8bs_gemm_q_tiles(P, None, 8, P, P, 512, 1024, P, P, 1 << 20, None) == E_NULL
     import torch
     if not torch.cuda.is_available():
@@ -261,13 +262,14 @@ def test_tile_layout_config_rules(lib):
             if t.path == fp8bs.PATH_MFMA:
                 assert n % (16 * t.tiles_n * t.waves_n) == 0
             assert fp8bs.workspace_bytes(m, n, k) >= fp8bs.config_workspace_bytes(t, m, n, k)
-    with pytest.raises(fp8bs.Fp8bsError):
-        fp8bs.tiles_select_config(33, 5120, 5120)
+    t = fp8bs.tiles_select_config(64, 5120, 5120)
+    assert t.path == fp8bs.PATH_PREFILL and t.weight_layout == fp8bs.LAYOUT_TILES
+    assert t == fp8bs.tiles_select_config(64, 5120, 5120)
     c = GemmConfig(1, 1, 1, 4, 5, epilogue=1, weight_layout=fp8bs.LAYOUT_TILES)._c()
     r = lib.fp8bs_gemm_swiglu_ex(P, None, None, 8, P, P, 1024, 1024, P, P, P, P, 1 << 20,
                                  ctypes.byref(c), None)
     assert r == E_CFG  # the epilogue inside the GEMM has no tile-layout build
-    assert lib.fp8bs_gemm_swiglu_tiles(P, 33, P, P, 1024, 1024, P, P, P, P, 1 << 20, None) == E_SHAPE
+    assert lib.fp8bs_gemm_swiglu_tiles(P, 65536, P, P, 1024, 1024, P, P, P, P, 1 << 20, None) == E_SHAPE
     assert lib.fp8bs_gemm_swiglu_tiles(P, 8, P, P, 1152, 1024, P, P, P, P, 1 << 20, None) == E_SHAPE
     assert lib.fp8bs_gemm_swiglu_tiles(None, 8, P, P, 1024, 1024, P, P, P, P, 1 << 20, None) == E_NULL
     import torch
@@ -277,9 +279,15 @@ def test_tile_layout_config_rules(lib):
                                      ctypes.byref(c), None)
         assert r == E_DEV
         assert lib.fp8bs_gemm_swiglu_tiles(P, 8, P, P, 1024, 1024, P, P, P, P, 1 << 20, None) == E_DEV
-    c = GemmConfig(5, 1, 2, 2, 2, weight_layout=fp8bs.LAYOUT_TILES)._c()
+    c = GemmConfig(5, 2, 2, 2, 2, weight_layout=fp8bs.LAYOUT_TILES)._c()  # no early-refill tile build
     r = lib.fp8bs_gemm_ex(P, None, None, 64, P, P, 512, 1024, P, P, 1 << 24, ctypes.byref(c), None)
     assert r == E_CFG
+    # the prefill kernel's 32-bit offsets: k >= 2^24 is a shape error, in either layout
+    for layout in (fp8bs.LAYOUT_ROWS, fp8bs.LAYOUT_TILES):
+        c = GemmConfig(5, 1, 2, 2, 2, weight_layout=layout)._c()
+        r = lib.fp8bs_gemm_ex(P, None, None, 64, P, P, 512, 1 << 24, P, P, 1 << 40,
+                              ctypes.byref(c), None)
+        assert r == E_SHAPE
     c = GemmConfig(1, 1, 1, 4, 5, weight_layout=2)._c()
     r = lib.fp8bs_gemm_ex(P, None, None, 8, P, P, 512, 1024, P, None, 0, ctypes.byref(c), None)
     assert r == E_CFG

@@ -1,10 +1,11 @@
 """GPU tests of the tile layout of the weight codes (fp8bs_pack_weight and
 the *_tiles GEMM calls): the rearrangement is the permutation the header
 describes, checked against a numpy reshape written from that description;
-every tile-layout kernel gives the same bits as the row-major kernel of the
-same configuration and stays within 2^-7 |ref| + 1e-3 rms(ref) of the CPU
-oracle; full-size shapes in the automatic configuration; ragged row ranges
-(workgroup ranges that do not start on a 16-row tile); determinism."""
+every tile-layout kernel (decode and prefill sizes) gives the same bits as
+the row-major kernel of the same configuration and stays within
+2^-7 |ref| + 1e-3 rms(ref) of the CPU oracle; full-size shapes in the
+automatic configuration; ragged row ranges (workgroup ranges that do not
+start on a 16-row tile); the SwiGLU call; graph replays; determinism."""
 import numpy as np
 import pytest
 
@@ -215,10 +216,40 @@ def test_tiles_deterministic(fp8bs, full):
         assert _bits_equal(y, y0)
 
 
-def test_tiles_rejects_prefill_sizes(fp8bs, ragged):
-    with pytest.raises(fp8bs.Fp8bsError):
-        x = torch.zeros((33, ragged.x.shape[1]), dtype=torch.bfloat16, device="cuda")
-        fp8bs.gemm_tiles(x, ragged.wt, ragged.ws)
+@pytest.mark.parametrize("m,n,k,wn,split", [(300, 512, 1280, 2, 1), (129, 768, 2048, 2, 3),
+                                             (64, 256, 384, 2, 1), (1000, 1280, 13 * 128, 2, 1),
+                                             (200, 1024, 1024, 4, 1), (33, 512, 128, 2, 1)])
+def test_prefill_tiles_matches_row_major_and_oracle(fp8bs, m, n, k, wn, split):
+    """The prefill-size kernel (m > 32) on tile-layout weights: the same bits
+    as on row-major weights in the same configuration, within the tolerance
+    of the oracle; ragged m tails, split K, one K block, both tile widths."""
+    from fp8_block_scaled_fp8bs_amd import GemmConfig
+    pr = _random_problem(fp8bs, m, n, k, 5000 + m + n + k)
+    rows_cfg = GemmConfig(fp8bs.PATH_PREFILL, 1, wn, 2, 2, split)
+    tile_cfg = GemmConfig(fp8bs.PATH_PREFILL, 1, wn, 2, 2, split, weight_layout=fp8bs.LAYOUT_TILES)
+    announce("prefill tiles", tile_cfg, m, n, k)
+    y_rows = fp8bs.gemm_ex(rows_cfg, pr.wq, pr.ws, x=pr.x)
+    y_tiles = fp8bs.gemm_ex(tile_cfg, pr.wt, pr.ws, x=pr.x)
+    torch.cuda.synchronize()
+    assert _bits_equal(y_rows, y_tiles)
+    ref = oracle.gemm_ref(pr.xq_ref, pr.xs_ref, pr.wq_ref, pr.ws_ref)
+    _assert_close(host_bits(y_tiles), ref, f"prefill tiles {tile_cfg} m={m}")
+
+
+def test_prefill_tiles_auto(fp8bs, full):
+    """gemm_tiles at prefill sizes picks the tile-layout prefill kernel and
+    gives the bits of the row-major call (same configuration)."""
+    pr = full["square"]
+    n, k = pr.wq.shape
+    rng = np.random.default_rng(77)
+    x = dev_bf16(bf16_from_f32(rng.standard_normal((256, k)).astype(np.float32)))
+    cfg = fp8bs.tiles_select_config(256, n, k)
+    announce("prefill tiles auto", cfg)
+    assert cfg.path == fp8bs.PATH_PREFILL and cfg.weight_layout == fp8bs.LAYOUT_TILES
+    y_t = fp8bs.gemm_tiles(x, pr.wt, pr.ws)
+    y_r = fp8bs.gemm(x, pr.wq, pr.ws)
+    torch.cuda.synchronize()
+    assert _bits_equal(y_t, y_r)
 
 
 def test_tiles_graph_replays_match_eager(fp8bs, full):
