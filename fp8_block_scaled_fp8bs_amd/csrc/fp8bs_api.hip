@@ -366,7 +366,7 @@ bool select_config(int64_t m, int64_t n, int64_t k, fp8bs_gemm_config* out, bool
       // wide N
       {{{{MF, 1, 1, 4, 5, 1, RK}, {MF, 1, 1, 8, 5, 1, RK}}, 2},
        {{{MF, 1, 1, 8, 5, 1, RK}, {MF, 1, 1, 4, 5, 1, RK}}, 2},
-       {{{MF, 1, 1, 8, 5, 1, RK}, {RW, 1, 1, 8, 3, 1, RK}}, 2},
+       {{{RW, 1, 1, 8, 3, 1, RK}, {MF, 1, 1, 8, 5, 1, RK}}, 2},
        {{{RW, 1, 1, 8, 3, 1, RK}, {RW, 2, 1, 8, 6, 1, RK}}, 2},
        {{{RW, 1, 1, 8, 3, 1, RK}, {RW, 2, 1, 8, 6, 1, RK}}, 2},
        {{{RW, 2, 1, 8, 6, 1, RK}, {RR, 1, 1, 8, 5, 1, RK}, {MF, 1, 8, 1, 5, 4, RK}}, 3}},
