@@ -329,6 +329,101 @@ def mlp_swiglu(args, fp8bs, dev) -> int:
     return 0
 
 
+def mlp_pair(args, fp8bs, dev) -> int:
+    """The wide-then-narrow MLP pair as one chain, at every M of the step
+    mix: the up/gate projection 5120 -> 34816 with the SwiGLU epilogue and
+    the FP8 cast of h (one gemm_swiglu call), then the down projection
+    17408 -> 5120 on those codes (gemm_q), captured in one graph per M over
+    rotating weight pools of at least --pool-gib GiB each. Timed on
+    tile-layout and on row-major weights. Algorithmic bytes of the pair:
+    both weights (codes and scales), bf16 X, the bf16 up/gate output y, h
+    (codes and scales) written once and read once, and the bf16 output."""
+    import dataclasses
+
+    import torch
+
+    from workloads import WORKLOADS
+
+    up, down = WORKLOADS["mlp_up"], WORKLOADS["mlp_down"]
+    assert down.k == up.n // 2 and down.n == up.k
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1600)
+
+    def make_pool(n, k):
+        count = max(1, math.ceil(args.pool_gib * (1 << 30) / (n * k)))
+        pool = []
+        for _ in range(count):
+            w = (torch.randn((n, k), generator=gen, device=dev, dtype=torch.float32) * 0.02).to(torch.bfloat16)
+            wq, wsc = fp8bs.quantize_weight(w)
+            del w
+            pool.append((wq, fp8bs.pack_weight(wq), wsc))
+        return pool
+
+    pu, pd = make_pool(up.n, up.k), make_pool(down.n, down.k)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    inter = up.n // 2
+    for m in [int(v) for v in args.step_m.split(",")]:
+        x = torch.randn((m, up.k), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        y = torch.empty((m, up.n), dtype=torch.bfloat16, device=dev)
+        hq = torch.empty((m, inter), dtype=torch.uint8, device=dev)
+        hs = torch.empty((m, inter // 128), dtype=torch.float32, device=dev)
+        out = torch.empty((m, down.n), dtype=torch.bfloat16, device=dev)
+        wsb = max(fp8bs.workspace_bytes(m, up.n, up.k), fp8bs.workspace_bytes(m, down.n, down.k),
+                  fp8bs.swiglu_workspace_bytes(m, up.n, up.k))
+        work = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+        res = {}
+        for layout in ("tiles", "rows"):
+            def pair(i):
+                wu, wd = pu[i % len(pu)], pd[i % len(pd)]
+                if layout == "tiles":
+                    fp8bs.gemm_swiglu_tiles(x, wu[1], wu[2], out=y, h=(hq, hs), workspace=work)
+                    fp8bs.gemm_q_tiles(hq, hs, wd[1], wd[2], out=out, workspace=work)
+                else:
+                    fp8bs.gemm_swiglu(x, wu[0], wu[2], out=y, h=(hq, hs), workspace=work)
+                    fp8bs.gemm_q(hq, hs, wd[0], wd[2], out=out, workspace=work)
+            for i in range(3):
+                pair(i)
+            torch.cuda.synchronize()
+            steps = max(10, min(100, args.steps // 4))
+            g = torch.cuda.CUDAGraph()
+            cap = torch.cuda.Stream()
+            cap.wait_stream(stream)
+            with torch.cuda.stream(cap):
+                with torch.cuda.graph(g, stream=cap):
+                    for i in range(steps):
+                        pair(i)
+            stream.wait_stream(cap)
+            g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            best = float("inf")
+            for _ in range(3):
+                e0.record(stream)
+                g.replay()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                best = min(best, e0.elapsed_time(e1) * 1e3 / steps)
+            res[layout] = best
+            del g
+        hbytes = m * inter + 4 * m * (inter // 128)
+        nbytes = (up.n * up.k + 4 * (up.n // 128) * (up.k // 128) + 2 * m * up.k + 2 * m * up.n
+                  + 2 * hbytes + down.n * down.k + 4 * (down.n // 128) * (down.k // 128)
+                  + 2 * m * down.n)
+        print(json.dumps({
+            "mode": "mlp_pair", "m": m, "up": [up.n, up.k], "down": [down.n, down.k],
+            "us_per_pair": round(res["tiles"], 3), "GBps": round(nbytes / (res["tiles"] * 1e3), 1),
+            "pct_of_8TBps": round(100 * nbytes / (res["tiles"] * 1e3) / HBM_PEAK_GBPS, 2),
+            "algorithmic_bytes": nbytes, "weight_layout": "tiles",
+            "us_per_pair_row_major": round(res["rows"], 3),
+            "config_up": dataclasses.asdict(fp8bs.tiles_select_config(m, up.n, up.k)),
+            "config_down": dataclasses.asdict(fp8bs.tiles_select_config(m, down.n, down.k)),
+            "timing": "captured graph of the two calls per step over rotating weight pools, best of 3 replays"}),
+            flush=True)
+        del x, y, hq, hs, out, work
+    return 0
+
+
 MFMA_FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 matrix peak
 
 
@@ -440,6 +535,9 @@ def main() -> int:
     ap.add_argument("--weight-layout", default="tiles", choices=("tiles", "rows"),
                     help="weight codes for the GEMM and step-mix modes: the tile layout "
                          "(fp8bs_pack_weight, rearranged once before timing) or row-major")
+    ap.add_argument("--mlp-pair", action="store_true",
+                    help="the MLP pair as one chain: up/gate + SwiGLU + FP8 cast, then the down "
+                         "projection on those codes, at every M; one JSON line per M")
     ap.add_argument("--mlp-swiglu", action="store_true",
                     help="MLP up/gate projection with the SwiGLU epilogue at every M; "
                          "prints one JSON line per M")
@@ -467,6 +565,8 @@ def main() -> int:
         return step_mix(args, fp8bs, dev)
     if args.mlp_swiglu:
         return mlp_swiglu(args, fp8bs, dev)
+    if args.mlp_pair:
+        return mlp_pair(args, fp8bs, dev)
     if args.prefill:
         return prefill(args, fp8bs, dev)
 
