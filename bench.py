@@ -597,7 +597,7 @@ def main() -> int:
     x = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
     code_bytes = n * k
     pool_n = max(1, math.ceil(args.pool_gib * (1 << 30) / code_bytes))
-    tiles = args.weight_layout == "tiles" and m <= 32  # the tile layout serves decode sizes
+    tiles = args.weight_layout == "tiles"
     layout = "tiles" if tiles else "rows"
 
     def prepared(w):
