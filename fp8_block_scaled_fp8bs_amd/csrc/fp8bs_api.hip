@@ -715,6 +715,8 @@ fp8bs_status fp8bs_pack_weight(const uint8_t* w_fp8, int64_t n, int64_t k, uint8
   if (n < 0 || k < 0 || n % BLK || k % BLK) return FP8BS_ERR_SHAPE;
   if (n / BLK > (int64_t)1 << 24 || k / BLK > (int64_t)1 << 20) return FP8BS_ERR_SHAPE;
   if (n == 0 || k == 0) return FP8BS_OK;
+  // one thread per 16 bytes, 256 per workgroup: the grid must fit in 2^31 - 1
+  if ((n / 16) * (k / 256) > (int64_t)0x7FFFFFFF) return FP8BS_ERR_SHAPE;
   if (!w_fp8 || !w_tiles) return FP8BS_ERR_NULL;
   if (!aligned(w_fp8, 16) || !aligned(w_tiles, 16)) return FP8BS_ERR_ALIGN;
   const fp8bs_status st = current_device(nullptr);

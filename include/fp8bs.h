@@ -242,7 +242,8 @@ fp8bs_status fp8bs_gemm_ex(const void* x_bf16, const uint8_t* x_fp8, const float
  * and the prefill kernel (m > 32) both have tile-layout builds.             */
 
 /* Rearrange row-major codes w_fp8 [n][k] into the tile layout (n*k bytes at
- * w_tiles, which must not overlap w_fp8). Both pointers 16-byte aligned.   */
+ * w_tiles, which must not overlap w_fp8). Both pointers 16-byte aligned;
+ * n*k up to 2^43 bytes (else FP8BS_ERR_SHAPE).                              */
 fp8bs_status fp8bs_pack_weight(const uint8_t* w_fp8, int64_t n, int64_t k, uint8_t* w_tiles,
                                void* stream);
 

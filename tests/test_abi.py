@@ -230,6 +230,7 @@ def test_tile_layout_argument_errors(lib):
     assert lib.fp8bs_pack_weight(P + 8, 128, 128, P, None) == E_ALIGN
     assert lib.fp8bs_pack_weight(P, 128, 128, P + 4, None) == E_ALIGN
     assert lib.fp8bs_pack_weight(None, 0, 128, None, None) == OK
+    assert lib.fp8bs_pack_weight(P, 1 << 22, 1 << 21, P, None) == E_SHAPE  # grid past 2^31 - 1
     g = lib.fp8bs_gemm_tiles
     assert g(P, (1 << 20) + 1, P, P, 512, 1024, P, P, 1 << 20, None) == E_SHAPE
     assert g(P, 33, P, P, 512, 1024, P, None, 0, None) == E_WS  # prefill casts X into it
