@@ -31,6 +31,7 @@ struct DeviceInfo {
   bool ok = false;
   int max_lds = 0;
   int num_cu = 0;
+  int index = 0;
 };
 DeviceInfo g_dev[kMaxDevices];
 std::mutex g_dev_mu;
@@ -51,6 +52,7 @@ fp8bs_status current_device(DeviceInfo* out) {
       return FP8BS_ERR_DEVICE;
     }
     d.ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    d.index = dev;
     int v = 0;
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess)
       d.max_lds = v;
@@ -66,6 +68,25 @@ fp8bs_status current_device(DeviceInfo* out) {
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// Kernels that take more than 64 KB of dynamic LDS need the per-function
+// limit raised once per device (to the device maximum); a bit per device
+// records that it was done, so a launch pays for it only the first time.
+constexpr int kMaxKernels = 4096;
+std::atomic<uint64_t> g_lds_raised[kMaxKernels];
+
+fp8bs_status raise_lds_limit(const void* fn, int slot, const DeviceInfo& dev) {
+  if (slot < 0 || slot >= kMaxKernels) return FP8BS_ERR_LAUNCH;
+  const uint64_t bit = uint64_t(1) << dev.index;
+  if (g_lds_raised[slot].load(std::memory_order_acquire) & bit) return FP8BS_OK;
+  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, dev.max_lds) !=
+      hipSuccess) {
+    (void)hipGetLastError();
+    return FP8BS_ERR_LAUNCH;
+  }
+  g_lds_raised[slot].fetch_or(bit, std::memory_order_acq_rel);
+  return FP8BS_OK;
+}
 
 fp8bs_status launch(const void* fn, dim3 grid, dim3 block, size_t lds, void* stream, void** args) {
   const hipError_t e = hipLaunchKernel(fn, grid, block, args, lds, as_stream(stream));
@@ -91,6 +112,12 @@ namespace {
 
 constexpr int64_t kMaxDecodeM = 32;       // activation rows of the decode kernels (paths 1-4, 6)
 constexpr int64_t kMaxM = (int64_t)1 << 20;  // activation rows of the prefill path
+// Compute units the configuration table, the row-range split and the
+// stream-K partition assume (a full MI355X). Launch geometry never depends on
+// the device's own count, so a shape runs the same kernel with the same
+// work split, and gives the same bits, on a partitioned device too (more
+// rounds of workgroups there).
+constexpr int kTableCUs = 256;
 
 // Row-range paths: one workgroup per compute unit, n split over them.
 inline bool is_row_range(int path) {
@@ -227,7 +254,6 @@ constexpr int DT = FP8BS_PATH_DOT;
 constexpr int RW = FP8BS_PATH_MFMA_ROWS;
 constexpr int ST = FP8BS_PATH_MFMA_STREAM;
 constexpr int RR = FP8BS_PATH_MFMA_ROWS_REG;
-constexpr int kTableCUs = 256;  // the configuration table assumes a full MI355X
 
 // Configurations the SwiGLU call accepts. With the separate epilogue:
 // everything but the last-arriver reduce (the split sum carries the
@@ -435,26 +461,39 @@ fp8bs_status launch_swiglu_quant(const void* y_bf16, int64_t m, int64_t inter, u
 }
 
 
+// Shape limits of every GEMM entry point: n and k whole blocks; n below
+// 2^31 (the kernels index columns in 32 bits), k/128 at most 2^20; m up to
+// 2^20 (the SwiGLU call: 65535, one epilogue wave row per activation row);
+// the prefill kernel (m > 32) forms 32-bit offsets within a 256-row slab of
+// W, so there k < 2^24.
+bool gemm_shape_ok(int64_t m, int64_t n, int64_t k, bool swiglu) {
+  if (m < 0 || m > kMaxM || n < 0 || k < 0 || n % BLK || k % BLK) return false;
+  if (n / BLK >= (int64_t)1 << 24 || k / BLK > (int64_t)1 << 20) return false;
+  if (swiglu && (n % (2 * BLK) || m > 65535)) return false;
+  if (m > kMaxDecodeM && (int64_t)256 * k >= ((int64_t)1 << 32)) return false;
+  return true;
+}
+
 // The GEMM, optionally with the SwiGLU epilogue (swiglu: h_fp8 and h_scale
-// receive the re-quantized SwiGLU output).
-fp8bs_status gemm_impl(const void* x_bf16, const uint8_t* x_fp8, const float* x_scale, int64_t m,
-                       const uint8_t* w_fp8, const float* w_scale, int64_t n, int64_t k,
-                       void* y_bf16, void* workspace, size_t workspace_bytes,
-                       const fp8bs_gemm_config* cfg_in, void* stream, bool swiglu = false,
-                       uint8_t* h_fp8 = nullptr, float* h_scale = nullptr,
+// receive the re-quantized SwiGLU output). fused: the activations are bf16
+// x_bf16 (cast in the kernel), else codes x_fp8 and scales x_scale.
+// Checks run in the documented order -- shape, NULL pointers, alignment,
+// configuration, workspace, device -- and all of them before any launch.
+fp8bs_status gemm_impl(bool fused, const void* x_bf16, const uint8_t* x_fp8,
+                       const float* x_scale, int64_t m, const uint8_t* w_fp8,
+                       const float* w_scale, int64_t n, int64_t k, void* y_bf16, void* workspace,
+                       size_t workspace_bytes, const fp8bs_gemm_config* cfg_in, void* stream,
+                       bool swiglu = false, uint8_t* h_fp8 = nullptr, float* h_scale = nullptr,
                        int layout = FP8BS_LAYOUT_ROWS) {
-  // shapes
-  if (m < 0 || m > kMaxM || n < 0 || k < 0 || n % BLK || k % BLK) return FP8BS_ERR_SHAPE;
-  if (n / BLK > (int64_t)1 << 24 || k / BLK > (int64_t)1 << 20) return FP8BS_ERR_SHAPE;
-  if (swiglu && (n % (2 * BLK) || m > 65535)) return FP8BS_ERR_SHAPE;  // one epilogue wave row per m
+  // shapes (an empty output is a no-op whatever the pointers)
+  if (!gemm_shape_ok(m, n, k, swiglu)) return FP8BS_ERR_SHAPE;
   if (m == 0 || n == 0) return FP8BS_OK;
-  const bool fused = x_bf16 != nullptr;
   // pointers
   if (!y_bf16) return FP8BS_ERR_NULL;
   if (swiglu && (!h_fp8 || !h_scale)) return FP8BS_ERR_NULL;
   if (k > 0) {
     if (!w_fp8 || !w_scale) return FP8BS_ERR_NULL;
-    if (!fused && (!x_fp8 || !x_scale)) return FP8BS_ERR_NULL;
+    if (fused ? !x_bf16 : (!x_fp8 || !x_scale)) return FP8BS_ERR_NULL;
   }
   // alignment
   if (!aligned(y_bf16, 16)) return FP8BS_ERR_ALIGN;
@@ -492,10 +531,10 @@ fp8bs_status gemm_impl(const void* x_bf16, const uint8_t* x_fp8, const float* x_
       (c.weight_layout != FP8BS_LAYOUT_TILES || (swiglu && c.epilogue != FP8BS_EPILOGUE_SEPARATE)))
     return FP8BS_ERR_CONFIG;
   // the prefill kernel forms its per-lane weight offsets in 32 bits (up to
-  // 256 rows times k, or 16 tiles times k/128 times 2 KB): larger k is
-  // rejected before anything is launched
+  // 256 rows times k, or 16 tiles times k/128 times 2 KB): an explicit
+  // prefill configuration needs the prefill shape limit too
   if (c.path == FP8BS_PATH_PREFILL && (int64_t)256 * k >= ((int64_t)1 << 32))
-    return FP8BS_ERR_SHAPE;
+    return FP8BS_ERR_CONFIG;
   if (c.split_k < 1 || c.split_k > 64 || c.split_k > kbn) return FP8BS_ERR_CONFIG;
   if (c.path == FP8BS_PATH_PREFILL ? c.reduce != FP8BS_REDUCE_KERNEL : m > kMaxDecodeM)
     return FP8BS_ERR_CONFIG;
@@ -528,14 +567,12 @@ fp8bs_status gemm_impl(const void* x_bf16, const uint8_t* x_fp8, const float* x_
   DeviceInfo dev;
   const fp8bs_status st = current_device(&dev);
   if (st != FP8BS_OK) return st;
-  const size_t lds = config_lds_bytes(c, (int)m, n, kbn, dev.num_cu, in_gemm);
+  const size_t lds = config_lds_bytes(c, (int)m, n, kbn, kTableCUs, in_gemm);
   if (lds > (size_t)dev.max_lds) return FP8BS_ERR_CONFIG;
   if (lds > 64 * 1024) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(ke->fn),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess) {
-      (void)hipGetLastError();
-      return FP8BS_ERR_LAUNCH;
-    }
+    const fp8bs_status ls = raise_lds_limit(reinterpret_cast<const void*>(ke->fn),
+                                            (int)(ke - kernel_registry().data()), dev);
+    if (ls != FP8BS_OK) return ls;
   }
 
   GemmParams p;
@@ -563,7 +600,7 @@ fp8bs_status gemm_impl(const void* x_bf16, const uint8_t* x_fp8, const float* x_
   void* args[] = {&p};
   dim3 grid((unsigned)(n / rows), (unsigned)c.split_k);
   if (is_row_range(c.path)) {
-    p.rows_per_wg = rows_per_workgroup(n, dev.num_cu, c.weight_layout);
+    p.rows_per_wg = rows_per_workgroup(n, kTableCUs, c.weight_layout);
     grid = dim3((unsigned)((n + p.rows_per_wg - 1) / p.rows_per_wg), (unsigned)c.split_k);
   }
   // the SwiGLU epilogue arrives on each (side, 128-column block) pair of a
@@ -660,19 +697,14 @@ fp8bs_status fp8bs_quantize_act(const void* x_bf16, int64_t m, int64_t k, uint8_
 fp8bs_status fp8bs_gemm(const void* x_bf16, int64_t m, const uint8_t* w_fp8, const float* w_scale,
                         int64_t n, int64_t k, void* y_bf16, void* workspace,
                         size_t workspace_bytes, void* stream) {
-  if (!x_bf16 && m > 0 && n > 0 && k > 0) {
-    // the shape checks come first; a NULL activation pointer is a NULL error
-    if (m > kMaxM || n % BLK || k % BLK) return FP8BS_ERR_SHAPE;
-    return FP8BS_ERR_NULL;
-  }
-  return gemm_impl(x_bf16, nullptr, nullptr, m, w_fp8, w_scale, n, k, y_bf16, workspace,
+  return gemm_impl(true, x_bf16, nullptr, nullptr, m, w_fp8, w_scale, n, k, y_bf16, workspace,
                    workspace_bytes, nullptr, stream);
 }
 
 fp8bs_status fp8bs_gemm_q(const uint8_t* x_fp8, const float* x_scale, int64_t m,
                           const uint8_t* w_fp8, const float* w_scale, int64_t n, int64_t k,
                           void* y_bf16, void* workspace, size_t workspace_bytes, void* stream) {
-  return gemm_impl(nullptr, x_fp8, x_scale, m, w_fp8, w_scale, n, k, y_bf16, workspace,
+  return gemm_impl(false, nullptr, x_fp8, x_scale, m, w_fp8, w_scale, n, k, y_bf16, workspace,
                    workspace_bytes, nullptr, stream);
 }
 
@@ -705,15 +737,16 @@ fp8bs_status fp8bs_gemm_ex(const void* x_bf16, const uint8_t* x_fp8, const float
                            int64_t m, const uint8_t* w_fp8, const float* w_scale, int64_t n,
                            int64_t k, void* y_bf16, void* workspace, size_t workspace_bytes,
                            const fp8bs_gemm_config* cfg, void* stream) {
+  if (!gemm_shape_ok(m, n, k, false)) return FP8BS_ERR_SHAPE;
   if (!cfg) return FP8BS_ERR_NULL;
-  return gemm_impl(x_bf16, x_fp8, x_scale, m, w_fp8, w_scale, n, k, y_bf16, workspace,
-                   workspace_bytes, cfg, stream);
+  return gemm_impl(x_bf16 != nullptr, x_bf16, x_fp8, x_scale, m, w_fp8, w_scale, n, k, y_bf16,
+                   workspace, workspace_bytes, cfg, stream);
 }
 
 fp8bs_status fp8bs_pack_weight(const uint8_t* w_fp8, int64_t n, int64_t k, uint8_t* w_tiles,
                                void* stream) {
   if (n < 0 || k < 0 || n % BLK || k % BLK) return FP8BS_ERR_SHAPE;
-  if (n / BLK > (int64_t)1 << 24 || k / BLK > (int64_t)1 << 20) return FP8BS_ERR_SHAPE;
+  if (n / BLK >= (int64_t)1 << 24 || k / BLK > (int64_t)1 << 20) return FP8BS_ERR_SHAPE;
   if (n == 0 || k == 0) return FP8BS_OK;
   // one thread per 16 bytes, 256 per workgroup: the grid must fit in 2^31 - 1
   if ((n / 16) * (k / 256) > (int64_t)0x7FFFFFFF) return FP8BS_ERR_SHAPE;
@@ -733,9 +766,7 @@ fp8bs_status fp8bs_pack_weight(const uint8_t* w_fp8, int64_t n, int64_t k, uint8
 fp8bs_status fp8bs_gemm_tiles(const void* x_bf16, int64_t m, const uint8_t* w_tiles,
                               const float* w_scale, int64_t n, int64_t k, void* y_bf16,
                               void* workspace, size_t workspace_bytes, void* stream) {
-  if (m < 0 || m > kMaxM || n < 0 || k < 0 || n % BLK || k % BLK) return FP8BS_ERR_SHAPE;
-  if (!x_bf16 && m > 0 && n > 0 && k > 0) return FP8BS_ERR_NULL;
-  return gemm_impl(x_bf16, nullptr, nullptr, m, w_tiles, w_scale, n, k, y_bf16, workspace,
+  return gemm_impl(true, x_bf16, nullptr, nullptr, m, w_tiles, w_scale, n, k, y_bf16, workspace,
                    workspace_bytes, nullptr, stream, false, nullptr, nullptr, FP8BS_LAYOUT_TILES);
 }
 
@@ -743,8 +774,7 @@ fp8bs_status fp8bs_gemm_q_tiles(const uint8_t* x_fp8, const float* x_scale, int6
                                 const uint8_t* w_tiles, const float* w_scale, int64_t n,
                                 int64_t k, void* y_bf16, void* workspace, size_t workspace_bytes,
                                 void* stream) {
-  if (m < 0 || m > kMaxM || n < 0 || k < 0 || n % BLK || k % BLK) return FP8BS_ERR_SHAPE;
-  return gemm_impl(nullptr, x_fp8, x_scale, m, w_tiles, w_scale, n, k, y_bf16, workspace,
+  return gemm_impl(false, nullptr, x_fp8, x_scale, m, w_tiles, w_scale, n, k, y_bf16, workspace,
                    workspace_bytes, nullptr, stream, false, nullptr, nullptr, FP8BS_LAYOUT_TILES);
 }
 
@@ -771,11 +801,7 @@ fp8bs_status fp8bs_gemm_swiglu(const void* x_bf16, int64_t m, const uint8_t* w_f
                                const float* w_scale, int64_t n, int64_t k, void* y_bf16,
                                uint8_t* h_fp8, float* h_scale, void* workspace,
                                size_t workspace_bytes, void* stream) {
-  if (!x_bf16 && m > 0 && n > 0 && k > 0) {
-    if (m > kMaxM || n % (2 * BLK) || k % BLK) return FP8BS_ERR_SHAPE;
-    return FP8BS_ERR_NULL;
-  }
-  return gemm_impl(x_bf16, nullptr, nullptr, m, w_fp8, w_scale, n, k, y_bf16, workspace,
+  return gemm_impl(true, x_bf16, nullptr, nullptr, m, w_fp8, w_scale, n, k, y_bf16, workspace,
                    workspace_bytes, nullptr, stream, true, h_fp8, h_scale);
 }
 
@@ -783,9 +809,7 @@ fp8bs_status fp8bs_gemm_swiglu_tiles(const void* x_bf16, int64_t m, const uint8_
                                      const float* w_scale, int64_t n, int64_t k, void* y_bf16,
                                      uint8_t* h_fp8, float* h_scale, void* workspace,
                                      size_t workspace_bytes, void* stream) {
-  if (m < 0 || m > 65535 || n < 0 || k < 0 || n % (2 * BLK) || k % BLK) return FP8BS_ERR_SHAPE;
-  if (!x_bf16 && m > 0 && n > 0 && k > 0) return FP8BS_ERR_NULL;
-  return gemm_impl(x_bf16, nullptr, nullptr, m, w_tiles, w_scale, n, k, y_bf16, workspace,
+  return gemm_impl(true, x_bf16, nullptr, nullptr, m, w_tiles, w_scale, n, k, y_bf16, workspace,
                    workspace_bytes, nullptr, stream, true, h_fp8, h_scale, FP8BS_LAYOUT_TILES);
 }
 
@@ -794,8 +818,10 @@ fp8bs_status fp8bs_gemm_swiglu_ex(const void* x_bf16, const uint8_t* x_fp8, cons
                                   int64_t n, int64_t k, void* y_bf16, uint8_t* h_fp8,
                                   float* h_scale, void* workspace, size_t workspace_bytes,
                                   const fp8bs_gemm_config* cfg, void* stream) {
-  return gemm_impl(x_bf16, x_fp8, x_scale, m, w_fp8, w_scale, n, k, y_bf16, workspace,
-                   workspace_bytes, cfg, stream, true, h_fp8, h_scale);
+  if (!gemm_shape_ok(m, n, k, true)) return FP8BS_ERR_SHAPE;
+  if (!cfg) return FP8BS_ERR_NULL;
+  return gemm_impl(x_bf16 != nullptr, x_bf16, x_fp8, x_scale, m, w_fp8, w_scale, n, k, y_bf16,
+                   workspace, workspace_bytes, cfg, stream, true, h_fp8, h_scale);
 }
 
 fp8bs_status fp8bs_gemm_swiglu_select_config(int64_t m, int64_t n, int64_t k,
@@ -837,7 +863,7 @@ const char* fp8bs_status_string(fp8bs_status s) {
   switch (s) {
     case FP8BS_OK: return "FP8BS_OK";
     case FP8BS_ERR_NULL: return "FP8BS_ERR_NULL: a required pointer is NULL";
-    case FP8BS_ERR_SHAPE: return "FP8BS_ERR_SHAPE: unsupported shape (n, k must be multiples of 128; gemm m in 0..32)";
+    case FP8BS_ERR_SHAPE: return "FP8BS_ERR_SHAPE: unsupported shape (n, k must be multiples of 128; an extent is negative or beyond its documented limit)";
     case FP8BS_ERR_ALIGN: return "FP8BS_ERR_ALIGN: pointer misaligned";
     case FP8BS_ERR_WORKSPACE: return "FP8BS_ERR_WORKSPACE: workspace missing or too small";
     case FP8BS_ERR_DEVICE: return "FP8BS_ERR_DEVICE: no current HIP device or not gfx950";

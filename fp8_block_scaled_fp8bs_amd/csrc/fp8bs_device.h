@@ -263,18 +263,49 @@ __device__ __forceinline__ float cast_quarter_cols(const uint4 (&xw)[4], uint32_
 
 // ----------------------------------------------------- SwiGLU epilogue ---
 
-// h = silu(g) * u for a pair of (gate, up) bf16 values packed in one dword
-// each, rounded to bf16: silu(g) = g / (1 + e^-g) (the gated unit of
-// Shazeer, "GLU Variants Improve Transformer"), evaluated in fp32 with a
-// correctly rounded division and without contraction into fused
-// multiply-adds, so every kernel that applies it gives the same bits.
-__device__ __forceinline__ uint32_t swiglu_pair(uint32_t g, uint32_t u) {
+// fp64 -> bf16 bits in one rounding (nearest, ties to the even mantissa):
+// a value whose leading bit has weight 2^e keeps the multiple of 2^(e-7)
+// nearest to it, values below 2^-126 the nearest multiple of 2^-133
+// (subnormals); magnitudes that round past the largest finite bf16 become
+// infinity, and zero keeps its sign. Integer rounding on the fp64 pattern
+// for the normal range, an exact power-of-two scaling and rint below it.
+__device__ __forceinline__ uint32_t bf16_rne_f64(double v) {
+  const uint64_t bits = (uint64_t)__double_as_longlong(v);
+  const uint32_t sign = (uint32_t)(bits >> 48) & 0x8000u;
+  const uint64_t a = bits & 0x7FFFFFFFFFFFFFFFull;
+  if (a > 0x7FF0000000000000ull) return sign | 0x7FC0u;   // NaN
+  if (a >= 0x3810000000000000ull) {                        // |v| >= 2^-126
+    // drop 45 of the 52 fraction bits; a carry moves into the exponent
+    const uint64_t r = a + ((1ull << 44) - 1ull) + ((a >> 45) & 1ull);
+    const int64_t e = (int64_t)(r >> 52) - 1023 + 127;     // biased bf16 exponent
+    if (e >= 255) return sign | 0x7F80u;
+    return sign | (uint32_t)(e << 7) | (uint32_t)((r >> 45) & 0x7Fu);
+  }
+  // |v| < 2^-126: the scaled value is exact and below 128; 128 itself is
+  // the pattern of the smallest normal, 2^-126
+  const double t = __builtin_rint(__longlong_as_double((long long)a) * 0x1p133);
+  return sign | (uint32_t)t;
+}
+
+// h = silu(g) * u for one (gate, up) pair of bf16 values, rounded once to
+// bf16: silu(g) = g / (1 + e^-g) (the gated unit of Shazeer, "GLU Variants
+// Improve Transformer"). Evaluated in fp64: e^-g overflows only below
+// g = -709, where silu(g) * u lies far below the smallest bf16, so the
+// quotient g / inf = -0 gives the right bf16 zero; for every other bf16 g
+// the intermediates stay normal fp64 values (fp32 evaluation would lose
+// e^g to subnormals or overflow for g below about -87). No contraction
+// into fused multiply-adds, so every kernel that applies it gives the same
+// bits.
+__device__ __forceinline__ uint32_t swiglu_one(float g, float u) {
 #pragma clang fp contract(off)
-  const float g0 = bf16_lo(g), g1 = bf16_hi(g);
-  const float u0 = bf16_lo(u), u1 = bf16_hi(u);
-  const float h0 = g0 / (1.0f + expf(-g0)) * u0;
-  const float h1 = g1 / (1.0f + expf(-g1)) * u1;
-  return pack_bf16x2(h0, h1);
+  const double gd = (double)g;
+  const double h = gd / (1.0 + exp(-gd)) * (double)u;
+  return bf16_rne_f64(h);
+}
+
+// The pair of (gate, up) values packed as bf16 in one dword each.
+__device__ __forceinline__ uint32_t swiglu_pair(uint32_t g, uint32_t u) {
+  return swiglu_one(bf16_lo(g), bf16_lo(u)) | (swiglu_one(bf16_hi(g), bf16_hi(u)) << 16);
 }
 
 // The SwiGLU step and the 1x128 cast for one activation row of one 128-column

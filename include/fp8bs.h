@@ -44,16 +44,21 @@
  *     asynchronous on it.
  *   - Arguments are checked before anything is launched. On any non-OK
  *     status nothing has been launched and no memory has been touched.
- *     Checks, in order: NULL pointers, shapes, alignment, workspace size,
- *     device (must be gfx950). A failed launch returns FP8BS_ERR_LAUNCH;
- *     faults inside a kernel surface at the caller's next synchronization.
+ *     Checks, in order: shapes (a call whose output is empty returns
+ *     FP8BS_OK right after them, whatever its pointers), NULL pointers,
+ *     alignment, explicit kernel configuration, workspace size, device
+ *     (must be gfx950). The first failing check decides the status. A failed
+ *     launch returns FP8BS_ERR_LAUNCH; faults inside a kernel surface at the
+ *     caller's next synchronization.
  *   - There is no fallback: an unsupported shape is an error, never a
  *     silently slower path.
  *   - Determinism: the same inputs, shape, device and library build give
  *     bit-identical outputs. The GEMM uses no floating-point atomics.
  *   - Shapes: n and k must be multiples of 128 (whole blocks); m may be any
- *     value >= 0 for the quantizers and 0..32 for the GEMM. A zero extent
- *     is a no-op (k == 0 in the GEMM writes zeros: the empty sum).
+ *     value >= 0 for the quantizers and 0..2^20 for the GEMM (decode kernels
+ *     up to 32 rows, the prefill kernel above). The GEMM also needs
+ *     n < 2^31 (n/128 < 2^24) and k/128 <= 2^20. A zero extent is a no-op
+ *     (k == 0 in the GEMM writes zeros: the empty sum).
  *   - Alignment: bf16 and code pointers 16-byte aligned; scale pointers
  *     4-byte aligned; workspace 16-byte aligned.
  */

@@ -104,6 +104,40 @@ def test_gemm_argument_errors_before_any_launch(lib):
         assert gemm(lib, work=P, wbytes=1 << 24) == E_DEV
 
 
+def test_gemm_check_order(lib):
+    """Every GEMM entry point checks shape, then NULL pointers, then
+    alignment, then the configuration, then the workspace, then the device:
+    with several faults in one call the earliest check decides."""
+    big_n = 1 << 31                       # n / 128 = 2^24: column indices overflow 32 bits
+    # a bad shape wins over NULL and misaligned pointers
+    assert gemm(lib, x=None, n=500) == E_SHAPE
+    assert gemm(lib, x=None, y=None, w=None, k=1000) == E_SHAPE
+    assert gemm(lib, x=P + 2, m=-1) == E_SHAPE
+    assert gemm(lib, n=big_n) == E_SHAPE
+    assert gemm(lib, x=None, n=big_n) == E_SHAPE
+    assert gemm(lib, m=33, k=1 << 24) == E_SHAPE          # prefill offsets need k < 2^24
+    assert lib.fp8bs_gemm_q(None, None, 8, P, P, 500, 1024, P, None, 0, None) == E_SHAPE
+    assert lib.fp8bs_gemm_tiles(None, 8, P, P, big_n, 1024, P, None, 0, None) == E_SHAPE
+    assert lib.fp8bs_gemm_q_tiles(None, None, 8, P, P, 512, 1000, P, None, 0, None) == E_SHAPE
+    assert lib.fp8bs_gemm_ex(None, None, None, 8, P, P, 500, 1024, P, None, 0, None, None) == E_SHAPE
+    assert lib.fp8bs_gemm_swiglu(None, 8, P, P, 640, 1024, P, P, P, None, 0, None) == E_SHAPE
+    assert lib.fp8bs_gemm_swiglu_ex(None, None, None, 8, P, P, 640, 1024, P, P, P, None, 0,
+                                    None, None) == E_SHAPE
+    assert lib.fp8bs_pack_weight(None, big_n, 128, None, None) == E_SHAPE
+    # the largest n the kernels index passes the shape check
+    assert gemm(lib, x=None, n=big_n - 128) == E_NULL
+    # NULL wins over misalignment and a missing workspace
+    assert gemm(lib, x=None, w=P + 8, n=5120, k=17408) == E_NULL
+    assert lib.fp8bs_gemm_q(P, None, 8, P + 8, P, 512, 1024, P, None, 0, None) == E_NULL
+    # misalignment wins over a missing workspace
+    assert gemm(lib, y=P + 4, n=5120, k=17408) == E_ALIGN
+    # the configuration is checked before the workspace
+    import fp8_block_scaled_fp8bs_amd as fp8bs
+    c = fp8bs._Config(1, 3, 1, 1, 4, 2, 0, 0)   # 3 tiles per wave is not compiled
+    assert lib.fp8bs_gemm_ex(P, None, None, 8, P, P, 512, 1024, P, None, 0, ctypes.byref(c),
+                             None) == E_CFG
+
+
 def test_gemm_workspace_checked(lib):
     import fp8_block_scaled_fp8bs_amd as fp8bs
     cfg = fp8bs.select_config(8, 5120, 17408)

@@ -5,12 +5,14 @@ The epilogue turns floating-point values into integer codes, so the checks
 are layered:
 
 * standalone epilogue on seeded bf16 inputs: codes and scales bit-exact to
-  the oracle, block by block. The kernel evaluates h = silu(g) * u in fp32
-  (a few ulp from the exact value), the oracle in fp64, and both round h to
-  bf16; where the exact h lies within a relative 2^-18 of a bf16 rounding
-  boundary either neighbour is a correct bf16 h, and the block passes when
-  the kernel's codes and scale equal the oracle's cast of one of those
-  candidate blocks. Everywhere else there is exactly one correct answer;
+  the oracle, block by block. Kernel and oracle both evaluate h = silu(g) * u
+  in fp64 and round it once to bf16; they can differ only through their fp64
+  exponential (an ulp or two) and the rounding of one division and one
+  product, a relative 2^-50 or so. So where the exact h lies within a
+  relative 2^-40 of a bf16 rounding boundary either neighbour is a correct
+  bf16 h, and the block passes when the kernel's codes and scale equal the
+  oracle's cast of one of those candidate blocks. Everywhere else there is
+  exactly one correct answer;
 * fused call: y equal bit for bit to the plain GEMM in the same
   configuration and within the GEMM tolerance of the oracle; h equal bit for
   bit to the standalone epilogue applied to that y; and, end to end against
@@ -30,7 +32,7 @@ from workloads import WORKLOADS, act_bf16, bf16_from_f32
 pytestmark = pytest.mark.gpu
 
 TOL = dict(rel=2.0 ** -7, abs_rms=1e-3)
-WINDOW = 2.0 ** -18   # relative distance from a bf16 rounding boundary treated as a tie
+WINDOW = 2.0 ** -40   # relative distance from a bf16 rounding boundary treated as a tie
 
 
 @pytest.fixture(scope="module")
@@ -129,6 +131,94 @@ def test_standalone_epilogue_special_values(fp8bs):
     assert hs[0, 0] == 0.0 and hs[0, 2] == 0.0
     assert np.array_equal(hq[0, :128] & 0x80, np.where((np.arange(128) % 2 == 1) ^
                                                         (np.arange(128) % 4 >= 2), 0x80, 0))
+
+
+def _negative_gate_rows(rng, inter):
+    """Gate and up rows whose h needs fp64: gates where e^g is below the
+    smallest normal fp32 (g < -87.3) or overflows e^-g in fp32 (g < -88.7),
+    with up values from 1 to near the largest bf16 so that h spans normal
+    and subnormal bf16 values and zeros."""
+    rows_g, rows_u = [], []
+    j = np.arange(inter)
+    # whole blocks of gates in [-97, -85] with up = 1
+    rows_g.append(-85.0 - 12.0 * rng.random(inter))
+    rows_u.append(np.ones(inter))
+    # mixed blocks: every other gate very negative, the rest ordinary
+    g = rng.standard_normal(inter) * 3.0
+    g[::2] = -85.0 - 12.0 * rng.random(inter // 2)
+    rows_g.append(g)
+    rows_u.append(rng.standard_normal(inter) * 4.0)
+    # the bf16 neighbours of the fp32 overflow point -88.72 (spacing 0.5 there)
+    rows_g.append(np.array([-87.5, -88.0, -88.5, -89.0, -89.5, -90.0, -88.0, -89.0])[j % 8])
+    rows_u.append(np.where(j % 3 == 0, 1.0, np.where(j % 3 == 1, -2.5, 1e20)))
+    # far below: g in [-180, -87] with up near the top of the bf16 range, so
+    # h is normal, subnormal or zero; a block of gates -800 and -1e30 (h = -0)
+    g = -87.0 - 93.0 * rng.random(inter)
+    g[256:384] = np.where(j[256:384] % 2, -800.0, -1e30)
+    rows_g.append(g)
+    rows_u.append(np.exp(rng.uniform(0.0, 88.0, inter)) * np.where(j % 5 == 0, -1.0, 1.0))
+    return np.array(rows_g, np.float32), np.array(rows_u, np.float32)
+
+
+def test_standalone_epilogue_very_negative_gates(fp8bs):
+    """Gates below -85, where silu(g) = g e^g needs more than fp32 range: the
+    kernel's codes and scales equal the oracle's block by block."""
+    inter = 512
+    g, u = _negative_gate_rows(np.random.default_rng(13), inter)
+    y_bits = np.concatenate([bf16_from_f32(g), bf16_from_f32(u)], axis=1)
+    hq, hs = _host(*fp8bs.swiglu_quant(dev_bf16(y_bits)))
+    blocks, _ = check_epilogue_exact(y_bits, hq, hs)
+    assert blocks == 4 * 4
+    h = oracle.swiglu_quant_ref(y_bits)[0]
+    # the cases reach nonzero h below the fp32 limits, and exact zeros
+    hf = oracle.bf16_bits_to_f32(h)
+    assert np.any((hf != 0) & (np.abs(hf) < 2.0 ** -126)) and np.any(hf[0] != 0)
+    assert np.all(hf[3, 256:384] == 0)
+
+
+# Every placement of the epilogue on outputs whose gate half is very
+# negative: (path, tiles_n, waves_n, waves_k, depth, split_k, reduce, epilogue).
+NEG_GATE_CONFIGS = [
+    (1, 1, 2, 4, 5, 1, 0, 1),    # inside the MFMA grid kernel
+    (3, 4, 1, 8, 4, 1, 0, 1),    # inside the row-range kernel
+    (1, 1, 5, 1, 5, 4, 0, 0),    # in the split sum
+    (1, 1, 5, 1, 5, 1, 0, 0),    # second kernel
+]
+
+
+@pytest.mark.parametrize("cfg", NEG_GATE_CONFIGS)
+def test_fused_very_negative_gates(fp8bs, cfg):
+    """A GEMM whose gate outputs fall in [-101, -86] and whose up outputs span
+    1e-3 .. 1e30: y equals the plain GEMM and is within tolerance of the
+    oracle, h equals the standalone epilogue on that y, and h equals the
+    oracle's epilogue applied to the kernel's y, block by block."""
+    from fp8_block_scaled_fp8bs_amd import GemmConfig
+    c = GemmConfig(*cfg)
+    m, inter, k = 8, 640, 512
+    rng = np.random.default_rng(21)
+    x = (1.0 + 0.01 * rng.standard_normal((m, k))).astype(np.float32)
+    n_idx = np.arange(inter)
+    w_gate = -(84.0 + 14.0 * (n_idx % 128) / 128.0) / k
+    # one magnitude per 128-row block (1e-3 .. 1e29), up to 10x within it, so
+    # the block quantization keeps every row's weights
+    w_up = 10.0 ** (-3.0 + 8.0 * (n_idx // 128) + (n_idx % 128) / 128.0) / k
+    w = np.concatenate([np.repeat(w_gate[:, None], k, 1), np.repeat(w_up[:, None], k, 1)])
+    w = w * (1.0 + 0.01 * rng.standard_normal(w.shape))
+    pr = Problem(fp8bs, bf16_from_f32(w.astype(np.float32)), bf16_from_f32(x))
+    announce("gemm_swiglu very negative gates", c)
+    y, hq, hs = fp8bs.gemm_swiglu_ex(c, pr.wq, pr.ws, x=pr.x)
+    y_plain = fp8bs.gemm_ex(dataclasses.replace(c, epilogue=0), pr.wq, pr.ws, x=pr.x)
+    hq2, hs2 = fp8bs.swiglu_quant(y)
+    torch.cuda.synchronize()
+    yb = host_bits(y)
+    assert np.array_equal(yb, host_bits(y_plain))
+    rep = oracle.tolerance_report(yb, pr.ref(m), **TOL)
+    assert rep["finite"] and rep["n_bad"] == 0, rep
+    gate = oracle.bf16_bits_to_f32(yb[:, :inter])
+    assert gate.max() < -80.0 and gate.min() > -105.0
+    hq, hs = hq.cpu().numpy(), hs.cpu().numpy()
+    assert np.array_equal(hq, hq2.cpu().numpy()) and same_bits_f32(hs, hs2.cpu().numpy())
+    check_epilogue_exact(yb, hq, hs)
 
 
 # --------------------------------------------------------- fused up/gate ---
