@@ -80,33 +80,57 @@ def stored_traffic(workload: str, m: int, layout: str) -> dict | None:
         return None
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(workload, m: int, budget_s: float) -> dict:
-    """Time the CPU oracle (cast + fp64 GEMM) on the same workload."""
+    """Time the CPU oracle (cast + fp64 GEMM) on the same workload: on every
+    host core the process may use (BLAS threads set to that count), then on
+    one core."""
     import numpy as np
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     import oracle
     w_bits = workload.weight()
     x_bits = workload.act(m)
     wq, ws = oracle.quantize_weight_ref(w_bits)     # one-off, not timed (as on the GPU)
-    oracle.gemm_fused_ref(x_bits, wq, ws)           # warm-up
-    times = []
-    t_end = time.perf_counter() + budget_s
-    while len(times) < 3 or (time.perf_counter() < t_end and len(times) < 1000):
-        t0 = time.perf_counter()
-        oracle.gemm_fused_ref(x_bits, wq, ws)
-        times.append(time.perf_counter() - t0)
-    med = float(np.median(times))
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    cores = len(os.sched_getaffinity(0))
+
+    def timed(budget, limit):
+        with threadpool_limits(limits=limit):
+            oracle.gemm_fused_ref(x_bits, wq, ws)           # warm-up
+            times = []
+            t_end = time.perf_counter() + budget
+            while len(times) < 3 or (time.perf_counter() < t_end and len(times) < 1000):
+                t0 = time.perf_counter()
+                oracle.gemm_fused_ref(x_bits, wq, ws)
+                times.append(time.perf_counter() - t0)
+            threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        return float(np.median(times)), len(times), int(threads)
+
+    med, count, threads = timed(budget_s, cores)
+    med1, count1, threads1 = timed(budget_s / 3, 1)
+    nbytes = workload.algorithmic_bytes(m)
     return {
-        "value": workload.algorithmic_bytes(m) / med / 1e9,
+        "value": nbytes / med / 1e9,
         "unit": "GB/s",
-        "cores": int(threads),
+        "cores": threads,
         "kind": "oracle",
-        "sample": f"{len(times)} full oracle GEMMs (per-row cast + fp64 block GEMM) of the "
-                  f"timed workload, median {med * 1e3:.1f} ms each; host {platform.processor() or platform.machine()}, "
-                  f"{len(os.sched_getaffinity(0))} cores visible",
+        "sample": f"{count} full oracle GEMMs (per-row cast + fp64 block GEMM) of the timed "
+                  f"workload, median {med * 1e3:.1f} ms each, on {threads} BLAS threads; host "
+                  f"{cpu_model()}, {cores} cores visible",
         "us_per_gemm": med * 1e6,
+        "one_core": {"value": nbytes / med1 / 1e9, "unit": "GB/s", "cores": threads1,
+                     "us_per_gemm": med1 * 1e6, "gemms": count1},
+        "cpu_model": cpu_model(),
     }
 
 
@@ -643,27 +667,69 @@ def main() -> int:
     eager_ms = e0.elapsed_time(e1) / args.steps
 
     # --- graph: the same K steps captured once and replayed ------------------
+    # The timed graph (exactly K steps) is launched right behind an untimed
+    # lead graph of at least LEAD steps, with no synchronization between
+    # them, so the timed region starts when the lead graph's last kernel ends
+    # and holds the K GEMMs back to back: the graph launch latency stays
+    # outside it, whatever K is.
     graph_ms = None
-    if not args.eager_only:
+    spread = None
+    LEAD = 200
+
+    def capture(fn, count):
         g = torch.cuda.CUDAGraph()
         cap = torch.cuda.Stream()
         cap.wait_stream(stream)
         with torch.cuda.stream(cap):
             with torch.cuda.graph(g, stream=cap):
-                for i in range(args.steps):
-                    step(i)
+                for i in range(count):
+                    fn(i)
         stream.wait_stream(cap)
+        return g
+
+    def timed_replay(g_lead, g):
+        g_lead.replay()
+        torch.cuda.synchronize()
+        g_lead.replay()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        g.replay()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1)
+
+    if not args.eager_only:
+        g_lead = capture(lambda i: step(args.steps + i), max(LEAD, args.steps))
+        g = capture(step, args.steps)
         g.replay()  # warm replay
         torch.cuda.synchronize()
-        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        g0.record(stream)
-        g.replay()
-        g1.record(stream)
+        graph_ms = timed_replay(g_lead, g) / args.steps
+        # spread: 20 more replays of the K-step graph, each timed on its own
+        # (events back to back, the lead graph first), per-GEMM time of each
+        per = []
+        g_lead.replay()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(21)]
+        ev[0].record(stream)
+        for r in range(20):
+            g.replay()
+            ev[r + 1].record(stream)
         torch.cuda.synchronize()
-        graph_ms = g0.elapsed_time(g1) / args.steps
+        per = sorted(ev[r].elapsed_time(ev[r + 1]) * 1e3 / args.steps for r in range(20))
+        spread = {"replays": 20, "gemms_per_replay": args.steps,
+                  "us_per_gemm_p10": round(per[2], 3), "us_per_gemm_median": round(per[10], 3),
+                  "us_per_gemm_p90": round(per[18], 3)}
+        # the same measurement on a 400-step graph, as a check that the
+        # per-GEMM time does not depend on K
+        g400 = capture(step, 400)
+        g400.replay()
+        torch.cuda.synchronize()
+        spread["us_per_gemm_400_step_graph"] = round(timed_replay(g_lead, g400) * 1e3 / 400, 3)
+        del g400
 
     launches = fp8bs.launch_count("gemm_mfma") + fp8bs.launch_count("gemm_dot") - launches0
-    expected = args.warmup + args.steps * (1 if args.eager_only else 2)
+    # host launch calls: warm-up, eager steps, and the captures (replays make none)
+    graph_launches = 0 if args.eager_only else max(LEAD, args.steps) + args.steps + 400
+    expected = args.warmup + args.steps + graph_launches
     if launches != expected:
         print(f"kernel launch count {launches} != expected {expected}", file=sys.stderr)
         return 1
@@ -672,20 +738,27 @@ def main() -> int:
         print(f"unexpected runtime mappings: {maps}", file=sys.stderr)
         return 1
 
-    # --- streaming-read ceiling over the same byte count ---------------------
+    # --- streaming-read ceiling over the same bytes ----------------------------
+    # A plain read of the weight codes of each step, timed exactly like the
+    # GEMM: a graph of K launches over the same rotating pool behind a lead
+    # graph. One workgroup of 512 threads per compute unit (or two), each
+    # reading a contiguous range with non-temporal 16-byte loads, 2 x depth
+    # in flight per lane. The best configuration is the ceiling.
     sink = torch.zeros(4, dtype=torch.int32, device=dev)
-    for i in range(min(pool_n, 8)):
-        fp8bs.diag_read(pool[i][0], sink)
-    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    r0.record(stream)
-    reps = max(args.steps // 2, 1)
-    for i in range(reps):
-        fp8bs.diag_read(pool[i % pool_n][0], sink)
-    r1.record(stream)
-    torch.cuda.synchronize()
-    read_us = r0.elapsed_time(r1) * 1e3 / reps
-    read_gbps = code_bytes / (read_us * 1e3)
+    ceiling = {}
+    if not args.eager_only:
+        for blocks, depth in ((256, 4), (256, 8), (256, 16), (512, 8)):
+            def rd(i, blocks=blocks, depth=depth):
+                fp8bs.diag_stream(pool[i % pool_n][0], sink, blocks=blocks, depth=depth)
+            gl = capture(lambda i: rd(args.steps + i), max(LEAD, args.steps))
+            gr = capture(rd, args.steps)
+            gr.replay()
+            torch.cuda.synchronize()
+            us_r = timed_replay(gl, gr) * 1e3 / args.steps
+            ceiling[f"{blocks}x512_depth{depth}"] = {"us": round(us_r, 3),
+                                                     "GBps": round(code_bytes / (us_r * 1e3), 1)}
+            del gl, gr
+    best = max(ceiling.values(), key=lambda v: v["GBps"]) if ceiling else None
 
     # --- library reference: the same product in bf16 through torch (hipBLASLt)
     lib_ref = None if args.no_library_ref else library_reference(args, x, n, k, gen, dev, stream)
@@ -731,7 +804,12 @@ def main() -> int:
         "us_per_gemm": round(us, 3),
         "pct_of_8TBps": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "eager_us_per_gemm": round(eager_ms * 1e3, 3),
-        "stream_read_ceiling_GBps": round(read_gbps, 1),
+        "replay_spread": spread,
+        "stream_read_ceiling": ({"bytes": code_bytes, "best_us": best["us"], "best_GBps": best["GBps"],
+                                 "gemm_frac_of_ceiling": round(best["us"] / us, 4),
+                                 "configs": ceiling,
+                                 "timing": "graph of K launches behind a lead graph, as the GEMM"}
+                                if best else None),
         "bf16_library_reference": (dict(lib_ref, fp8_speedup=round(lib_ref["us_per_gemm"] / us, 2))
                                    if lib_ref else None),
         "mfma_flops_frac": round(2 * m * n * k / (us * 1e-6) / (FP8_DENSE_PEAK_TFLOPS * 1e12), 6),

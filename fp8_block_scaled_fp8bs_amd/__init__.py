@@ -22,7 +22,8 @@ __all__ = [
     "workspace_bytes", "config_workspace_bytes", "select_config",
     "swiglu_quant", "gemm_swiglu", "gemm_swiglu_ex", "swiglu_select_config",
     "swiglu_workspace_bytes",
-    "encode_e4m3", "launch_count", "build_info", "diag_read", "diag_copy",
+    "encode_e4m3", "launch_count", "build_info", "diag_read", "diag_copy", "diag_stream",
+    "streamk_plan_check", "PATH_MFMA_STREAMK",
     "hip_runtime_mappings", "PATH_MFMA", "PATH_DOT", "REDUCE_KERNEL",
     "REDUCE_LAST_ARRIVER", "EPILOGUE_SEPARATE", "EPILOGUE_IN_GEMM", "LAYOUT_ROWS",
     "LAYOUT_TILES", "COUNTER",
@@ -34,6 +35,7 @@ _LIB = None
 
 PATH_AUTO, PATH_MFMA, PATH_DOT, PATH_MFMA_ROWS, PATH_MFMA_STREAM, PATH_PREFILL = 0, 1, 2, 3, 4, 5
 PATH_MFMA_ROWS_REG = 6
+PATH_MFMA_STREAMK = 7
 REDUCE_KERNEL, REDUCE_LAST_ARRIVER = 0, 1
 EPILOGUE_SEPARATE, EPILOGUE_IN_GEMM = 0, 1
 LAYOUT_ROWS, LAYOUT_TILES = 0, 1
@@ -119,6 +121,8 @@ def load() -> ctypes.CDLL:
         "fp8bs_build_info": (ctypes.c_char_p, []),
         "fp8bs_diag_read": (i32, [vp, sz, vp, i32, vp]),
         "fp8bs_diag_copy": (i32, [vp, vp, sz, vp]),
+        "fp8bs_diag_stream": (i32, [vp, sz, vp, i32, i32, vp]),
+        "fp8bs_streamk_plan_check": (i32, [i64, i64, i32, i32]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -428,6 +432,20 @@ def build_info() -> str:
 def diag_read(t: torch.Tensor, sink: torch.Tensor, blocks: int = 0, stream=None) -> None:
     nbytes = t.numel() * t.element_size()
     _check(load().fp8bs_diag_read(t.data_ptr(), nbytes, sink.data_ptr(), blocks, _stream(stream)))
+
+
+def diag_stream(t: torch.Tensor, sink: torch.Tensor, blocks: int = 256, depth: int = 8,
+                stream=None, nbytes: int | None = None) -> None:
+    """Streaming-read ceiling kernel over the first nbytes (default: all) of t."""
+    nb = t.numel() * t.element_size() if nbytes is None else int(nbytes)
+    _check(load().fp8bs_diag_stream(t.data_ptr(), nb, sink.data_ptr(), blocks, depth,
+                                    _stream(stream)))
+
+
+def streamk_plan_check(n: int, k: int, split: int, workgroups: int = 256) -> int:
+    """Host-side self-check of the stream-K work partition (0 = consistent,
+    1 = not a supported partition, other values: the first inconsistency)."""
+    return int(load().fp8bs_streamk_plan_check(n, k, split, workgroups))
 
 
 def diag_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:

@@ -1,6 +1,7 @@
 // C ABI of the library: argument checks, the fixed configuration table,
 // kernel launches and launch counters. Every kernel runs on the caller's
 // stream; nothing here allocates, frees or synchronizes.
+#include <algorithm>
 #include <atomic>
 #include <cstring>
 #include <mutex>
@@ -12,6 +13,7 @@
 #include "fp8bs_quant.h"
 #include "fp8bs_reduce.h"
 #include "fp8bs_registry.h"
+#include "fp8bs_streamk.h"
 
 using namespace fp8bs;
 
@@ -143,6 +145,9 @@ const KernelEntry* find_kernel(const fp8bs_gemm_config& c, int m, bool fused,
   if (c.path == FP8BS_PATH_MFMA || c.path == FP8BS_PATH_MFMA_ROWS ||
       c.path == FP8BS_PATH_MFMA_ROWS_REG) {
     mt = m <= 16 ? 1 : 2;
+  } else if (c.path == FP8BS_PATH_MFMA_STREAMK) {
+    if (swiglu) return nullptr;  // the epilogue runs in a second kernel
+    mt = m <= 16 ? 1 : 2;
   } else if (c.path == FP8BS_PATH_MFMA_STREAM) {
     if (c.tiles_n != 1) return nullptr;
     mt = m <= 8 ? 1 : (m <= 16 ? 2 : 4);  // staging passes
@@ -173,6 +178,7 @@ const KernelEntry* find_kernel(const fp8bs_gemm_config& c, int m, bool fused,
 // path divides n by the compute-unit count at launch instead).
 int config_rows(const fp8bs_gemm_config& c) {
   if (is_row_range(c.path)) return 4;
+  if (c.path == FP8BS_PATH_MFMA_STREAMK) return 16;
   if (c.path == FP8BS_PATH_PREFILL) return pf_tile_n(c.waves_n);
   return (c.path == FP8BS_PATH_DOT ? 8 : 16) * c.tiles_n * c.waves_n;
 }
@@ -200,6 +206,8 @@ size_t config_lds_bytes(const fp8bs_gemm_config& c, int m, int64_t n, int kbn, i
   if (c.path == FP8BS_PATH_PREFILL)
     return (size_t)(c.depth > 1 ? pf_dma_lds_bytes(c.waves_n, c.depth) : pf_lds_bytes(c.waves_n));
   const int mt = m <= 16 ? 1 : 2;
+  if (c.path == FP8BS_PATH_MFMA_STREAMK)
+    return (size_t)lds_streamk_bytes(c.split_k > 0 ? kbn / c.split_k : kbn, m, c.waves_k, mt);
   if (is_row_range(c.path)) {
     // weight scales of the row range first, then the kernel's own layout,
     // then (SwiGLU epilogue) the staged outputs
@@ -230,6 +238,20 @@ size_t config_lds_bytes(const fp8bs_gemm_config& c, int m, int64_t n, int kbn, i
 
 constexpr size_t kLdsLimit = 160 * 1024;  // one workgroup per CU at most
 
+// The stream-K plan of a configuration (workgroups: the table's compute units).
+SkPlan streamk_plan(const fp8bs_gemm_config& c, int64_t n, int64_t k) {
+  return sk_plan((int)(n / 16), (int)(k / BLK), c.split_k, kTableCUs);
+}
+
+// Whether a stream-K configuration can run this shape: a supported plan,
+// weight offsets within a 31-bit buffer range, one workgroup per CU.
+bool streamk_fits(const fp8bs_gemm_config& c, int64_t m, int64_t n, int64_t k) {
+  if (c.waves_n != 1 || c.waves_k < 1 || c.waves_k > 15 || c.split_k < 1) return false;
+  if (m > kMaxDecodeM || n * k >= ((int64_t)1 << 31)) return false;
+  return sk_plan_ok(streamk_plan(c, n, k));
+}
+
+
 fp8bs_gemm_config make_cfg(int path, int tn, int wn, int wk, int d, int split) {
   fp8bs_gemm_config c;
   std::memset(&c, 0, sizeof(c));
@@ -254,6 +276,7 @@ constexpr int DT = FP8BS_PATH_DOT;
 constexpr int RW = FP8BS_PATH_MFMA_ROWS;
 constexpr int ST = FP8BS_PATH_MFMA_STREAM;
 constexpr int RR = FP8BS_PATH_MFMA_ROWS_REG;
+constexpr int SK = FP8BS_PATH_MFMA_STREAMK;
 
 // Configurations the SwiGLU call accepts. With the separate epilogue:
 // everything but the last-arriver reduce (the split sum carries the
@@ -279,6 +302,7 @@ bool candidate_fits(const Candidate& cd, int64_t m, int64_t n, int kbn, fp8bs_ge
   if (c.split_k > kbn) return false;
   if (cd.path == ST && !stream_offsets_fit(m, (int64_t)kbn * BLK)) return false;
   if (cd.path == RR && !rows_reg_fits(c, kbn)) return false;
+  if (cd.path == SK && !streamk_fits(c, m, n, (int64_t)kbn * BLK)) return false;
   if (kbn > 0 && config_lds_bytes(c, (int)m, n, kbn, kTableCUs) > kLdsLimit) return false;
   *out = c;
   return true;
@@ -432,6 +456,8 @@ size_t prefill_workspace(const fp8bs_gemm_config& c, int64_t m, int64_t n, int64
 
 size_t cfg_workspace(const fp8bs_gemm_config& c, int64_t m, int64_t n, int64_t k, bool fused) {
   if (c.path == FP8BS_PATH_PREFILL) return prefill_workspace(c, m, n, k, fused);
+  if (c.path == FP8BS_PATH_MFMA_STREAMK)
+    return (size_t)sk_workspace_bytes(streamk_plan(c, n, k), m <= 16 ? 1 : 2);
   size_t b = cfg_partial_bytes(c, m, n);
   if (c.split_k > 1 && c.reduce == FP8BS_REDUCE_LAST_ARRIVER) {
     const int rows = config_rows(c);
@@ -444,6 +470,7 @@ size_t cfg_workspace(const fp8bs_gemm_config& c, int64_t m, int64_t n, int64_t k
 // 64-bit arrival counter per 128-column block of h.
 size_t swiglu_workspace(const fp8bs_gemm_config& c, int64_t m, int64_t n, int64_t k, bool fused) {
   if (c.path == FP8BS_PATH_PREFILL) return prefill_workspace(c, m, n, k, fused);
+  if (c.path == FP8BS_PATH_MFMA_STREAMK) return cfg_workspace(c, m, n, k, fused);
   if (c.split_k > 1) return cfg_partial_bytes(c, m, n);
   if (c.epilogue != FP8BS_EPILOGUE_IN_GEMM) return 0;
   return (size_t)((n / (2 * BLK)) * sizeof(uint64_t) + 15) / 16 * 16;
@@ -545,11 +572,14 @@ fp8bs_status gemm_impl(bool fused, const void* x_bf16, const uint8_t* x_fp8,
     return FP8BS_ERR_CONFIG;
   if (c.path == FP8BS_PATH_MFMA_STREAM && !stream_offsets_fit(m, k)) return FP8BS_ERR_CONFIG;
   if (c.path == FP8BS_PATH_MFMA_ROWS_REG && !rows_reg_fits(c, kbn)) return FP8BS_ERR_CONFIG;
+  const bool streamk = c.path == FP8BS_PATH_MFMA_STREAMK;
+  if (streamk && (!streamk_fits(c, m, n, k) || c.reduce != FP8BS_REDUCE_KERNEL))
+    return FP8BS_ERR_CONFIG;
   if (c.reduce != FP8BS_REDUCE_KERNEL && c.reduce != FP8BS_REDUCE_LAST_ARRIVER)
     return FP8BS_ERR_CONFIG;
   if (swiglu && !swiglu_supported(c, (int)m)) return FP8BS_ERR_CONFIG;
   const bool in_gemm = swiglu && c.epilogue == FP8BS_EPILOGUE_IN_GEMM;
-  const bool split = c.split_k > 1;
+  const bool split = c.split_k > 1 && !streamk;  // stream-K: split_k counts K chunks
   const bool last_arriver = split && c.reduce == FP8BS_REDUCE_LAST_ARRIVER;
   const bool prefill = c.path == FP8BS_PATH_PREFILL;
   const KernelEntry* ke = find_kernel(c, (int)m, fused && !prefill, in_gemm);
@@ -609,6 +639,10 @@ fp8bs_status gemm_impl(bool fused, const void* x_bf16, const uint8_t* x_fp8,
                      SWIGLU_MAX_ARRIVALS)
     return FP8BS_ERR_CONFIG;
   dim3 block(64 * (is_row_range(c.path) ? 1 : c.waves_n) * c.waves_k);
+  if (streamk) {
+    grid = dim3((unsigned)kTableCUs);
+    block = dim3(64 * (c.waves_k + 1));
+  }
   if (prefill) {
     grid = dim3((unsigned)(n / pf_tile_n(c.waves_n)), (unsigned)((m + PF_TILE_M - 1) / PF_TILE_M),
                 (unsigned)c.split_k);
@@ -859,6 +893,57 @@ fp8bs_status fp8bs_encode_e4m3(const float* in, int64_t count, uint8_t* out, int
                 dim3((unsigned)(((count + 3) / 4 + 255) / 256)), dim3(256), 0, stream, args);
 }
 
+int32_t fp8bs_streamk_plan_check(int64_t n, int64_t k, int32_t split, int32_t workgroups) {
+  if (n <= 0 || k <= 0 || n % BLK || k % BLK || workgroups < 1 || split < 1) return 1;
+  if (n / 16 > 0x7FFFFFFF || k / BLK > 0x7FFFFFFF) return 1;
+  const SkPlan q = sk_plan((int)(n / 16), (int)(k / BLK), split, workgroups);
+  if (!sk_plan_ok(q)) return 1;
+  const int64_t units = (int64_t)q.ntiles * q.kbn;
+  if (units > ((int64_t)1 << 28)) return 1;  // keep the check's own memory small
+  std::vector<uint8_t> cover((size_t)units, 0);
+  // per tile: (first absolute K block, slot) of each segment
+  std::vector<std::vector<std::pair<int, int64_t>>> segs((size_t)q.ntiles);
+  const int64_t nslots = sk_slot_count(q);
+  for (int w = 0; w < q.P; ++w) {
+    int nsk;
+    const int nseg = sk_segments(q, w, &nsk);
+    if (nseg < 1) return 2;
+    const int chunk = sk_chunk_of(q, w);
+    for (int i = 0; i < nseg; ++i) {
+      const SkSegment g = sk_segment(q, w, nsk, i);
+      if (g.chunk != chunk) return 3;  // staged activations cover one chunk
+      if (g.b0 < 0 || g.b1 > q.kc || g.b0 >= g.b1 || g.tile < 0 || g.tile >= q.ntiles) return 4;
+      if (g.slot >= nslots) return 5;
+      for (int b = g.b0; b < g.b1; ++b) {
+        uint8_t& c = cover[(size_t)g.tile * q.kbn + (size_t)g.chunk * q.kc + b];
+        if (c) return 6;  // a unit computed twice
+        c = 1;
+      }
+      segs[g.tile].push_back({g.chunk * q.kc + g.b0, g.slot});
+    }
+  }
+  for (uint8_t c : cover)
+    if (!c) return 7;  // a unit never computed
+  std::vector<uint8_t> used((size_t)nslots, 0);
+  for (int t = 0; t < q.ntiles; ++t) {
+    std::vector<std::pair<int, int64_t>>& v = segs[t];
+    std::sort(v.begin(), v.end());
+    int64_t slots[SK_MAXPIECES];
+    const int np = sk_tile_pieces(q, t, slots);
+    if (np != (int)v.size() || np > SK_MAXPIECES) return 8;
+    if (np == 1 && (q.S != 1 || v[0].first != 0)) return 9;  // written directly: a whole tile
+    for (int i = 0; i < np; ++i) {
+      if (slots[i] != v[i].second) return 10;  // summation order = K order
+      if (np > 1) {
+        if (slots[i] < 0 || slots[i] >= nslots) return 5;
+        if (used[(size_t)slots[i]]) return 11;  // two pieces in one slot
+        used[(size_t)slots[i]] = 1;
+      }
+    }
+  }
+  return 0;
+}
+
 const char* fp8bs_status_string(fp8bs_status s) {
   switch (s) {
     case FP8BS_OK: return "FP8BS_OK";
@@ -912,6 +997,27 @@ fp8bs_status fp8bs_diag_read(const void* src, size_t bytes, void* sink, int32_t 
   g_counts[CNT_DIAG]++;
   return launch(reinterpret_cast<const void*>(diag_read_kernel), dim3((unsigned)want), dim3(256),
                 0, stream, args);
+}
+
+fp8bs_status fp8bs_diag_stream(const void* src, size_t bytes, void* sink, int32_t blocks,
+                               int32_t depth, void* stream) {
+  if (bytes % 16 || blocks < 1 || (depth != 4 && depth != 8 && depth != 16)) return FP8BS_ERR_SHAPE;
+  if (bytes == 0) return FP8BS_OK;
+  const int64_t per = ((int64_t)bytes / 16 + blocks - 1) / blocks * 16;
+  if (per >= ((int64_t)1 << 31) - (int64_t)3 * 512 * 16 * 16) return FP8BS_ERR_SHAPE;
+  if (!src || !sink) return FP8BS_ERR_NULL;
+  if (!aligned(src, 16) || !aligned(sink, 16)) return FP8BS_ERR_ALIGN;
+  const fp8bs_status st = current_device(nullptr);
+  if (st != FP8BS_OK) return st;
+  const uint8_t* s8 = static_cast<const uint8_t*>(src);
+  int64_t nb = (int64_t)bytes, pr = per;
+  uint32_t* sk = static_cast<uint32_t*>(sink);
+  void* args[] = {&s8, &nb, &pr, &sk};
+  const void* fn = depth == 4 ? reinterpret_cast<const void*>(diag_stream_kernel<4>)
+                   : depth == 8 ? reinterpret_cast<const void*>(diag_stream_kernel<8>)
+                                : reinterpret_cast<const void*>(diag_stream_kernel<16>);
+  g_counts[CNT_DIAG]++;
+  return launch(fn, dim3((unsigned)blocks), dim3(512), 0, stream, args);
 }
 
 fp8bs_status fp8bs_diag_copy(const void* src, void* dst, size_t bytes, void* stream) {

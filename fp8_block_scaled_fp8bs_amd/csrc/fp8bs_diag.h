@@ -1,5 +1,5 @@
-// Bandwidth reference kernels: a streaming read and a plain copy, launched
-// with the same 16-byte-per-lane access width as the GEMM's weight stream.
+// Bandwidth reference kernels: streaming reads and a plain copy, with the
+// same 16-byte-per-lane access width as the GEMM's weight stream.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -23,6 +23,47 @@ __global__ __launch_bounds__(256) void diag_read_kernel(const uint4* __restrict_
   for (; i < n16; i += stride) {
     const uint4 a = src[i];
     acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  if (acc == 0x9E3779B9u) sink[threadIdx.x & 3] = acc;
+}
+
+// Streaming-read ceiling: the read pattern a weight stream would use at
+// best. Workgroup b (512 threads) reads the contiguous range
+// [b * per, (b + 1) * per) with non-temporal 16-byte buffer loads: one
+// instruction covers 1 KB per wave, 8 KB per workgroup, and two rounds of U
+// loads per lane stay in flight (the second round is requested before the
+// first is consumed). Loads past the range return zeros from the buffer
+// bounds check without touching memory. The XOR of everything read is
+// stored only if it equals a value no real input produces in practice.
+template <int U>
+__global__ __launch_bounds__(512) void diag_stream_kernel(const uint8_t* __restrict__ src,
+                                                          int64_t bytes, int64_t per,
+                                                          uint32_t* __restrict__ sink) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const int64_t beg = (int64_t)blockIdx.x * per;
+  if (beg >= bytes) return;
+  const int64_t len = bytes - beg < per ? bytes - beg : per;
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(src + beg), (short)0, (int)len, 0x00020000);
+  constexpr uint32_t step = 512u * 16u * U;
+  const int rounds = (int)((len + step - 1) / step);
+  uint32_t off = threadIdx.x * 16u;
+  u32x4 a[U], b[U];
+  uint32_t acc = 0;
+#pragma unroll
+  for (int u = 0; u < U; ++u) a[u] = __builtin_amdgcn_raw_buffer_load_b128(r, off + u * 8192u, 0, 2);
+  for (int i = 0; i < rounds; i += 2) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      b[u] = __builtin_amdgcn_raw_buffer_load_b128(r, off + step + u * 8192u, 0, 2);
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= a[u].x ^ a[u].y ^ a[u].z ^ a[u].w;
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      a[u] = __builtin_amdgcn_raw_buffer_load_b128(r, off + 2 * step + u * 8192u, 0, 2);
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= b[u].x ^ b[u].y ^ b[u].z ^ b[u].w;
+    off += 2 * step;
   }
   if (acc == 0x9E3779B9u) sink[threadIdx.x & 3] = acc;
 }

@@ -5,13 +5,14 @@
 #include <vector>
 
 #include "fp8bs_gemm.h"
+#include "fp8bs_streamk.h"
 
 namespace fp8bs {
 
 struct KernelEntry {
   int path;    // 1 = MFMA grid, 2 = DOT grid, 3 = MFMA row range (one workgroup per CU),
                // 4 = MFMA streaming row range, 5 = prefill-size tiled MFMA GEMM,
-               // 6 = MFMA row range with register-resident activations
+               // 6 = MFMA row range with register-resident activations, 7 = stream-K
   int mt;      // MFMA: 16-row activation tiles (1: m <= 16, 2: m <= 32); DOT: max m
   int tn;      // MFMA: 16-row weight tiles per wave; DOT: 8-row groups per wave
   int wn, wk, d;
@@ -129,3 +130,15 @@ struct KernelRegistrar {
   {6, 2, PRE, 1, WK, NJ, 1, gemm_rows_reg_kernel<2, WK, NJ, PRE, true, false, true>, 0, 1},  \
   {6, 1, PRE, 1, WK, NJ, 0, gemm_rows_reg_kernel<1, WK, NJ, PRE, false, false, true>, 0, 1}, \
   {6, 2, PRE, 1, WK, NJ, 0, gemm_rows_reg_kernel<2, WK, NJ, PRE, false, false, true>, 0, 1},
+
+// Stream-K kernel: (streaming waves, tiles in flight per wave, of which
+// requested before the activation cast), both weight layouts.
+#define FP8BS_STREAMK_ENTRY(WK, D, PRE)                                                   \
+  {7, 1, PRE, 1, WK, D, 1, gemm_streamk_kernel<1, WK, D, PRE, true, false>, 0, 0},        \
+  {7, 2, PRE, 1, WK, D, 1, gemm_streamk_kernel<2, WK, D, PRE, true, false>, 0, 0},        \
+  {7, 1, PRE, 1, WK, D, 0, gemm_streamk_kernel<1, WK, D, PRE, false, false>, 0, 0},       \
+  {7, 2, PRE, 1, WK, D, 0, gemm_streamk_kernel<2, WK, D, PRE, false, false>, 0, 0},       \
+  {7, 1, PRE, 1, WK, D, 1, gemm_streamk_kernel<1, WK, D, PRE, true, true>, 0, 1},         \
+  {7, 2, PRE, 1, WK, D, 1, gemm_streamk_kernel<2, WK, D, PRE, true, true>, 0, 1},         \
+  {7, 1, PRE, 1, WK, D, 0, gemm_streamk_kernel<1, WK, D, PRE, false, true>, 0, 1},        \
+  {7, 2, PRE, 1, WK, D, 0, gemm_streamk_kernel<2, WK, D, PRE, false, true>, 0, 1},

@@ -143,7 +143,8 @@ enum {
   FP8BS_PATH_MFMA_ROWS = 3,
   FP8BS_PATH_MFMA_STREAM = 4,
   FP8BS_PATH_PREFILL = 5,
-  FP8BS_PATH_MFMA_ROWS_REG = 6
+  FP8BS_PATH_MFMA_ROWS_REG = 6,
+  FP8BS_PATH_MFMA_STREAMK = 7
 };
 enum { FP8BS_REDUCE_KERNEL = 0, FP8BS_REDUCE_LAST_ARRIVER = 1 };
 enum { FP8BS_EPILOGUE_SEPARATE = 0, FP8BS_EPILOGUE_IN_GEMM = 1 };
@@ -169,7 +170,18 @@ enum { FP8BS_LAYOUT_ROWS = 0, FP8BS_LAYOUT_TILES = 1 };
  *             number of K blocks per wave and k / 128 must not exceed
  *             waves_k * depth; tiles_n gives how many weight blocks are
  *             requested before the cast; waves_n and split_k must be 1).
- *             Paths 1-4 and 6 take m <= 32.
+ *             MFMA_STREAMK (stream-K: 256 workgroups, one per compute unit
+ *             of a full MI355X, each streaming an equal share of the
+ *             (16-row tile, K block) units in one launch; K is cut into
+ *             split_k chunks (split_k divides k/128; with split_k > 1 every
+ *             workgroup must get whole cells of one chunk); tiles that the
+ *             share cuts into pieces are summed in a fixed order by the
+ *             workgroup completing them, found with one 64-bit arrival
+ *             counter per tile in the workspace; waves_k streaming waves
+ *             plus one output wave per workgroup, depth tiles in flight per
+ *             wave, tiles_n of them requested before the activation cast;
+ *             waves_n must be 1; needs n*k < 2^31 and m <= 32).
+ *             Paths 1-4, 6 and 7 take m <= 32.
  *   tiles_n   MFMA: 16-row tiles per wave (1, 2, 4); DOT: 8-row groups per wave (1, 2, 4)
  *   waves_n   waves side by side along N in one workgroup (1, 2, 4)
  *   waves_k   waves splitting a workgroup's K range (1, 2, 4, 8); their
@@ -221,6 +233,15 @@ fp8bs_status fp8bs_gemm_select_config(int64_t m, int64_t n, int64_t k,
 /* Workspace bytes a given configuration needs.                              */
 size_t fp8bs_gemm_config_workspace_bytes(const fp8bs_gemm_config* cfg,
                                          int64_t m, int64_t n, int64_t k);
+
+/* Self-check of the stream-K work partition (path MFMA_STREAMK) for an
+ * n x k weight cut into `split` K chunks over `workgroups` workgroups, run on
+ * the host with the partition code the kernel runs: 0 when every (16-row
+ * tile, K block) unit is computed exactly once, each workgroup stays in one
+ * K chunk, and every tile's pieces are listed in K order in distinct
+ * workspace slots; 1 when the partition is not one the kernel supports;
+ * another value names the first inconsistency found. No GPU is involved.  */
+int32_t fp8bs_streamk_plan_check(int64_t n, int64_t k, int32_t split, int32_t workgroups);
 
 /* fp8bs_gemm / fp8bs_gemm_q with an explicit configuration (cfg != NULL).
  * x_bf16 != NULL selects the fused cast; otherwise x_fp8 and x_scale are
@@ -379,6 +400,15 @@ const char* fp8bs_build_info(void);
  * four 16-byte loads per lane, at most 16 per CU).                          */
 fp8bs_status fp8bs_diag_read(const void* src, size_t bytes, void* sink, int32_t blocks,
                              void* stream);
+
+/* Streaming-read ceiling over `bytes` bytes (multiple of 16, 16-byte
+ * aligned): `blocks` workgroups of 512 threads each read one contiguous
+ * range of about bytes/blocks with non-temporal 16-byte loads, 2 * depth
+ * loads per lane in flight (depth 4, 8 or 16). The plain read a weight
+ * stream could reach at best at this size; sink as for fp8bs_diag_read.
+ * bytes/blocks must stay below about 2^31.                                  */
+fp8bs_status fp8bs_diag_stream(const void* src, size_t bytes, void* sink, int32_t blocks,
+                               int32_t depth, void* stream);
 
 /* Plain copy of `bytes` bytes (multiple of 16, both 16-byte aligned).       */
 fp8bs_status fp8bs_diag_copy(const void* src, void* dst, size_t bytes, void* stream);
