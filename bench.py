@@ -192,14 +192,25 @@ def step_mix(args, fp8bs, dev) -> int:
         stream.wait_stream(cap)
         g.replay()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        reps = max(1, args.steps // 40)
-        e0.record(stream)
+        reps = max(3, args.steps // 40)
+        graph_us, eager_us = [], []
         for _ in range(reps):
+            # the same 256 GEMMs as one graph replay, then as 256 stream
+            # launches from the host (eager), each timed on the stream
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
             g.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / reps
+            e1.record(stream)
+            torch.cuda.synchronize()
+            graph_us.append(e0.elapsed_time(e1) * 1e3)
+            e0.record(stream)
+            one_step()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            eager_us.append(e0.elapsed_time(e1) * 1e3)
+        us = sorted(graph_us)[len(graph_us) // 2]
+        us_eager = sorted(eager_us)[len(eager_us) // 2]
         by_shape = {name: order.count(name) * WORKLOADS[name].algorithmic_bytes(m) for name in STEP_SHAPES}
         total = sum(by_shape.values())
         print(json.dumps({
@@ -207,8 +218,13 @@ def step_mix(args, fp8bs, dev) -> int:
             "counts": {name: order.count(name) for name in STEP_SHAPES},
             "us_per_step": round(us, 1), "algorithmic_bytes_per_step": total,
             "GBps": round(total / (us * 1e3), 1), "pct_of_8TBps": round(100 * total / (us * 1e3) / HBM_PEAK_GBPS, 2),
+            "eager_us_per_step": round(us_eager, 1),
+            "graph_saves_us_per_step": round(us_eager - us, 1),
+            "graph_saves_pct": round(100 * (us_eager - us) / us_eager, 2),
+            "eager_gap_us_per_launch": round((us_eager - us) / len(order), 3),
             "bytes_by_shape": by_shape, "replays": reps,
-            "timing": "one captured HIP graph of the 256-GEMM step, replayed"}), flush=True)
+            "timing": "median over replays: one captured HIP graph of the 256-GEMM step, "
+                      "and the same 256 calls launched eagerly from the host"}), flush=True)
         del xs, ys, workspace, g
     return 0
 
@@ -448,6 +464,73 @@ def mlp_pair(args, fp8bs, dev) -> int:
     return 0
 
 
+def _find_csv(root: str, suffix: str) -> list:
+    out = []
+    for d, _, files in os.walk(root):
+        out += [os.path.join(d, f) for f in files if f.endswith(suffix)]
+    return sorted(out)
+
+
+def _pct(v: list, q: float) -> float:
+    v = sorted(v)
+    return v[min(len(v) - 1, max(0, int(round(q * (len(v) - 1)))))]
+
+
+def summarize_trace(root: str, last: int) -> int:
+    """Print a markdown summary of a rocprofv3 --kernel-trace CSV directory:
+    per kernel, all dispatches (calls, mean, min, max) and the last `last`
+    dispatches (median, p10, p90), in ns."""
+    import csv
+    files = _find_csv(root, "kernel_trace.csv")
+    if not files:
+        print(f"no kernel_trace.csv under {root}", file=sys.stderr)
+        return 1
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    by = {}
+    for r in rows:
+        by.setdefault(r["Kernel_Name"], []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    print("| kernel | calls | mean ns | min ns | max ns |")
+    print("|---|---|---|---|---|")
+    for k, v in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+        print(f"| `{k[:110]}` | {len(v)} | {sum(v) / len(v):.0f} | {min(v)} | {max(v)} |")
+    print()
+    for k, v in by.items():
+        if "fp8bs::" in k and ("gemm" in k or "splitk" in k or "swiglu" in k or "diag_stream" in k):
+            t = v[-last:]
+            print(f"- `{k[:110]}`: last {len(t)} dispatches: median {_pct(t, 0.5):.0f} ns, "
+                  f"p10 {_pct(t, 0.1):.0f} ns, p90 {_pct(t, 0.9):.0f} ns, mean {sum(t) / len(t):.0f} ns")
+    return 0
+
+
+def summarize_pmc(root: str, counter: str) -> int:
+    """Print per-kernel medians (over dispatches) of one rocprofv3 --pmc
+    counter from a counter_collection CSV directory."""
+    import csv
+    files = _find_csv(root, "counter_collection.csv")
+    if not files:
+        print(f"no counter_collection.csv under {root}", file=sys.stderr)
+        return 1
+    per = {}
+    for f in files:
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r.get("Counter_Name") != counter:
+                    continue
+                key = (r["Kernel_Name"], r.get("Dispatch_Id", r.get("Correlation_Id", "")))
+                per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    by = {}
+    for (k, _), v in per.items():
+        by.setdefault(k, []).append(v)
+    for k, v in sorted(by.items(), key=lambda kv: -len(kv[1])):
+        print(f"- `{k[:110]}`: {counter} median {_pct(v, 0.5):.2f} over {len(v)} dispatches "
+              f"(min {min(v):.2f}, max {max(v):.2f})")
+    return 0
+
+
 MFMA_FP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 matrix peak
 
 
@@ -565,7 +648,19 @@ def main() -> int:
     ap.add_argument("--mlp-swiglu", action="store_true",
                     help="MLP up/gate projection with the SwiGLU epilogue at every M; "
                          "prints one JSON line per M")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="print a summary of a rocprofv3 --kernel-trace CSV directory and exit")
+    ap.add_argument("--summarize-pmc", metavar="DIR",
+                    help="print per-kernel medians of --counter from a rocprofv3 --pmc directory")
+    ap.add_argument("--counter", default="FETCH_SIZE")
+    ap.add_argument("--last", type=int, default=200,
+                    help="dispatches per kernel counted as the timed ones in --summarize-trace")
     args = ap.parse_args()
+
+    if args.summarize_trace:
+        return summarize_trace(args.summarize_trace, args.last)
+    if args.summarize_pmc:
+        return summarize_pmc(args.summarize_pmc, args.counter)
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -646,9 +741,12 @@ def main() -> int:
     print(f"# pool {pool_n} weights ({pool_n * code_bytes / 2**30:.2f} GiB), config {cfg}",
           file=sys.stderr, flush=True)
 
+    calls = [0]
+
     def step(i):
         wq, wsc = pool[i % pool_n]
         gemm(x, wq, wsc, out=y, workspace=workspace)
+        calls[0] += 1
 
     launches0 = fp8bs.launch_count("gemm_mfma") + fp8bs.launch_count("gemm_dot")
     for i in range(args.warmup):
@@ -667,69 +765,63 @@ def main() -> int:
     eager_ms = e0.elapsed_time(e1) / args.steps
 
     # --- graph: the same K steps captured once and replayed ------------------
-    # The timed graph (exactly K steps) is launched right behind an untimed
-    # lead graph of at least LEAD steps, with no synchronization between
-    # them, so the timed region starts when the lead graph's last kernel ends
-    # and holds the K GEMMs back to back: the graph launch latency stays
-    # outside it, whatever K is.
+    # One graph holds LEAD untimed steps, a timestamp kernel, exactly the K
+    # timed steps and a second timestamp kernel; the two read the GPU's
+    # constant-rate wall clock when they run. The timed region therefore
+    # starts while the GPU is already busy and holds the K GEMMs back to
+    # back: the graph launch latency stays outside it, whatever K is.
     graph_ms = None
     spread = None
     LEAD = 200
+    stamps = torch.zeros(2, dtype=torch.int64, device=dev)
+    clock_hz = fp8bs.diag_timestamp_hz()
+    timing_note = f"two wall-clock timestamp kernels inside one graph, after {LEAD}+ lead steps"
 
-    def capture(fn, count):
+    def capture(fn, count, lead=0):
         g = torch.cuda.CUDAGraph()
         cap = torch.cuda.Stream()
         cap.wait_stream(stream)
         with torch.cuda.stream(cap):
             with torch.cuda.graph(g, stream=cap):
+                for i in range(lead):
+                    fn(count + i)
+                fp8bs.diag_timestamp(stamps[0:1])
                 for i in range(count):
                     fn(i)
+                fp8bs.diag_timestamp(stamps[1:2])
         stream.wait_stream(cap)
         return g
 
-    def timed_replay(g_lead, g):
-        g_lead.replay()
-        torch.cuda.synchronize()
-        g_lead.replay()
-        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0.record(stream)
+    def timed_graph(fn, count):
+        """Per-call ms of `count` back-to-back calls, and a function that
+        replays the graph once more and returns the next per-call time."""
+        g = capture(fn, count, lead=max(LEAD, count))
         g.replay()
-        t1.record(stream)
         torch.cuda.synchronize()
-        return t0.elapsed_time(t1)
+
+        def again():
+            g.replay()
+            torch.cuda.synchronize()
+            t = stamps.cpu().tolist()
+            return (t[1] - t[0]) / clock_hz * 1e3 / count
+        return again(), again
 
     if not args.eager_only:
-        g_lead = capture(lambda i: step(args.steps + i), max(LEAD, args.steps))
-        g = capture(step, args.steps)
-        g.replay()  # warm replay
-        torch.cuda.synchronize()
-        graph_ms = timed_replay(g_lead, g) / args.steps
-        # spread: 20 more replays of the K-step graph, each timed on its own
-        # (events back to back, the lead graph first), per-GEMM time of each
-        per = []
-        g_lead.replay()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(21)]
-        ev[0].record(stream)
-        for r in range(20):
-            g.replay()
-            ev[r + 1].record(stream)
-        torch.cuda.synchronize()
-        per = sorted(ev[r].elapsed_time(ev[r + 1]) * 1e3 / args.steps for r in range(20))
+        graph_ms, again = timed_graph(step, args.steps)
+        # spread: 20 more replays of the same graph, each window timed alone
+        per = sorted(again() * 1e3 for _ in range(20))
         spread = {"replays": 20, "gemms_per_replay": args.steps,
                   "us_per_gemm_p10": round(per[2], 3), "us_per_gemm_median": round(per[10], 3),
                   "us_per_gemm_p90": round(per[18], 3)}
-        # the same measurement on a 400-step graph, as a check that the
+        # the same measurement with 400 timed steps, as a check that the
         # per-GEMM time does not depend on K
-        g400 = capture(step, 400)
-        g400.replay()
-        torch.cuda.synchronize()
-        spread["us_per_gemm_400_step_graph"] = round(timed_replay(g_lead, g400) * 1e3 / 400, 3)
-        del g400
+        t400, _ = timed_graph(step, 400)
+        spread["us_per_gemm_400_steps"] = round(t400 * 1e3, 3)
 
     launches = fp8bs.launch_count("gemm_mfma") + fp8bs.launch_count("gemm_dot") - launches0
-    # host launch calls: warm-up, eager steps, and the captures (replays make none)
-    graph_launches = 0 if args.eager_only else max(LEAD, args.steps) + args.steps + 400
-    expected = args.warmup + args.steps + graph_launches
+    # every host-side GEMM call (warm-up, eager steps, graph captures; replays
+    # make none) must have launched the GEMM kernel once
+    expected = calls[0]
     if launches != expected:
         print(f"kernel launch count {launches} != expected {expected}", file=sys.stderr)
         return 1
@@ -747,17 +839,13 @@ def main() -> int:
     sink = torch.zeros(4, dtype=torch.int32, device=dev)
     ceiling = {}
     if not args.eager_only:
-        for blocks, depth in ((256, 4), (256, 8), (256, 16), (512, 8)):
+        for blocks, depth in ((256, 4), (256, 8), (256, 16), (512, 4)):
             def rd(i, blocks=blocks, depth=depth):
                 fp8bs.diag_stream(pool[i % pool_n][0], sink, blocks=blocks, depth=depth)
-            gl = capture(lambda i: rd(args.steps + i), max(LEAD, args.steps))
-            gr = capture(rd, args.steps)
-            gr.replay()
-            torch.cuda.synchronize()
-            us_r = timed_replay(gl, gr) * 1e3 / args.steps
+            ms_r, _ = timed_graph(rd, args.steps)
+            us_r = ms_r * 1e3
             ceiling[f"{blocks}x512_depth{depth}"] = {"us": round(us_r, 3),
                                                      "GBps": round(code_bytes / (us_r * 1e3), 1)}
-            del gl, gr
     best = max(ceiling.values(), key=lambda v: v["GBps"]) if ceiling else None
 
     # --- library reference: the same product in bf16 through torch (hipBLASLt)
@@ -799,7 +887,8 @@ def main() -> int:
                        "split_k": cfg.split_k,
                        "launches_per_gemm": 2 if cfg.split_k > 1 and cfg.reduce == 0 else 1},
             "weight_layout": layout,
-            "timing": "hip graph of the steps, replayed" if graph_ms is not None else "stream launches",
+            "timing": (f"hip graph replay, K steps timed with {timing_note}" if graph_ms is not None
+                       else "stream launches"),
         },
         "us_per_gemm": round(us, 3),
         "pct_of_8TBps": round(100 * gbps / HBM_PEAK_GBPS, 2),
@@ -808,7 +897,7 @@ def main() -> int:
         "stream_read_ceiling": ({"bytes": code_bytes, "best_us": best["us"], "best_GBps": best["GBps"],
                                  "gemm_frac_of_ceiling": round(best["us"] / us, 4),
                                  "configs": ceiling,
-                                 "timing": "graph of K launches behind a lead graph, as the GEMM"}
+                                 "timing": "K launches timed exactly like the GEMM steps"}
                                 if best else None),
         "bf16_library_reference": (dict(lib_ref, fp8_speedup=round(lib_ref["us_per_gemm"] / us, 2))
                                    if lib_ref else None),

@@ -23,7 +23,7 @@ __all__ = [
     "swiglu_quant", "gemm_swiglu", "gemm_swiglu_ex", "swiglu_select_config",
     "swiglu_workspace_bytes",
     "encode_e4m3", "launch_count", "build_info", "diag_read", "diag_copy", "diag_stream",
-    "streamk_plan_check", "PATH_MFMA_STREAMK",
+    "streamk_plan_check", "PATH_MFMA_STREAMK", "diag_timestamp", "diag_timestamp_hz",
     "hip_runtime_mappings", "PATH_MFMA", "PATH_DOT", "REDUCE_KERNEL",
     "REDUCE_LAST_ARRIVER", "EPILOGUE_SEPARATE", "EPILOGUE_IN_GEMM", "LAYOUT_ROWS",
     "LAYOUT_TILES", "COUNTER",
@@ -122,7 +122,9 @@ def load() -> ctypes.CDLL:
         "fp8bs_diag_read": (i32, [vp, sz, vp, i32, vp]),
         "fp8bs_diag_copy": (i32, [vp, vp, sz, vp]),
         "fp8bs_diag_stream": (i32, [vp, sz, vp, i32, i32, vp]),
-        "fp8bs_streamk_plan_check": (i32, [i64, i64, i32, i32]),
+        "fp8bs_diag_timestamp": (i32, [vp, vp]),
+        "fp8bs_diag_timestamp_hz": (ctypes.c_uint64, []),
+        "fp8bs_streamk_plan_check": (i32, [i64, i64, i32, i32, i32]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -442,10 +444,21 @@ def diag_stream(t: torch.Tensor, sink: torch.Tensor, blocks: int = 256, depth: i
                                     _stream(stream)))
 
 
-def streamk_plan_check(n: int, k: int, split: int, workgroups: int = 256) -> int:
+def diag_timestamp(out: torch.Tensor, stream=None) -> None:
+    """Write the GPU wall clock into out (an int64 tensor of at least one
+    element) when the launch runs."""
+    _check(load().fp8bs_diag_timestamp(out.data_ptr(), _stream(stream)))
+
+
+def diag_timestamp_hz() -> int:
+    return int(load().fp8bs_diag_timestamp_hz())
+
+
+def streamk_plan_check(n: int, k: int, split: int, workgroups: int = 256,
+                       whole: bool = False) -> int:
     """Host-side self-check of the stream-K work partition (0 = consistent,
     1 = not a supported partition, other values: the first inconsistency)."""
-    return int(load().fp8bs_streamk_plan_check(n, k, split, workgroups))
+    return int(load().fp8bs_streamk_plan_check(n, k, split, workgroups, int(whole)))
 
 
 def diag_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:

@@ -72,17 +72,24 @@ inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintp
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
 // Kernels that take more than 64 KB of dynamic LDS need the per-function
-// limit raised once per device (to the device maximum); a bit per device
-// records that it was done, so a launch pays for it only the first time.
+// limit raised once per device: to the device maximum less the kernel's
+// static LDS. A bit per device records that it was done, so a launch pays
+// for it only the first time.
 constexpr int kMaxKernels = 4096;
 std::atomic<uint64_t> g_lds_raised[kMaxKernels];
 
-fp8bs_status raise_lds_limit(const void* fn, int slot, const DeviceInfo& dev) {
+fp8bs_status raise_lds_limit(const void* fn, int slot, const DeviceInfo& dev, size_t need) {
   if (slot < 0 || slot >= kMaxKernels) return FP8BS_ERR_LAUNCH;
   const uint64_t bit = uint64_t(1) << dev.index;
   if (g_lds_raised[slot].load(std::memory_order_acquire) & bit) return FP8BS_OK;
-  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, dev.max_lds) !=
-      hipSuccess) {
+  hipFuncAttributes attr;
+  if (hipFuncGetAttributes(&attr, fn) != hipSuccess) {
+    (void)hipGetLastError();
+    return FP8BS_ERR_LAUNCH;
+  }
+  const int limit = dev.max_lds - (int)attr.sharedSizeBytes;
+  if (limit < (int)need) return FP8BS_ERR_CONFIG;
+  if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, limit) != hipSuccess) {
     (void)hipGetLastError();
     return FP8BS_ERR_LAUNCH;
   }
@@ -100,6 +107,7 @@ fp8bs_status launch(const void* fn, dim3 grid, dim3 block, size_t lds, void* str
 }
 
 // ----------------------------------------------------------- GEMM configs ---
+
 
 }  // namespace
 
@@ -164,11 +172,13 @@ const KernelEntry* find_kernel(const fp8bs_gemm_config& c, int m, bool fused,
   } else {
     return nullptr;
   }
-  const bool rows = is_row_range(c.path);  // waves_n unused
+  // waves_n is unused by the row-range paths and a partition mode of stream-K
+  const bool rows = is_row_range(c.path);
+  const bool any_wn = rows || c.path == FP8BS_PATH_MFMA_STREAMK;
+  const int variant = rows ? (swiglu ? 1 : (c.split_k > 1 ? 2 : 0)) : 0;
   for (const KernelEntry& e : kernel_registry())
-    if (e.path == c.path && e.mt == mt && e.tn == c.tiles_n && (rows || e.wn == c.waves_n) &&
-        e.wk == c.waves_k && e.d == c.depth && e.fused == (int)fused &&
-        e.variant == (rows ? (swiglu ? 1 : (c.split_k > 1 ? 2 : 0)) : 0) &&
+    if (e.path == c.path && e.mt == mt && e.tn == c.tiles_n && (any_wn || e.wn == c.waves_n) &&
+        e.wk == c.waves_k && e.d == c.depth && e.fused == (int)fused && e.variant == variant &&
         e.layout == c.weight_layout)
       return &e;
   return nullptr;
@@ -240,13 +250,14 @@ constexpr size_t kLdsLimit = 160 * 1024;  // one workgroup per CU at most
 
 // The stream-K plan of a configuration (workgroups: the table's compute units).
 SkPlan streamk_plan(const fp8bs_gemm_config& c, int64_t n, int64_t k) {
-  return sk_plan((int)(n / 16), (int)(k / BLK), c.split_k, kTableCUs);
+  return sk_plan((int)(n / 16), (int)(k / BLK), c.split_k, kTableCUs, c.waves_n == 2 ? 1 : 0);
 }
 
 // Whether a stream-K configuration can run this shape: a supported plan,
 // weight offsets within a 31-bit buffer range, one workgroup per CU.
 bool streamk_fits(const fp8bs_gemm_config& c, int64_t m, int64_t n, int64_t k) {
-  if (c.waves_n != 1 || c.waves_k < 1 || c.waves_k > 15 || c.split_k < 1) return false;
+  if (c.waves_n < 1 || c.waves_n > 2 || c.waves_k < 1 || c.waves_k > 15 || c.split_k < 1)
+    return false;
   if (m > kMaxDecodeM || n * k >= ((int64_t)1 << 31)) return false;
   return sk_plan_ok(streamk_plan(c, n, k));
 }
@@ -601,7 +612,7 @@ fp8bs_status gemm_impl(bool fused, const void* x_bf16, const uint8_t* x_fp8,
   if (lds > (size_t)dev.max_lds) return FP8BS_ERR_CONFIG;
   if (lds > 64 * 1024) {
     const fp8bs_status ls = raise_lds_limit(reinterpret_cast<const void*>(ke->fn),
-                                            (int)(ke - kernel_registry().data()), dev);
+                                            (int)(ke - kernel_registry().data()), dev, lds);
     if (ls != FP8BS_OK) return ls;
   }
 
@@ -620,6 +631,8 @@ fp8bs_status gemm_impl(bool fused, const void* x_bf16, const uint8_t* x_fp8,
   p.hq = h_fp8;
   p.hs = h_scale;
   p.epoch = g_epoch.fetch_add(1) & ((uint64_t(1) << 56) - 1);
+  p.sk_whole = streamk && c.waves_n == 2 ? 1 : 0;
+  p.rows_per_wg = 0;
   p.m = (int)m;
   p.n = (int)n;
   p.k = (int)k;
@@ -893,10 +906,11 @@ fp8bs_status fp8bs_encode_e4m3(const float* in, int64_t count, uint8_t* out, int
                 dim3((unsigned)(((count + 3) / 4 + 255) / 256)), dim3(256), 0, stream, args);
 }
 
-int32_t fp8bs_streamk_plan_check(int64_t n, int64_t k, int32_t split, int32_t workgroups) {
+int32_t fp8bs_streamk_plan_check(int64_t n, int64_t k, int32_t split, int32_t workgroups,
+                                 int32_t whole) {
   if (n <= 0 || k <= 0 || n % BLK || k % BLK || workgroups < 1 || split < 1) return 1;
-  if (n / 16 > 0x7FFFFFFF || k / BLK > 0x7FFFFFFF) return 1;
-  const SkPlan q = sk_plan((int)(n / 16), (int)(k / BLK), split, workgroups);
+  if (n / 16 > 0x7FFFFFFF || k / BLK > 0x7FFFFFFF || whole < 0 || whole > 1) return 1;
+  const SkPlan q = sk_plan((int)(n / 16), (int)(k / BLK), split, workgroups, whole);
   if (!sk_plan_ok(q)) return 1;
   const int64_t units = (int64_t)q.ntiles * q.kbn;
   if (units > ((int64_t)1 << 28)) return 1;  // keep the check's own memory small
@@ -1018,6 +1032,28 @@ fp8bs_status fp8bs_diag_stream(const void* src, size_t bytes, void* sink, int32_
                                 : reinterpret_cast<const void*>(diag_stream_kernel<16>);
   g_counts[CNT_DIAG]++;
   return launch(fn, dim3((unsigned)blocks), dim3(512), 0, stream, args);
+}
+
+fp8bs_status fp8bs_diag_timestamp(uint64_t* out, void* stream) {
+  if (!out) return FP8BS_ERR_NULL;
+  if (!aligned(out, 8)) return FP8BS_ERR_ALIGN;
+  const fp8bs_status st = current_device(nullptr);
+  if (st != FP8BS_OK) return st;
+  unsigned long long* o = reinterpret_cast<unsigned long long*>(out);
+  void* args[] = {&o};
+  g_counts[CNT_DIAG]++;
+  return launch(reinterpret_cast<const void*>(diag_timestamp_kernel), dim3(1), dim3(64), 0,
+                stream, args);
+}
+
+uint64_t fp8bs_diag_timestamp_hz(void) {
+  int dev = -1, khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  return (uint64_t)khz * 1000u;
 }
 
 fp8bs_status fp8bs_diag_copy(const void* src, void* dst, size_t bytes, void* stream) {

@@ -50,6 +50,7 @@ struct GemmParams {
   int rows_per_wg;      // row-range kernel: output columns per workgroup (multiple of 4)
   uint8_t* hq;          // SwiGLU epilogue: E4M3 codes [m][n/2]
   float* hs;            // SwiGLU epilogue: fp32 scales [m][n/256]
+  int sk_whole;         // stream-K kernel: whole-cell partition
 };
 
 // LDS layout of a workgroup:

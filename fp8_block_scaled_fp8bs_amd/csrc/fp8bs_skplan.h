@@ -16,6 +16,11 @@
 //   * Stream-K part: the remaining C - R*P cells, laid end to end as units,
 //     are split evenly: workgroup w takes units [Usk*w/P, Usk*(w+1)/P).
 //     A cell of this part may be shared by several workgroups.
+//   * Whole-cell mode (S = 1 only): no stream-K part; workgroup w takes the
+//     whole cells [C*w/P, C*(w+1)/P), so the counts differ by at most one
+//     cell and no tile is ever cut. Where the cells do not divide evenly, a
+//     few workgroups stream one more tile than the rest, in exchange for no
+//     hand-off between workgroups at all.
 //
 // Each maximal run of a workgroup's units inside one cell is a segment. The
 // fp32 sum of a segment is a "piece" of its tile's output. A tile whose only
@@ -48,10 +53,12 @@ struct SkPlan {
   int64_t C;    // cells
   int64_t Usk;  // units of the stream-K part
   int64_t dp_slots;  // workspace piece slots of data-parallel cells (S > 1)
+  int whole;         // whole-cell mode
 };
 
-FP8BS_HD inline SkPlan sk_plan(int ntiles, int kbn, int S, int P) {
+FP8BS_HD inline SkPlan sk_plan(int ntiles, int kbn, int S, int P, int whole = 0) {
   SkPlan q;
+  q.whole = whole;
   q.ntiles = ntiles;
   q.kbn = kbn;
   q.S = S;
@@ -59,9 +66,20 @@ FP8BS_HD inline SkPlan sk_plan(int ntiles, int kbn, int S, int P) {
   q.P = P;
   q.C = (int64_t)ntiles * S;
   q.R = P > 0 ? (int)(q.C / P) : 0;
-  q.Usk = (q.C - (int64_t)q.R * P) * q.kc;
+  q.Usk = whole ? 0 : (q.C - (int64_t)q.R * P) * q.kc;
   q.dp_slots = S > 1 ? (int64_t)q.R * P : 0;
   return q;
+}
+
+// Whole cells of workgroup w: [*c0, *c0 + count).
+FP8BS_HD inline int sk_cells(const SkPlan& q, int w, int* c0) {
+  if (q.whole) {
+    const int a = (int)(q.C * w / q.P), b = (int)(q.C * (w + 1) / q.P);
+    *c0 = a;
+    return b - a;
+  }
+  *c0 = w * q.R;
+  return q.R;
 }
 
 // First stream-K unit of workgroup w (w = P gives the end).
@@ -89,10 +107,14 @@ struct SkSegment {
 // first (their pieces reach the workspace early), then its whole cells.
 // Returns the number of stream-K segments in *nsk and the total count.
 FP8BS_HD inline int sk_segments(const SkPlan& q, int w, int* nsk) {
-  const int64_t ua = sk_begin(q, w), ub = sk_begin(q, w + 1);
-  const int n = ub > ua ? (int)((ub - 1) / q.kc - ua / q.kc + 1) : 0;
+  int n = 0;
+  if (q.Usk > 0) {
+    const int64_t ua = sk_begin(q, w), ub = sk_begin(q, w + 1);
+    n = ub > ua ? (int)((ub - 1) / q.kc - ua / q.kc + 1) : 0;
+  }
   *nsk = n;
-  return n + q.R;
+  int c0;
+  return n + sk_cells(q, w, &c0);
 }
 
 FP8BS_HD inline SkSegment sk_segment(const SkPlan& q, int w, int nsk, int i) {
@@ -110,7 +132,9 @@ FP8BS_HD inline SkSegment sk_segment(const SkPlan& q, int w, int nsk, int i) {
     s.slot = sk_slot(q, w, zz);
   } else {
     // C < 2^31 in a valid plan: 32-bit arithmetic
-    const int z = w * q.R + (i - nsk);
+    int c0;
+    sk_cells(q, w, &c0);
+    const int z = c0 + (i - nsk);
     s.tile = z % q.ntiles;
     s.chunk = z / q.ntiles;
     s.b0 = 0;
@@ -126,7 +150,7 @@ FP8BS_HD inline int sk_tile_pieces(const SkPlan& q, int t, int64_t* slots) {
   int np = 0;
   for (int c = 0; c < q.S; ++c) {
     const int64_t z = (int64_t)c * q.ntiles + t;
-    if (z < (int64_t)q.R * q.P) {
+    if (q.whole || z < (int64_t)q.R * q.P) {
       if (np < SK_MAXPIECES) slots[np] = q.S > 1 ? z : -1;  // S = 1: the whole tile, no slot
       ++np;
     } else {
@@ -156,7 +180,8 @@ FP8BS_HD inline int sk_chunk_of(const SkPlan& q, int w) {
 // SK_MAXPIECES pieces; at least one segment per workgroup.
 FP8BS_HD inline bool sk_plan_ok(const SkPlan& q) {
   if (q.S < 1 || q.P < 1 || q.kbn < 1 || q.ntiles < 1 || q.kbn % q.S) return false;
-  if (q.C >= ((int64_t)1 << 31)) return false;
+  if (q.C >= ((int64_t)1 << 31) || q.C * q.P >= ((int64_t)1 << 62)) return false;
+  if (q.whole) return q.S == 1 && q.C >= q.P;
   if (q.S > SK_MAXPIECES) return false;
   if (q.S > 1 && (q.Usk != 0 || q.R < 1 || q.ntiles % q.R)) return false;
   if (q.Usk > 0) {

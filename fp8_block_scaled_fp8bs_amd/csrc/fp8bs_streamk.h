@@ -22,17 +22,26 @@
 //     in wave order, and either writes the bf16 outputs (a tile with one
 //     piece) or stores the piece to the workspace and arrives on the tile's
 //     counter; the arrival that completes the count adds all the tile's
-//     pieces in plan order and writes the bf16 outputs. Its stores, fences
+//     pieces in plan order and writes the bf16 outputs. Its stores, waits
 //     and counter updates therefore never hold up the weight stream (the
 //     wait counter of a wave covers loads and stores alike).
 // Each workgroup computes its pieces first, so the cross-workgroup additions
 // happen while the rest of the weights stream in.
 //
-// Cross-workgroup ordering follows the HIP memory model: plain stores of a
-// piece, an agent-scope release fence, then the counter update; the last
-// arriver issues an agent-scope acquire fence before it reads the pieces.
-// The counter carries a per-launch epoch (see arrive()), so it needs no
-// initialization and is left at zero for graph replays.
+// Cross-workgroup hand-off (the protocol of the split-K helpers in
+// fp8bs_gemm.h): the 8 XCDs have separate L2 caches, so a piece is written
+// with device-coherent stores (agent-scope atomic stores, which write
+// through the writer's L2), the output wave waits until its own stores are
+// performed (on this architecture the vmcnt counter covers stores), and
+// only then arrives: an agent-scope integer read-modify-write on the tile's
+// counter. The arrival that completes the count reads the pieces with
+// device-coherent loads, which are not served from a stale line of its own
+// L2. No cache-wide write-back or invalidate is issued: with agent-scope
+// release/acquire fences around the arrival instead (an L2 write-back and
+// an L2 invalidate each time), this kernel took 18.5 us for the square
+// projection at m = 8 on MI355X, 2.4x the grid kernel, and 50 us for the
+// MLP down projection, whose workgroups arrive five times each. The counter carries a per-launch epoch (see arrive()), so it
+// needs no initialization and is left at zero for graph replays.
 #pragma once
 
 #include "fp8bs_gemm.h"
@@ -41,6 +50,29 @@
 namespace fp8bs {
 
 constexpr int SK_NBUF = 4;  // LDS partial-sum buffers between streaming and output waves
+
+// The hand-off between the waves of one workgroup goes through LDS only.
+// LDS performs each wave's operations in issue order, so a data write
+// issued before a counter update is visible to any wave that has read the
+// updated counter; the accesses only must not be reordered by the compiler
+// (a signal fence), and need no hardware wait. The counters are addressed
+// as LDS so that their atomics are LDS instructions: on a generic address
+// an atomic would also wait for the wave's outstanding weight loads.
+typedef __attribute__((address_space(3))) int lds_int;
+
+__device__ __forceinline__ void lds_signal_add(lds_int* c) {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void lds_signal_set(lds_int* c, int v) {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __hip_atomic_store(c, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void lds_wait_at_least(lds_int* c, int target) {
+  while (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target)
+    __builtin_amdgcn_s_sleep(1);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
 // Dynamic LDS: staged activations of one chunk (codes + scales), then
 // SK_NBUF buffers of WK wave partials.
@@ -53,6 +85,7 @@ __host__ __device__ inline int64_t sk_slot_count(const SkPlan& q) {
   return q.dp_slots + (int64_t)q.P * SK_MAXSK;
 }
 __host__ __device__ inline int64_t sk_workspace_bytes(const SkPlan& q, int mt) {
+  if (q.whole && q.S == 1) return 0;  // no tile is cut: no pieces, no counters
   return sk_slot_count(q) * mt * 1024 + (int64_t)q.ntiles * 8;
 }
 
@@ -65,13 +98,13 @@ struct SkCursor {
 
 template <int MT, int WK, int D, int PRE, bool FUSED, int CR, bool PK>
 __device__ __forceinline__ void gemm_streamk_body(const GemmParams& p, uint8_t* lds_all,
-                                                  int* s_arrived, int* s_consumed) {
+                                                  lds_int* s_arrived, lds_int* s_consumed) {
   constexpr int NT = 64 * (WK + 1);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int M = p.m;
-  const SkPlan q = sk_plan(p.n >> 4, p.kbn, p.split, (int)gridDim.x);
+  const SkPlan q = sk_plan(p.n >> 4, p.kbn, p.split, (int)gridDim.x, p.sk_whole);
   const int w = blockIdx.x;
   int nsk;
   const int nseg = sk_segments(q, w, &nsk);
@@ -170,8 +203,9 @@ __device__ __forceinline__ void gemm_streamk_body(const GemmParams& p, uint8_t* 
     // 4. stream: compute item i from slot i % D, then refill the slot
     SkCursor cc{0, 0, 0, 0, 0, 0, 0};
     seg_at(cc);
-    // items per wave: the stream-K segments, then R whole cells
-    int items = q.R * ((q.kc + WK - 1) / WK);
+    // items per wave: the stream-K segments, then the whole cells
+    int c0;
+    int items = sk_cells(q, w, &c0) * ((q.kc + WK - 1) / WK);
     for (int s = 0; s < nsk; ++s) {
       const SkSegment sg = sk_segment(q, w, nsk, s);
       items += (sg.b1 - sg.b0 + WK - 1) / WK;
@@ -210,19 +244,13 @@ __device__ __forceinline__ void gemm_streamk_body(const GemmParams& p, uint8_t* 
       if (cc.j == cc.nj - 1) {
         // end of segment cc.s: hand the partial to the output wave
         const int buf = cc.s % SK_NBUF;
-        if (cc.s >= SK_NBUF) {
-          while (__hip_atomic_load(s_consumed, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) <
-                 cc.s - SK_NBUF + 1)
-            __builtin_amdgcn_s_sleep(1);
-        }
+        if (cc.s >= SK_NBUF) lds_wait_at_least(s_consumed, cc.s - SK_NBUF + 1);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           red[((buf * WK + wk) * MT + mt) * 64 + lane] = acc[mt];
           acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        if (lane == 0)
-          __hip_atomic_fetch_add(&s_arrived[buf], 1, __ATOMIC_RELEASE,
-                                 __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (lane == 0) lds_signal_add(&s_arrived[buf]);
       }
       advance(cc);
     };
@@ -244,8 +272,6 @@ __device__ __forceinline__ void gemm_streamk_body(const GemmParams& p, uint8_t* 
   const int64_t nslots = sk_slot_count(q);
   float* pieces = p.part;
   uint64_t* counters = reinterpret_cast<uint64_t*>(pieces + nslots * MT * 256);
-  const __amdgpu_buffer_rsrc_t pr = __builtin_amdgcn_make_buffer_rsrc(
-      pieces, (short)0, (int)(nslots * MT * 1024), 0x00020000);
   auto store_out = [&](int tile, const f32x4 (&v)[MT]) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -259,17 +285,14 @@ __device__ __forceinline__ void gemm_streamk_body(const GemmParams& p, uint8_t* 
   for (int s = 0; s < nseg; ++s) {
     const int buf = s % SK_NBUF;
     const int target = WK * (s / SK_NBUF + 1);
-    while (__hip_atomic_load(&s_arrived[buf], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) <
-           target)
-      __builtin_amdgcn_s_sleep(1);
+    lds_wait_at_least(&s_arrived[buf], target);
     f32x4 v[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       v[mt] = red[((buf * WK) * MT + mt) * 64 + lane];
       for (int k = 1; k < WK; ++k) v[mt] += red[((buf * WK + k) * MT + mt) * 64 + lane];
     }
-    if (lane == 0)
-      __hip_atomic_store(s_consumed, s + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (lane == 0) lds_signal_set(s_consumed, s + 1);
     const SkSegment sg = sk_segment(q, w, nsk, s);
     int64_t slots[SK_MAXPIECES];
     const int np = sk_tile_pieces(q, sg.tile, slots);
@@ -277,32 +300,47 @@ __device__ __forceinline__ void gemm_streamk_body(const GemmParams& p, uint8_t* 
       store_out(sg.tile, v);
       continue;
     }
-    // a piece: to the workspace, then arrive on the tile's counter
+    // a piece: to the workspace with device-coherent stores, then arrive on
+    // the tile's counter once they are performed
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-      reinterpret_cast<f32x4*>(pieces)[(sg.slot * MT + mt) * 64 + lane] = v[mt];
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    for (int mt = 0; mt < MT; ++mt) {
+      float* dst = pieces + ((sg.slot * MT + mt) * 64 + lane) * 4;
+      store_coherent64(dst, (uint64_t)__float_as_uint(v[mt][0]) |
+                                ((uint64_t)__float_as_uint(v[mt][1]) << 32));
+      store_coherent64(dst + 2, (uint64_t)__float_as_uint(v[mt][2]) |
+                                    ((uint64_t)__float_as_uint(v[mt][3]) << 32));
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     int last = 0;
     if (lane == 0) last = arrive(counters + sg.tile, p.epoch, (uint64_t)np) ? 1 : 0;
     last = __builtin_amdgcn_readfirstlane(last);
     if (!last) continue;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    // every piece of the tile requested at once, then added in plan order
-    f32x4 pv[SK_MAXPIECES][MT];
+    // every piece of the tile requested at once (coherent loads; slots past
+    // the count read the first piece again and are not added), then added
+    // in plan order
+    uint64_t pv[SK_MAXPIECES][MT][2];
 #pragma unroll
     for (int i = 0; i < SK_MAXPIECES; ++i)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const uint32_t off = i < np ? (uint32_t)(((slots[i] * MT + mt) * 64 + lane) * 16) : BUF_OOB;
-        pv[i][mt] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(pr, off, 0, 0));
+        const float* src = pieces + (((i < np ? slots[i] : slots[0]) * MT + mt) * 64 + lane) * 4;
+        pv[i][mt][0] = load_coherent64(src);
+        pv[i][mt][1] = load_coherent64(src + 2);
       }
     f32x4 sum[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      sum[mt] = pv[0][mt];
 #pragma unroll
-      for (int i = 1; i < SK_MAXPIECES; ++i)
-        if (i < np) sum[mt] += pv[i][mt];
+      for (int i = 0; i < SK_MAXPIECES; ++i) {
+        const f32x4 e = {__uint_as_float((uint32_t)pv[i][mt][0]),
+                         __uint_as_float((uint32_t)(pv[i][mt][0] >> 32)),
+                         __uint_as_float((uint32_t)pv[i][mt][1]),
+                         __uint_as_float((uint32_t)(pv[i][mt][1] >> 32))};
+        if (i == 0)
+          sum[mt] = e;
+        else if (i < np)
+          sum[mt] += e;
+      }
     }
     store_out(sg.tile, sum);
   }
@@ -310,21 +348,16 @@ __device__ __forceinline__ void gemm_streamk_body(const GemmParams& p, uint8_t* 
 
 template <int MT, int WK, int D, int PRE, bool FUSED, bool PK>
 __global__ __launch_bounds__(64 * (WK + 1)) void gemm_streamk_kernel(GemmParams p) {
-  constexpr int NT = 64 * (WK + 1);
   extern __shared__ __align__(16) uint8_t lds_all[];
-  __shared__ int s_arrived[SK_NBUF];
-  __shared__ int s_consumed;
+  __shared__ int s_flags[SK_NBUF + 1];  // arrivals per buffer, then segments consumed
+  lds_int* s_arrived = (lds_int*)s_flags;
+  lds_int* s_consumed = s_arrived + SK_NBUF;
   if constexpr (FUSED) {
-    const SkPlan q = sk_plan(p.n >> 4, p.kbn, p.split, (int)gridDim.x);
-    const int rounds = act_rounds(q.kc * p.m * 4, NT);
-    if (rounds == 1)
-      gemm_streamk_body<MT, WK, D, PRE, true, 1, PK>(p, lds_all, s_arrived, &s_consumed);
-    else if (rounds == 2)
-      gemm_streamk_body<MT, WK, D, PRE, true, 2, PK>(p, lds_all, s_arrived, &s_consumed);
-    else
-      gemm_streamk_body<MT, WK, D, PRE, true, 3, PK>(p, lds_all, s_arrived, &s_consumed);
+    // one body with three activation-load rounds: the path is selected only
+    // explicitly, so it is not specialised per size like the table's kernels
+    gemm_streamk_body<MT, WK, D, PRE, true, 3, PK>(p, lds_all, s_arrived, s_consumed);
   } else {
-    gemm_streamk_body<MT, WK, D, PRE, false, 1, PK>(p, lds_all, s_arrived, &s_consumed);
+    gemm_streamk_body<MT, WK, D, PRE, false, 1, PK>(p, lds_all, s_arrived, s_consumed);
   }
 }
 

@@ -180,7 +180,10 @@ enum { FP8BS_LAYOUT_ROWS = 0, FP8BS_LAYOUT_TILES = 1 };
  *             counter per tile in the workspace; waves_k streaming waves
  *             plus one output wave per workgroup, depth tiles in flight per
  *             wave, tiles_n of them requested before the activation cast;
- *             waves_n must be 1; needs n*k < 2^31 and m <= 32).
+ *             waves_n selects the partition: 1 = equal runs of units, tiles
+ *             cut where needed; 2 = whole tiles only (split_k must be 1),
+ *             the workgroups' tile counts differing by at most one, no
+ *             workspace; needs n*k < 2^31 and m <= 32).
  *             Paths 1-4, 6 and 7 take m <= 32.
  *   tiles_n   MFMA: 16-row tiles per wave (1, 2, 4); DOT: 8-row groups per wave (1, 2, 4)
  *   waves_n   waves side by side along N in one workgroup (1, 2, 4)
@@ -235,13 +238,15 @@ size_t fp8bs_gemm_config_workspace_bytes(const fp8bs_gemm_config* cfg,
                                          int64_t m, int64_t n, int64_t k);
 
 /* Self-check of the stream-K work partition (path MFMA_STREAMK) for an
- * n x k weight cut into `split` K chunks over `workgroups` workgroups, run on
- * the host with the partition code the kernel runs: 0 when every (16-row
+ * n x k weight cut into `split` K chunks over `workgroups` workgroups
+ * (whole = 1: the whole-tile partition, waves_n = 2 in a configuration), run
+ * on the host with the partition code the kernel runs: 0 when every (16-row
  * tile, K block) unit is computed exactly once, each workgroup stays in one
  * K chunk, and every tile's pieces are listed in K order in distinct
  * workspace slots; 1 when the partition is not one the kernel supports;
  * another value names the first inconsistency found. No GPU is involved.  */
-int32_t fp8bs_streamk_plan_check(int64_t n, int64_t k, int32_t split, int32_t workgroups);
+int32_t fp8bs_streamk_plan_check(int64_t n, int64_t k, int32_t split, int32_t workgroups,
+                                 int32_t whole);
 
 /* fp8bs_gemm / fp8bs_gemm_q with an explicit configuration (cfg != NULL).
  * x_bf16 != NULL selects the fused cast; otherwise x_fp8 and x_scale are
@@ -409,6 +414,14 @@ fp8bs_status fp8bs_diag_read(const void* src, size_t bytes, void* sink, int32_t 
  * bytes/blocks must stay below about 2^31.                                  */
 fp8bs_status fp8bs_diag_stream(const void* src, size_t bytes, void* sink, int32_t blocks,
                                int32_t depth, void* stream);
+
+/* Writes the GPU's constant-rate wall-clock counter to out[0] (8-byte
+ * aligned device pointer) when the launch runs on `stream`: two of them
+ * around a run of kernels in a captured graph time exactly that run.
+ * fp8bs_diag_timestamp_hz gives the counter's rate for the current device
+ * (0 if it cannot be read).                                                */
+fp8bs_status fp8bs_diag_timestamp(uint64_t* out, void* stream);
+uint64_t fp8bs_diag_timestamp_hz(void);
 
 /* Plain copy of `bytes` bytes (multiple of 16, both 16-byte aligned).       */
 fp8bs_status fp8bs_diag_copy(const void* src, void* dst, size_t bytes, void* stream);

@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 TOL = dict(rel=2.0 ** -7, abs_rms=1e-3)
 
 # (streaming waves, tiles in flight per wave, tiles requested before the cast)
-SK_SHAPES = [(8, 7, 2), (8, 7, 7), (8, 6, 3), (8, 8, 4), (4, 10, 3), (6, 8, 3)]
+SK_SHAPES = [(8, 7, 2), (6, 8, 3)]
 
 
 @pytest.fixture(scope="module")
@@ -107,6 +107,20 @@ def test_every_streamk_config(fp8bs, problems, name, shape, m):
     _run(fp8bs, problems[name], cfg, m)
 
 
+@pytest.mark.parametrize("shape", SK_SHAPES)
+@pytest.mark.parametrize("name,m", [("ragged", 8), ("ragged", 1), ("ragged", 20), ("wide", 8),
+                                    ("wide", 32)])
+def test_whole_tile_partition(fp8bs, problems, name, shape, m):
+    """waves_n = 2: whole tiles only, 1 or 2 tiles per workgroup (ragged:
+    320 tiles; wide: 2176 tiles, 8 or 9 per workgroup), no workspace."""
+    from fp8_block_scaled_fp8bs_amd import GemmConfig
+    wk, d, pre = shape
+    cfg = GemmConfig(fp8bs.PATH_MFMA_STREAMK, pre, 2, wk, d, 1)
+    announce("stream-K whole", name, cfg, "m", m)
+    assert fp8bs.config_workspace_bytes(cfg, m, *PROBLEMS[name][:2]) == 0
+    _run(fp8bs, problems[name], cfg, m)
+
+
 @pytest.fixture(scope="module")
 def full(fp8bs):
     out = {}
@@ -119,16 +133,30 @@ def full(fp8bs):
     return out
 
 
-@pytest.mark.parametrize("name,split", [("square", 1), ("square", 4), ("mlp_down", 4),
-                                        ("mlp_down", 8), ("mlp_down", 1)])
+@pytest.mark.parametrize("name,split,whole", [("square", 1, 0), ("square", 4, 0),
+                                              ("mlp_down", 4, 0), ("mlp_down", 8, 0),
+                                              ("square", 1, 1)])
 @pytest.mark.parametrize("m", [1, 8, 16])
-def test_streamk_full_size(fp8bs, full, name, split, m):
+def test_streamk_full_size(fp8bs, full, name, split, whole, m):
     """The square (5120 x 5120) and MLP-down (17408 -> 5120) weights with their
-    seeded activations, full output, one and several K chunks."""
+    seeded activations, full output, one and several K chunks, and the
+    whole-tile partition."""
     from fp8_block_scaled_fp8bs_amd import GemmConfig
-    cfg = GemmConfig(fp8bs.PATH_MFMA_STREAMK, 2, 1, 8, 7, split)
+    cfg = GemmConfig(fp8bs.PATH_MFMA_STREAMK, 2, 1 + whole, 8, 7, split)
     announce("stream-K full", name, cfg, "m", m)
     _run(fp8bs, full[name], cfg, m)
+
+
+def test_streamk_lds_limit_rejected(fp8bs, full):
+    """MLP down in one K chunk would stage 136 activation blocks per
+    workgroup, more LDS than a compute unit has: a configuration error
+    before any launch, not a failed launch."""
+    from fp8_block_scaled_fp8bs_amd import Fp8bsError, GemmConfig
+    pr = full["mlp_down"]
+    with pytest.raises(Fp8bsError) as e:
+        fp8bs.gemm_ex(GemmConfig(fp8bs.PATH_MFMA_STREAMK, 2, 1, 8, 7, 1), pr.wq, pr.ws,
+                      x=pr.x[:8].contiguous())
+    assert e.value.status == 7
 
 
 def test_streamk_bit_identical_runs_and_reused_workspace(fp8bs, problems):
@@ -140,7 +168,7 @@ def test_streamk_bit_identical_runs_and_reused_workspace(fp8bs, problems):
     work = torch.empty(1 << 23, dtype=torch.uint8, device="cuda")
     work.fill_(0xA5)
     a, b = problems["ragged"], problems["chunks"]
-    ca, cb = GemmConfig(SKP, 2, 1, 8, 7, 1), GemmConfig(SKP, 3, 1, 8, 6, 4)
+    ca, cb = GemmConfig(SKP, 2, 1, 8, 7, 1), GemmConfig(SKP, 3, 1, 6, 8, 4)
     xa, xb = a.x[:8].contiguous(), b.x[:16].contiguous()
     ya = fp8bs.gemm_ex(ca, a.wq, a.ws, x=xa)   # fresh workspace
     yb = fp8bs.gemm_ex(cb, b.wq, b.ws, x=xb)

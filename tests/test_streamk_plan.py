@@ -37,6 +37,16 @@ def test_plan_covers_every_unit_once(fp8bs, n, k, split):
     assert fp8bs.streamk_plan_check(n, k, split, 256) == OK
 
 
+@pytest.mark.parametrize("n,k", [(5120, 5120), (34816, 5120), (248320, 5120), (5120, 17408),
+                                 (4096, 1024), (6144, 2944), (4224, 256)])
+def test_whole_tile_plan(fp8bs, n, k):
+    """Whole-tile partition: every unit once, no tile cut (one piece each),
+    tile counts per workgroup differing by at most one; only one K chunk."""
+    assert fp8bs.streamk_plan_check(n, k, 1, 256, whole=True) == OK
+    assert fp8bs.streamk_plan_check(n, k, 2, 256, whole=True) == UNSUPPORTED
+    assert fp8bs.streamk_plan_check(n, k, 1, n // 16 + 1, whole=True) == UNSUPPORTED
+
+
 @pytest.mark.parametrize("workgroups", [1, 7, 64, 255, 300])
 def test_plan_other_workgroup_counts(fp8bs, workgroups):
     """The partition arithmetic does not assume 256 workgroups."""
@@ -73,7 +83,9 @@ def test_streamk_config_rules(fp8bs):
         return lib.fp8bs_gemm_ex(P, None, None, m, P, P, n, k, P, P, wbytes, ctypes.byref(c), None)
     SKP = fp8bs.PATH_MFMA_STREAMK
     assert ex(GemmConfig(SKP, 2, 1, 8, 7, split_k=3)) == E_CFG            # 3 does not divide 40
-    assert ex(GemmConfig(SKP, 2, 2, 8, 7)) == E_CFG                       # waves_n must be 1
+    assert ex(GemmConfig(SKP, 2, 3, 8, 7)) == E_CFG                       # waves_n: 1 or 2
+    assert ex(GemmConfig(SKP, 2, 2, 8, 7, split_k=4)) == E_CFG            # whole tiles: one chunk
+    assert fp8bs.config_workspace_bytes(GemmConfig(SKP, 2, 2, 8, 7), 8, 5120, 5120) == 0
     assert ex(GemmConfig(SKP, 2, 1, 8, 7), n=512, k=1024) == E_CFG        # too few units
     assert ex(GemmConfig(SKP, 2, 1, 8, 7, reduce=1)) == E_CFG
     assert ex(GemmConfig(SKP, 2, 1, 8, 5)) == E_CFG                       # not compiled
