@@ -17,7 +17,7 @@ import torch  # loaded first so that libfp8bs binds to the HIP runtime torch use
 
 __all__ = [
     "Fp8bsError", "GemmConfig", "load", "library_path",
-    "quantize_weight", "quantize_act", "gemm", "gemm_q", "gemm_ex",
+    "quantize_weight", "quantize_act", "gemm", "gemm_q", "gemm_ex", "gemm_noalloc",
     "pack_weight", "gemm_tiles", "gemm_q_tiles", "tiles_select_config", "gemm_swiglu_tiles",
     "workspace_bytes", "config_workspace_bytes", "select_config",
     "swiglu_quant", "gemm_swiglu", "gemm_swiglu_ex", "swiglu_select_config",
@@ -99,6 +99,8 @@ def load() -> ctypes.CDLL:
         "fp8bs_quantize_act": (i32, [vp, i64, i64, vp, vp, vp]),
         "fp8bs_gemm": (i32, [vp, i64, vp, vp, i64, i64, vp, vp, sz, vp]),
         "fp8bs_gemm_q": (i32, [vp, vp, i64, vp, vp, i64, i64, vp, vp, sz, vp]),
+        "fp8bs_gemm_noalloc": (i32, [vp, i64, vp, vp, i64, i64, vp, vp]),
+        "fp8bs_gemm_noalloc_max_scratch": (sz, []),
         "fp8bs_gemm_workspace_bytes": (sz, [i64, i64, i64]),
         "fp8bs_gemm_select_config": (i32, [i64, i64, i64, ctypes.POINTER(_Config)]),
         "fp8bs_gemm_config_workspace_bytes": (sz, [ctypes.POINTER(_Config), i64, i64, i64]),
@@ -229,6 +231,19 @@ def gemm(x: torch.Tensor, w_q: torch.Tensor, w_s: torch.Tensor, out=None, worksp
                              n, k, _dev(y, torch.bfloat16, "y", 2), ws, wl, _stream(stream)))
     _done(wst, stream)
     return y
+
+
+def gemm_noalloc(x: torch.Tensor, w_q: torch.Tensor, w_s: torch.Tensor, out: torch.Tensor,
+                 stream=None) -> torch.Tensor:
+    """gemm() through the entry point that allocates nothing: the library's
+    fixed per-GPU scratch replaces the workspace (out must be given)."""
+    m, k = x.shape
+    n = w_q.shape[0]
+    _check(load().fp8bs_gemm_noalloc(_dev(x, torch.bfloat16, "x", 2), m,
+                                     _dev(w_q, torch.uint8, "w_fp8", 2),
+                                     _dev(w_s, torch.float32, "w_scale", 2), n, k,
+                                     _dev(out, torch.bfloat16, "y", 2), _stream(stream)))
+    return out
 
 
 def gemm_q(x_q: torch.Tensor, x_s: torch.Tensor, w_q: torch.Tensor, w_s: torch.Tensor,

@@ -108,6 +108,39 @@ fp8bs_status launch(const void* fn, dim3 grid, dim3 block, size_t lds, void* str
 
 // ----------------------------------------------------------- GEMM configs ---
 
+// Fixed device scratch of fp8bs_gemm_noalloc: every GPU the library runs on
+// holds its own copy from load until the process ends. Host code never uses
+// the array's name as an address: its device address is looked up once per
+// device (hipGetSymbolAddress, with that device current) and kept.
+constexpr size_t kNoAllocScratchBytes = (size_t)8 << 20;
+
+}  // namespace
+
+namespace fp8bs {
+__device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+}  // namespace fp8bs
+
+namespace {
+
+void* g_scratch_ptr[kMaxDevices];
+bool g_scratch_ok[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of this device's scratch (nullptr on failure).
+void* scratch_address(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ok[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+    g_scratch_ok[dev] = true;
+  }
+  return g_scratch_ptr[dev];
+}
 
 }  // namespace
 
@@ -747,6 +780,35 @@ fp8bs_status fp8bs_gemm(const void* x_bf16, int64_t m, const uint8_t* w_fp8, con
   return gemm_impl(true, x_bf16, nullptr, nullptr, m, w_fp8, w_scale, n, k, y_bf16, workspace,
                    workspace_bytes, nullptr, stream);
 }
+
+fp8bs_status fp8bs_gemm_noalloc(const void* x_bf16, int64_t m, const uint8_t* w_fp8,
+                                const float* w_scale, int64_t n, int64_t k, void* y_bf16,
+                                void* stream) {
+  // the same checks as fp8bs_gemm, in the same order; the workspace is the
+  // library's fixed scratch, so a configuration needing more is rejected
+  // (FP8BS_ERR_WORKSPACE) before anything is launched
+  if (!gemm_shape_ok(m, n, k, false)) return FP8BS_ERR_SHAPE;
+  if (m == 0 || n == 0) return FP8BS_OK;
+  if (!y_bf16 || (k > 0 && (!x_bf16 || !w_fp8 || !w_scale))) return FP8BS_ERR_NULL;
+  fp8bs_gemm_config c;
+  if (k > 0) {
+    if (!select_config(m, n, k, &c)) return FP8BS_ERR_SHAPE;
+    if (cfg_workspace(c, m, n, k, true) > kNoAllocScratchBytes) return FP8BS_ERR_WORKSPACE;
+  }
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return FP8BS_ERR_DEVICE;
+  }
+  const fp8bs_status st = current_device(nullptr);
+  if (st != FP8BS_OK) return st;
+  void* ws = scratch_address(dev);
+  if (!ws) return FP8BS_ERR_DEVICE;
+  return gemm_impl(true, x_bf16, nullptr, nullptr, m, w_fp8, w_scale, n, k, y_bf16, ws,
+                   kNoAllocScratchBytes, nullptr, stream);
+}
+
+size_t fp8bs_gemm_noalloc_max_scratch(void) { return kNoAllocScratchBytes; }
 
 fp8bs_status fp8bs_gemm_q(const uint8_t* x_fp8, const float* x_scale, int64_t m,
                           const uint8_t* w_fp8, const float* w_scale, int64_t n, int64_t k,

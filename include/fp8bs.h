@@ -118,6 +118,25 @@ fp8bs_status fp8bs_gemm(const void* x_bf16, int64_t m,
                         void* y_bf16, void* workspace, size_t workspace_bytes,
                         void* stream);
 
+/* fp8bs_gemm without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). It allocates nothing and calls no
+ * allocating routine: split-K partials, arrival counters and the prefill
+ * path's cast activations go to a fixed scratch array in the library, one
+ * copy per GPU, held from library load until the process ends, of
+ * fp8bs_gemm_noalloc_max_scratch() bytes (8 MiB). A shape whose selected
+ * configuration needs more scratch than that (large prefill m) returns
+ * FP8BS_ERR_WORKSPACE before any launch. Same configuration as fp8bs_gemm,
+ * hence the same bits. Nothing in the scratch must start at zero: partials
+ * are written before they are read and counters carry a per-launch epoch.
+ * Every call on one GPU shares that GPU's scratch, so calls that overlap on
+ * one GPU (different streams without ordering between them) race; calls
+ * ordered on one stream do not.                                            */
+fp8bs_status fp8bs_gemm_noalloc(const void* x_bf16, int64_t m,
+                                const uint8_t* w_fp8, const float* w_scale, int64_t n, int64_t k,
+                                void* y_bf16, void* stream);
+size_t fp8bs_gemm_noalloc_max_scratch(void);
+
 /* Same product from already-quantized activations (codes [m][k] and scales
  * [m][k/128] as produced by fp8bs_quantize_act). With the same shape it runs
  * the same kernel configuration as fp8bs_gemm, so
