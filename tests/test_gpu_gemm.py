@@ -153,6 +153,24 @@ def test_vocab_parity_sampled_columns(fp8bs, vocab_weight, m):
     _assert_close(np.concatenate(gots, axis=1), np.concatenate(refs, axis=1), f"vocab m={m}")
 
 
+@pytest.mark.parametrize("m", [8, 16])
+def test_vocab_run_to_run_bit_identical(fp8bs, vocab_weight, m):
+    """The 248,320-wide layer in the configuration each layout's table picks:
+    ten runs give the same bits, row-major and tile-layout weights."""
+    wl = WORKLOADS["vocab"]
+    wq, ws = vocab_weight
+    wt = fp8bs.pack_weight(wq)
+    x = dev_bf16(act_bf16(wl.x_seed, wl.col_seed, 32, wl.k, wl.n_outlier, wl.outlier_factor)[:m])
+    announce("vocab identity", m, fp8bs.select_config(m, wl.n, wl.k), fp8bs.tiles_select_config(m, wl.n, wl.k))
+    r0, t0 = fp8bs.gemm(x, wq, ws), fp8bs.gemm_tiles(x, wt, ws)
+    for _ in range(10):
+        r, t = fp8bs.gemm(x, wq, ws), fp8bs.gemm_tiles(x, wt, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(r.view(torch.int16), r0.view(torch.int16))
+        assert torch.equal(t.view(torch.int16), t0.view(torch.int16))
+    del wt
+
+
 def _configs():
     out = []
     for (tn, wn, wk, d) in MFMA_SHAPES:

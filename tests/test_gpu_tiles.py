@@ -206,14 +206,20 @@ def test_vocab_sampled_block_rows(fp8bs):
                       f"vocab tiles m={m}")
 
 
-def test_tiles_deterministic(fp8bs, full):
-    pr = full["mlp_down"]
+@pytest.mark.parametrize("name", ["square", "mlp_up", "mlp_down"])
+def test_tiles_deterministic(fp8bs, full, name):
+    """Ten runs at M = 8 in the configuration each layout's table picks (the
+    bench's kernels) give the same bits, on tile-layout and row-major
+    weights."""
+    pr = full[name]
     x = pr.x[:8].contiguous()
     y0 = fp8bs.gemm_tiles(x, pr.wt, pr.ws)
+    r0 = fp8bs.gemm(x, pr.wq, pr.ws)
     for _ in range(10):
         y = fp8bs.gemm_tiles(x, pr.wt, pr.ws)
+        r = fp8bs.gemm(x, pr.wq, pr.ws)
         torch.cuda.synchronize()
-        assert _bits_equal(y, y0)
+        assert _bits_equal(y, y0) and _bits_equal(r, r0)
 
 
 @pytest.mark.parametrize("m,n,k,wn,split", [(300, 512, 1280, 2, 1), (129, 768, 2048, 2, 3),
