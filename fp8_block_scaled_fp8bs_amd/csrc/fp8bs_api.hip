@@ -198,8 +198,8 @@ const KernelEntry* find_kernel(const fp8bs_gemm_config& c, int m, bool fused,
   } else if (c.path == FP8BS_PATH_PREFILL) {
     // one kernel; it reads activation codes (the fused call casts them first)
     for (const KernelEntry& e : kernel_registry())
-      if (e.path == FP8BS_PATH_PREFILL && !swiglu && e.wn == c.waves_n && e.d == c.depth &&
-          e.tn == c.tiles_n && e.layout == c.weight_layout)
+      if (e.path == FP8BS_PATH_PREFILL && !swiglu && e.wn == c.waves_n && e.wk == c.waves_k &&
+          e.d == c.depth && e.tn == c.tiles_n && e.layout == c.weight_layout)
         return &e;
     return nullptr;
   } else {
@@ -217,12 +217,17 @@ const KernelEntry* find_kernel(const fp8bs_gemm_config& c, int m, bool fused,
   return nullptr;
 }
 
+// The wide prefill kernel, grid or 1-D schedule.
+bool pfw_config(const fp8bs_gemm_config& c) {
+  return c.path == FP8BS_PATH_PREFILL && (c.tiles_n == PF_WIDE || c.tiles_n == PF_WIDE_1D);
+}
+
 // Output columns per workgroup of a grid configuration (the row-range
 // path divides n by the compute-unit count at launch instead).
 int config_rows(const fp8bs_gemm_config& c) {
   if (is_row_range(c.path)) return 4;
   if (c.path == FP8BS_PATH_MFMA_STREAMK) return 16;
-  if (c.path == FP8BS_PATH_PREFILL) return pf_tile_n(c.waves_n);
+  if (c.path == FP8BS_PATH_PREFILL) return pfw_config(c) ? BLK : pf_tile_n(c.waves_n);
   return (c.path == FP8BS_PATH_DOT ? 8 : 16) * c.tiles_n * c.waves_n;
 }
 
@@ -246,8 +251,10 @@ int rows_per_workgroup(int64_t n, int num_cu, int layout = FP8BS_LAYOUT_ROWS) {
 
 size_t config_lds_bytes(const fp8bs_gemm_config& c, int m, int64_t n, int kbn, int num_cu,
                         bool swiglu = false) {
-  if (c.path == FP8BS_PATH_PREFILL)
+  if (c.path == FP8BS_PATH_PREFILL) {
+    if (pfw_config(c)) return (size_t)pfw_lds_bytes(c.waves_k, c.depth);
     return (size_t)(c.depth > 1 ? pf_dma_lds_bytes(c.waves_n, c.depth) : pf_lds_bytes(c.waves_n));
+  }
   const int mt = m <= 16 ? 1 : 2;
   if (c.path == FP8BS_PATH_MFMA_STREAMK)
     return (size_t)lds_streamk_bytes(c.split_k > 0 ? kbn / c.split_k : kbn, m, c.waves_k, mt);
@@ -493,7 +500,30 @@ size_t prefill_x_bytes(int64_t m, int64_t k) {
   return (size_t)((m * k + 255) / 256 * 256) + (size_t)((m * (k / BLK) * 4 + 15) / 16 * 16);
 }
 
-// Prefill workspace: the cast activations (fused call), then the split partials.
+// 1-D schedule of the wide prefill kernel (tiles_n PF_WIDE_1D): whole
+// 256 x 256 tiles in complete rounds of kTableCUs workgroups; the tiles left
+// over run as two 128-column halves each when those fit in half a round,
+// else as whole tiles in a last, partly filled round.
+struct PfwPlan {
+  int64_t full, units;
+};
+PfwPlan pfw_plan(int waves_m, int64_t m, int64_t n) {
+  const int64_t tm = pfw_tile_m(waves_m);
+  const int64_t tiles = ((n + PFW_TILE_N - 1) / PFW_TILE_N) * ((m + tm - 1) / tm);
+  PfwPlan q;
+  q.full = tiles / kTableCUs * kTableCUs;
+  const int64_t rem = tiles - q.full;
+  if (rem > 0 && 2 * rem <= kTableCUs) {
+    q.units = q.full + 2 * rem;
+  } else {
+    q.full = tiles;
+    q.units = tiles;
+  }
+  return q;
+}
+
+// Prefill workspace: the cast activations (fused call), then the split
+// partials.
 size_t prefill_workspace(const fp8bs_gemm_config& c, int64_t m, int64_t n, int64_t k, bool fused) {
   return (fused ? prefill_x_bytes(m, k) : 0) + cfg_partial_bytes(c, m, n);
 }
@@ -609,6 +639,9 @@ fp8bs_status gemm_impl(bool fused, const void* x_bf16, const uint8_t* x_fp8,
   if (c.split_k < 1 || c.split_k > 64 || c.split_k > kbn) return FP8BS_ERR_CONFIG;
   if (c.path == FP8BS_PATH_PREFILL ? c.reduce != FP8BS_REDUCE_KERNEL : m > kMaxDecodeM)
     return FP8BS_ERR_CONFIG;
+  // the 1-D schedule runs every tile over the whole K range
+  if (c.path == FP8BS_PATH_PREFILL && c.tiles_n == PF_WIDE_1D && c.split_k != 1)
+    return FP8BS_ERR_CONFIG;
   // row-range paths: split only on MFMA_ROWS, with the reduce kernel
   if (is_row_range(c.path) &&
       (c.waves_n != 1 ||
@@ -665,6 +698,8 @@ fp8bs_status gemm_impl(bool fused, const void* x_bf16, const uint8_t* x_fp8,
   p.hs = h_scale;
   p.epoch = g_epoch.fetch_add(1) & ((uint64_t(1) << 56) - 1);
   p.sk_whole = streamk && c.waves_n == 2 ? 1 : 0;
+  p.pf_full = 0;
+  p.pf_1d = 0;
   p.rows_per_wg = 0;
   p.m = (int)m;
   p.n = (int)n;
@@ -690,9 +725,22 @@ fp8bs_status gemm_impl(bool fused, const void* x_bf16, const uint8_t* x_fp8,
     block = dim3(64 * (c.waves_k + 1));
   }
   if (prefill) {
-    grid = dim3((unsigned)(n / pf_tile_n(c.waves_n)), (unsigned)((m + PF_TILE_M - 1) / PF_TILE_M),
-                (unsigned)c.split_k);
-    block = dim3(128 * c.waves_n);
+    if (pfw_config(c)) {
+      const int64_t tm = pfw_tile_m(c.waves_k);
+      grid = dim3((unsigned)((n + PFW_TILE_N - 1) / PFW_TILE_N), (unsigned)((m + tm - 1) / tm),
+                  (unsigned)c.split_k);
+      block = dim3(64 * c.waves_n * c.waves_k);
+      if (c.tiles_n == PF_WIDE_1D) {
+        const PfwPlan q = pfw_plan(c.waves_k, m, n);
+        grid = dim3((unsigned)q.units);
+        p.pf_full = (int)q.full;
+        p.pf_1d = 1;
+      }
+    } else {
+      grid = dim3((unsigned)(n / pf_tile_n(c.waves_n)),
+                  (unsigned)((m + PF_TILE_M - 1) / PF_TILE_M), (unsigned)c.split_k);
+      block = dim3(128 * c.waves_n);
+    }
     p.part = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
                                       (fused ? prefill_x_bytes(m, k) : 0));
     if (fused) {

@@ -51,6 +51,7 @@ struct GemmParams {
   uint8_t* hq;          // SwiGLU epilogue: E4M3 codes [m][n/2]
   float* hs;            // SwiGLU epilogue: fp32 scales [m][n/256]
   int sk_whole;         // stream-K kernel: whole-cell partition
+  int pf_full, pf_1d;   // wide prefill kernel: whole tiles of the 1-D schedule, schedule
 };
 
 // LDS layout of a workgroup:

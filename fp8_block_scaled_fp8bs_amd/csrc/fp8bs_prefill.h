@@ -496,4 +496,338 @@ __global__ __launch_bounds__(128 * WN, WN == 2 ? 2 : 1) void gemm_prefill_dma_ke
   }
 }
 
+
+// Wide wave tiles. In the kernel above each wave owns 64 x 64 outputs, so per
+// K block it reads 16 KB of operands out of LDS for 2 MFLOP, and a 128 x 128
+// workgroup tile fetches 32 KB from L2 per 4 MFLOP. Here each wave owns a
+// 64 (m) x 128 (n) part -- 4 activation by 8 weight subtiles, one whole
+// weight block row, so the weight scale is one value per wave and block --
+// and the workgroup, WM waves along m by 2 along n, a (64 WM) x 256 tile:
+// with WM = 4, 8 waves on 256 x 256 read 24 KB of LDS per 4 MFLOP and fetch
+// 64 KB per 16 MFLOP, half the L2 traffic per product of the 128 x 128 tile.
+// One workgroup per compute unit (the two stages take 130 KB of LDS). A
+// workgroup can also take a half tile, (64 WM) x 128, with 64 x 64 per wave
+// (the last tile of an odd number of 128-column blocks, and the tail of the
+// one-dimensional schedule below). The stages are filled by direct loads as
+// in gemm_prefill_dma_kernel: every wave issues the same number per stage
+// (the activation scales, WM loads of 256 bytes, are loaded by waves w and
+// w + WM alike, which write the same bytes). Per block, a wave reads its 4
+// activation operands, then for each weight subtile one operand and 4
+// MFMAs, and rescales each subtile's products into the fp32 accumulators one
+// subtile later; the wait and barrier that publish the next block come after
+// the block's last operand read, so the last MFMAs run while the waves meet.
+constexpr int PFW_TILE_N = 256;  // output columns of a whole tile
+constexpr int PF_WIDE = 3;       // tiles_n of a configuration: this kernel, grid schedule
+constexpr int PF_WIDE_1D = 4;    // tiles_n of a configuration: this kernel, 1-D schedule
+__host__ __device__ constexpr int pfw_tile_m(int wm) { return 64 * wm; }
+__host__ __device__ constexpr int pfw_stage_bytes(int wm) {
+  return PFW_TILE_N * BLK + pfw_tile_m(wm) * BLK + pfw_tile_m(wm) * 4;
+}
+__host__ __device__ constexpr int pfw_lds_bytes(int wm, int stages) {
+  return stages * pfw_stage_bytes(wm);
+}
+// Waves that issue the stage loads (one per SIMD), and the loads each issues
+// per stage with NT weight subtiles per wave (8: whole tile, 4: half tile):
+// 4 NT / 4 weight pieces of 1 KB, the activation pieces, one scale piece.
+constexpr int PFW_LOADERS = 4;
+__host__ __device__ constexpr int pfw_per_stage(int wm, int nt) {
+  return 4 * nt / PFW_LOADERS + pfw_tile_m(wm) * BLK / 1024 / PFW_LOADERS + 1;
+}
+
+// Tile q of the grouped order -> (n tile, m tile): groups of up to 8 m tiles,
+// and inside a group consecutive q share one n tile.
+__device__ __forceinline__ void pfw_tile_xy(int q, int tiles_n, int tiles_m, int& bx, int& by) {
+  constexpr int GM = 8;
+  const int group = q / (GM * tiles_n);
+  const int first = group * GM;
+  const int gm = tiles_m - first < GM ? tiles_m - first : GM;
+  const int r = q - group * GM * tiles_n;
+  by = first + r % gm;
+  bx = r / gm;
+}
+
+// Work of a workgroup: output columns n0 .. n0 + 255 (half: n0 .. n0 + 127),
+// rows m0 .., K blocks kb0 .. kb1 - 1.
+// Grid schedule (p.pf_1d == 0): grid (ceil(n / 256), ceil(m / (64 WM)),
+// split), the tile order of pf_tile_order, split z of K; a tile of one
+// 128-column block is a half tile.
+// 1-D schedule (p.pf_1d == 1): p.pf_full whole tiles, which fill complete
+// rounds of resident workgroups, then two half-tile units for each tile
+// left over (too few tiles to occupy every compute unit; each half has the
+// whole K range, so halves meet no partial sums). Workgroups are dispatched
+// to the 8 XCDs in turn, so whole tile b is taken from the grouped order at
+// (b mod 8) * (p.pf_full / 8) + b / 8: each XCD works through its own
+// contiguous eighth of it, a few weight and activation tiles at a time. The
+// second half of a one-block tile is empty.
+struct PfwWork {
+  int n0, m0, kb0, kb1;
+  bool half;
+};
+template <int TM>
+__device__ __forceinline__ PfwWork pfw_work(const GemmParams& p) {
+  PfwWork w;
+  int bx, by;
+  if (p.pf_1d == 0) {
+    pf_tile_order(bx, by);
+    split_range(blockIdx.z, p.split, p.kbn, w.kb0, w.kb1);
+    w.n0 = bx * PFW_TILE_N;
+    w.m0 = by * TM;
+    w.half = w.n0 + BLK >= p.n;
+    return w;
+  }
+  const int tiles_n = (p.n + PFW_TILE_N - 1) / PFW_TILE_N, tiles_m = (p.m + TM - 1) / TM;
+  const int b = blockIdx.x, full = p.pf_full;
+  w.kb0 = 0;
+  w.kb1 = p.kbn;
+  if (b < full) {
+    pfw_tile_xy((full & 7) == 0 ? (b & 7) * (full >> 3) + (b >> 3) : b, tiles_n, tiles_m, bx, by);
+    w.n0 = bx * PFW_TILE_N;
+    w.half = w.n0 + BLK >= p.n;
+  } else {
+    const int u = b - full;
+    pfw_tile_xy(full + (u >> 1), tiles_n, tiles_m, bx, by);
+    w.n0 = bx * PFW_TILE_N + (u & 1) * BLK;
+    w.half = true;
+  }
+  w.m0 = by * TM;
+  return w;
+}
+
+// f(integral_constant<I>) for I = I0 .. N-1, in order.
+template <int I, int N, typename F>
+__device__ __forceinline__ void pf_static_for(F& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    pf_static_for<I + 1, N>(f);
+  }
+}
+
+// One unit (whole tile, NT = 8, or half tile, NT = 4) of the kernel below.
+template <int WM, int S, bool PK, int NT, bool LOADER>
+__device__ __forceinline__ void pfw_unit(const GemmParams& p, uint8_t* lds_all, const PfwWork& work) {
+  constexpr int STAGE = pfw_stage_bytes(WM);
+  constexpr int TM = pfw_tile_m(WM);
+  constexpr int LW = PFW_LOADERS;
+  constexpr int WQ = 4 * NT / LW;           // weight pieces (1 KB) per loader and stage
+  constexpr int XQ = TM * BLK / 1024 / LW;  // activation pieces per loader and stage
+  constexpr int PER = pfw_per_stage(WM, NT);
+  static_assert(PER == WQ + XQ + 1 && TM * 4 == 256 * LW, "one scale piece per loader");
+  constexpr int WCOLS = 16 * NT;         // output columns of a wave
+  constexpr int XOFF = PFW_TILE_N * BLK;  // activation rows within a stage
+  constexpr int SOFF = XOFF + TM * BLK;   // activation scales within a stage
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave & 1, wm = wave >> 1;
+  const int n0 = work.n0, m0 = work.m0;
+  const int l16 = lane & 15, g = lane >> 4;
+  const int kb0 = work.kb0, last = work.kb1 - 1;
+  // a whole tile holds two weight blocks, one per wave column; a half tile one
+  const float* wsrow = p.ws + (size_t)(n0 / BLK + (NT == 8 ? wn : 0)) * (size_t)p.kbn;
+  const uint32_t lds0 = lds_addr(lds_all);
+
+  // Loader wave w < LW copies pieces q = w + LW i of the stage's weight rows
+  // (1 KB: rows 8q .. 8q+7, or half q % 2 of 2 KB tile q / 2) and of its
+  // activation rows, and scale piece w (rows 64 w ..). Every piece q a
+  // loader takes has q % 2 = w % 2, so one lane offset serves all of them:
+  // row 8q + lane / 8, 16-byte segment (lane % 8) ^ (lane / 8) ^ (q % 2)
+  // (the swizzle of pf_swz); the rest of each weight offset is uniform and
+  // goes into the scalar base. Activation rows past m (last m tile) are
+  // clamped per lane.
+  const uint32_t xseg = 16u * (uint32_t)((lane & 7) ^ (lane >> 3) ^ (wave & 1));
+  const uint32_t wlo = PK ? 16u * (uint32_t)lane : (uint32_t)(lane >> 3) * (uint32_t)p.k + xseg;
+  const int xlim = p.m - 1 - m0;  // last activation row of the tile
+  const int sr = 64 * wave + lane;
+  const uint32_t so = (uint32_t)(sr <= xlim ? sr : xlim) * (uint32_t)p.kbn * 4u;
+  const uint8_t* wbase = PK ? p.wq + (size_t)(n0 >> 4) * (size_t)p.kbn * 2048u
+                            : p.wq + (size_t)n0 * (size_t)p.k;
+  const uint8_t* xbase = p.xq + (size_t)m0 * (size_t)p.k;
+  const float* sbase = p.xs + (size_t)m0 * (size_t)p.kbn;
+
+  // The loads of block kb into a stage, by the loaders (LOADER: this wave
+  // is one; the kernel runs this function in two copies, so neither has a
+  // branch in its loop): WQ weight pieces, XQ activation pieces, the scale
+  // piece (PER in all). The other waves load nothing, so only the loaders
+  // can stall on a full memory queue, and on every SIMD the other wave keeps
+  // the matrix core busy meanwhile.
+  auto issue = [&](int kb, int stage) {
+    if constexpr (LOADER) {
+      kb = kb < last ? kb : last;
+      const uint32_t st = lds0 + (uint32_t)(stage * STAGE);
+      const uint8_t* wb = wbase + (size_t)kb * (PK ? 2048u : (size_t)BLK);
+      const uint8_t* xb = xbase + (size_t)kb * BLK;
+#pragma unroll
+      for (int i = 0; i < WQ; ++i) {
+        const int q = wave + LW * i;
+        const size_t off = PK ? (size_t)(q >> 1) * (size_t)p.kbn * 2048u + (size_t)(q & 1) * 1024u
+                              : (size_t)(8 * q) * (size_t)p.k;
+        dma16(st + (uint32_t)q * 1024u, wb + off, wlo);
+      }
+      // the clamped offsets are recomputed per block (a few VALU operations)
+      // rather than held in registers across the loop
+      int lr = lane >> 3;
+      asm volatile("" : "+v"(lr));
+#pragma unroll
+      for (int i = 0; i < XQ; ++i) {
+        const int q = wave + LW * i;
+        const int r = 8 * q + lr;
+        const uint32_t off = (uint32_t)(r <= xlim ? r : xlim) * (uint32_t)p.k + xseg;
+        dma16(st + (uint32_t)XOFF + (uint32_t)q * 1024u, xb, off);
+      }
+      dma4(st + (uint32_t)SOFF + (uint32_t)wave * 256u, sbase + kb, so);
+    }
+  };
+
+  f32x4 acc[NT][4];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // The activation operands and the scale products of block kb, from its stage.
+  i32x8 bop[4];
+  float sc[4];
+  auto read_x = [&](const uint8_t* st) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bop[j] = pf_swz_operand(st + XOFF, 64 * wm + 16 * j + l16, g);
+  };
+  auto read_sc = [&](int kb, const uint8_t* st) {
+    const float* sl = reinterpret_cast<const float*>(st + SOFF);
+    const float sw = load_invariant(wsrow, (size_t)kb);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sc[j] = sl[64 * wm + 16 * j + l16] * sw;
+  };
+
+  // S - 1 stages in flight (block kb0 + S - 1 is loaded during block kb0),
+  // then the first block's activation operands
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s) issue(kb0 + s, s);
+  wait_loads_then_barrier<(S - 2) * PER>();
+  read_x(lds_all);
+  read_sc(kb0, lds_all);
+
+  // One K block out of stage ST (a compile-time ring position). The wait
+  // and barrier that publish the next block's stage and free this one come
+  // after this block's last LDS read and last MFMA issue, so the matrix
+  // cores still work on the last products while the waves meet, refill the
+  // stage with the block S ahead and read the next block's activations.
+  // One K block out of stage ST (a compile-time ring position). The loads
+  // of block kb + S - 1 go into the stage the last barrier freed. The wait
+  // and barrier that publish the next block's
+  // stage and free this one come after this block's last LDS read and last
+  // MFMA issue, so the matrix cores still work on the last products while
+  // the waves meet and read the next block's activations.
+  auto block = [&](int kb, auto stc) {
+    constexpr int ST = decltype(stc)::value;
+    constexpr int SP = (ST + S - 1) % S;
+    const uint8_t* wl = lds_all + ST * STAGE;
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    f32x4 pb[2][4];
+    auto sub = [&](auto tc) {
+      constexpr int T = decltype(tc)::value;
+      if constexpr (T == 0) issue(kb + S - 1, SP);
+      const i32x8 aop = PK ? pf_tile_operand(wl, NT * wn + T, lane)
+                           : pf_swz_operand(wl, WCOLS * wn + 16 * T + l16, g);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        pb[T & 1][j] =
+            __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop[j], z, 0, 0, 0, 0, 0, 0);
+      if constexpr (T > 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[T - 1][j][i] = __builtin_fmaf(pb[(T - 1) & 1][j][i], sc[j], acc[T - 1][j][i]);
+      }
+    };
+    pf_static_for<0, NT>(sub);
+    wait_loads_then_barrier<(S - 2) * PER>();
+    const uint8_t* next = lds_all + ((ST + 1) % S) * STAGE;
+    read_x(next);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc[NT - 1][j][i] = __builtin_fmaf(pb[(NT - 1) & 1][j][i], sc[j], acc[NT - 1][j][i]);
+    read_sc(kb + 1 < last ? kb + 1 : last, next);
+  };
+
+  int kb = kb0;
+  for (; kb + S - 1 <= last; kb += S) pf_ring_turn<0, S>(kb, block);
+  pf_ring_tail<0, S>(kb, last, block);
+  // every load of this wave has landed; after the barrier, every load and
+  // every operand read of the workgroup is done and the LDS is free
+  asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+  lds_barrier();
+
+  if (p.out == OUT_PARTIAL) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int m = m0 + 64 * wm + 16 * j + l16;
+      if (m < p.m) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const int n = n0 + WCOLS * wn + 16 * t + 4 * g;
+          *reinterpret_cast<float4*>(p.part + ((size_t)blockIdx.z * p.m + m) * (size_t)p.n + n) =
+              make_float4(acc[t][j][0], acc[t][j][1], acc[t][j][2], acc[t][j][3]);
+        }
+      }
+    }
+    return;
+  }
+  // bf16 output: each wave stages its 64 x WCOLS part in its own LDS
+  // (row r: 2 WCOLS bytes in U = 2 NT 16-byte units, unit u at
+  // u ^ (r mod U), so both the 8-byte writes of 16 rows and the 16-byte
+  // reads of whole rows spread over the banks), then writes whole row
+  // segments of 2 WCOLS bytes, 1 KB per store instruction, instead of
+  // 32-byte pieces of 16 rows.
+  constexpr int U = 2 * NT;       // 16-byte units per staged row
+  constexpr int RPI = 64 / U;     // rows per store instruction
+  uint8_t* ob = lds_all + wave * (64 * 16 * U);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = 16 * j + l16;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int u = 2 * t + (g >> 1);
+      *reinterpret_cast<uint2*>(ob + r * 16 * U + 16 * (u ^ (r % U)) + 8 * (g & 1)) =
+          make_uint2(pack_bf16x2(acc[t][j][0], acc[t][j][1]),
+                     pack_bf16x2(acc[t][j][2], acc[t][j][3]));
+    }
+  }
+  // the wave reads back only what it wrote itself (LDS accesses of one wave
+  // complete in order)
+  const int u = lane % U;
+#pragma unroll
+  for (int i = 0; i < 64 / RPI; ++i) {
+    const int r = RPI * i + lane / U;
+    const int m = m0 + 64 * wm + r;
+    const uint4 v = *reinterpret_cast<const uint4*>(ob + r * 16 * U + 16 * (u ^ (r % U)));
+    if (m < p.m)
+      *reinterpret_cast<uint4*>(p.y + (size_t)m * (size_t)p.n + n0 + WCOLS * wn + 8 * u) = v;
+  }
+}
+
+// pfw_lds_bytes(WM, S) of dynamic LDS; 128 WM threads; grid as pfw_work.
+template <int WM, int S, bool PK = false>
+__global__ __launch_bounds__(128 * WM, 1) void gemm_prefill_wide_kernel(GemmParams p) {
+  static_assert(WM == 4, "8 waves: 4 along m, 2 along n");
+  static_assert(2 * WM * 16384 <= pfw_lds_bytes(WM, S), "output staging fits in the stages");
+  static_assert(S >= 2 && (S - 1) * pfw_per_stage(WM, 8) <= 63, "vmcnt range");
+  extern __shared__ __align__(16) uint8_t lds_all[];
+  const PfwWork work = pfw_work<pfw_tile_m(WM)>(p);
+  if (work.n0 >= p.n) return;  // the empty second half of a one-block tile
+  const bool loader = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) < PFW_LOADERS;
+  if (work.half) {
+    if (loader)
+      pfw_unit<WM, S, PK, 4, true>(p, lds_all, work);
+    else
+      pfw_unit<WM, S, PK, 4, false>(p, lds_all, work);
+  } else {
+    if (loader)
+      pfw_unit<WM, S, PK, 8, true>(p, lds_all, work);
+    else
+      pfw_unit<WM, S, PK, 8, false>(p, lds_all, work);
+  }
+}
+
 }  // namespace fp8bs

@@ -86,6 +86,108 @@ def test_prefill_every_variant(fp8bs, variant, m, n, k, split):
     assert np.array_equal(host_bits(y), host_bits(y2))
 
 
+WIDE = [(4, 2)]  # (waves along m, LDS stages) of the wide-wave-tile kernels
+
+
+@pytest.mark.parametrize("layout", ["rows", "tiles"])
+@pytest.mark.parametrize("wk,depth", WIDE)
+@pytest.mark.parametrize("m,n,k,split", [(300, 512, 1280, 1), (129, 768, 2048, 3), (64, 384, 384, 1),
+                                         (33, 1024, 128, 1), (520, 256, 2560, 2),
+                                         (1000, 2176, 640, 1), (257, 128, 256, 1)])
+def test_prefill_wide_wave_tiles(fp8bs, layout, wk, depth, m, n, k, split):
+    """The kernels with 64 x 128 outputs per wave (256 x 256 output tiles,
+    8 waves, grid schedule): ragged m tails, an odd number of 128-column
+    blocks (the last tile one block wide), split and unsplit, one K block
+    (fewer blocks than stages), both weight layouts. Full output against the
+    oracle, and the same bits as the 128 x 128 direct-load kernel in the same
+    split (the same products, rescaled in the same order)."""
+    import dataclasses
+    from fp8_block_scaled_fp8bs_amd import GemmConfig
+    cfg = GemmConfig(fp8bs.PATH_PREFILL, 3, 2, wk, depth, split)
+    base = GemmConfig(fp8bs.PATH_PREFILL, 1, 2, 2, 2, split)
+    announce("prefill wide wave tiles", cfg, layout, m, n, k)
+    x_bits, wq, ws, wq_ref, ws_ref = _problem(fp8bs, m, n, k, 7600 + m + n + k)
+    x = dev_bf16(x_bits)
+    w = wq
+    if layout == "tiles":
+        cfg = dataclasses.replace(cfg, weight_layout=fp8bs.LAYOUT_TILES)
+        w = fp8bs.pack_weight(wq)
+    y = fp8bs.gemm_ex(cfg, w, ws, x=x)
+    y_base = fp8bs.gemm_ex(base, wq, ws, x=x)
+    xq, xs = fp8bs.quantize_act(x)
+    y_q = fp8bs.gemm_ex(cfg, w, ws, x_q=xq, x_s=xs)
+    torch.cuda.synchronize()
+    xq_ref, xs_ref = oracle.quantize_act_ref(x_bits)
+    rep = oracle.tolerance_report(host_bits(y), oracle.gemm_ref(xq_ref, xs_ref, wq_ref, ws_ref), **TOL)
+    assert rep["finite"] and rep["n_bad"] == 0, rep
+    assert np.array_equal(host_bits(y), host_bits(y_base)), "differs from the 128 x 128 kernel"
+    assert np.array_equal(host_bits(y), host_bits(y_q)), "fused cast differs"
+
+
+@pytest.mark.parametrize("layout", ["rows", "tiles"])
+@pytest.mark.parametrize("m,n,k", [(2100, 8320, 384), (4096, 4352, 256), (2100, 12800, 256),
+                                   (300, 640, 1280), (33, 128, 256)])
+def test_prefill_wide_1d_schedule(fp8bs, layout, m, n, k):
+    """The 1-D schedule of the wide kernel: whole 256 x 256 tiles in complete
+    rounds of 256 workgroups, the tiles left over as two 128-column halves
+    when those fit in half a round. 2100 x 8320: 33 x 9 = 297 tiles, 41 left
+    over as 82 halves (the last tile column one 128-column block wide, so
+    one half of its tiles is empty; a ragged m tail); 4096 x 4352: 272 tiles,
+    16 left over; 2100 x 12800: 450 tiles, 194 left over (too many: a last
+    round of whole tiles); 300 x 640: 6 tiles, all halves; 33 x 128: one
+    half. Full output against the oracle and the bits of the unsplit
+    128 x 128 kernel (every tile, whole or half, runs the whole K range with
+    the same products rescaled in the same order); the bits repeat over
+    graph replays."""
+    import dataclasses
+    from fp8_block_scaled_fp8bs_amd import GemmConfig
+    cfg = GemmConfig(fp8bs.PATH_PREFILL, 4, 2, 4, 2, 1)
+    announce("prefill wide 1-D", cfg, layout, m, n, k)
+    x_bits, wq, ws, wq_ref, ws_ref = _problem(fp8bs, m, n, k, 7700 + m + n + k)
+    x = dev_bf16(x_bits)
+    w = wq
+    if layout == "tiles":
+        cfg = dataclasses.replace(cfg, weight_layout=fp8bs.LAYOUT_TILES)
+        w = fp8bs.pack_weight(wq)
+    y = fp8bs.gemm_ex(cfg, w, ws, x=x)
+    y1 = fp8bs.gemm_ex(GemmConfig(fp8bs.PATH_PREFILL, 1, 2, 2, 2, 1), wq, ws, x=x)
+    xq, xs = fp8bs.quantize_act(x)
+    yq = fp8bs.gemm_ex(cfg, w, ws, x_q=xq, x_s=xs)
+    torch.cuda.synchronize()
+    yb = host_bits(y)
+    xq_ref, xs_ref = oracle.quantize_act_ref(x_bits)
+    rep = oracle.tolerance_report(yb, oracle.gemm_ref(xq_ref, xs_ref, wq_ref, ws_ref), **TOL)
+    assert rep["finite"] and rep["n_bad"] == 0, rep
+    assert np.array_equal(yb, host_bits(y1)), "differs from the 128 x 128 kernel"
+    assert np.array_equal(yb, host_bits(yq)), "fused cast differs"
+    out = torch.empty_like(y)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fp8bs.gemm_ex(cfg, w, ws, x_q=xq, x_s=xs, out=out, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fp8bs.gemm_ex(cfg, w, ws, x_q=xq, x_s=xs, out=out)
+    for rep_i in range(3):
+        out.fill_(0)
+        fp8bs.gemm_ex(cfg, w, ws, x_q=xq, x_s=xs)  # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(out), yb), f"replay {rep_i}"
+
+
+def test_prefill_wide_1d_rejects_split(fp8bs):
+    """The 1-D schedule runs every tile over the whole K range: a K split in
+    its configuration is a configuration error."""
+    from fp8_block_scaled_fp8bs_amd import Fp8bsError, GemmConfig
+    x_bits, wq, ws, _, _ = _problem(fp8bs, 64, 256, 512, 7800)
+    with pytest.raises(Fp8bsError) as e:
+        fp8bs.gemm_ex(GemmConfig(fp8bs.PATH_PREFILL, 4, 2, 4, 2, 2), wq, ws, x=dev_bf16(x_bits))
+    assert e.value.status == 7
+
+
 @pytest.mark.parametrize("m,n,k", [(300, 8192, 256), (1000, 16384, 128), (129, 8320, 256)])
 def test_prefill_wide_grid_tile_order(fp8bs, m, n, k):
     """Wide unsplit grids (64 or more 128-column tiles) take the tile order
