@@ -385,7 +385,19 @@ bool select_config(int64_t m, int64_t n, int64_t k, fp8bs_gemm_config* out, bool
   if (m < 0 || m > kMaxM || n < 0 || k < 0 || n % BLK || k % BLK) return false;
   if (swiglu && n % (2 * BLK)) return false;
   if (m > kMaxDecodeM && n > 0 && k > 0) {
-    // prefill sizes: the tiled kernel with 4 waves on 128 x 128 output tiles
+    // prefill sizes with at least 150 256 x 256 output tiles (m n >= about
+    // 9.8 M): the wide kernel (8 waves, 64 x 128 outputs each) on the 1-D
+    // schedule. Measured on MI355X at m = 128 .. 8192 on the square, MLP-up
+    // and MLP-down weights: faster from 160 tiles up (square m = 2048:
+    // 76 against 84 us; m = 8192: 217 against 260 us), slower at 136 and
+    // fewer (MLP up m = 128: 80 against 71 us).
+    const int64_t wtiles = ((n + PFW_TILE_N - 1) / PFW_TILE_N) * ((m + 255) / 256);
+    if (wtiles >= 150) {
+      *out = make_cfg(FP8BS_PATH_PREFILL, PF_WIDE_1D, 2, 4, 2, 1);
+      out->weight_layout = layout;
+      return true;
+    }
+    // fewer tiles: the tiled kernel with 4 waves on 128 x 128 output tiles
     // and two LDS stages filled by direct loads (two workgroups per compute
     // unit), with K split when the tiles alone cannot fill the compute units
     // (each split keeps at least two K blocks). Measured on MI355X at

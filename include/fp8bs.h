@@ -180,9 +180,19 @@ enum { FP8BS_LAYOUT_ROWS = 0, FP8BS_LAYOUT_TILES = 1 };
  *             of MFMA_ROWS without a staging phase: each wave casts the
  *             activation blocks it uses as the first tile reaches them;
  *             tiles_n, waves_n and split_k must be 1; needs m*k*2 < 2^31), or
- *             PREFILL (any m: workgroups of 4 waves own 128 x 128 output
- *             tiles and step through K in 128-deep blocks staged in LDS;
- *             split_k must be 1, the other fields are not used), or
+ *             PREFILL (any m; reduce must be FP8BS_REDUCE_KERNEL): with
+ *             tiles_n 1 or 2, waves_k 2 and waves_n 2 or 4, workgroups of
+ *             2 waves_n waves own (64 waves_n) x 128 output tiles and step
+ *             through K in 128-deep blocks: depth 1 = through registers one
+ *             block ahead, depth 2..4 = a ring of LDS stages filled by
+ *             direct loads, refilled when the next block starts (tiles_n
+ *             1) or once every wave holds a block's operands (tiles_n 2);
+ *             with tiles_n 3 or 4, waves_n 2, waves_k 4 and depth 2, the
+ *             wide kernel: 8 waves own 256 x 256 output tiles (64 x 128
+ *             each), on a grid of tiles with K split over split_k
+ *             workgroups (tiles_n 3), or on the 1-D schedule (tiles_n 4,
+ *             split_k 1): whole tiles in complete rounds of 256
+ *             workgroups, the tiles left over as 128-column halves; or
  *             MFMA_ROWS_REG (the work split of MFMA_ROWS with each wave's
  *             activation operands held in registers instead of LDS, so m up
  *             to 32 runs unsplit at any K the registers hold: depth is the
@@ -233,8 +243,8 @@ enum { FP8BS_LAYOUT_ROWS = 0, FP8BS_LAYOUT_TILES = 1 };
  *             fp8bs_pack_weight; MFMA, MFMA_ROWS, MFMA_STREAM and
  *             MFMA_ROWS_REG paths, for the kernel shapes the tile-layout
  *             table selects, and PREFILL with the direct-load kernel of 2
- *             stages; not with DOT, nor with the SwiGLU epilogue inside
- *             the GEMM).                                                   */
+ *             stages and the wide kernel; not with DOT, nor with the
+ *             SwiGLU epilogue inside the GEMM).                            */
 typedef struct {
   int32_t path;
   int32_t tiles_n;
