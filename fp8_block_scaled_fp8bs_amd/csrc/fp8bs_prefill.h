@@ -802,8 +802,12 @@ __device__ __forceinline__ void pfw_unit(const GemmParams& p, uint8_t* lds_all, 
     const int r = RPI * i + lane / U;
     const int m = m0 + 64 * wm + r;
     const uint4 v = *reinterpret_cast<const uint4*>(ob + r * 16 * U + 16 * (u ^ (r % U)));
-    if (m < p.m)
-      *reinterpret_cast<uint4*>(p.y + (size_t)m * (size_t)p.n + n0 + WCOLS * wn + 8 * u) = v;
+    if (m < p.m) {
+      typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+      __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w},
+                                  reinterpret_cast<u32x4*>(p.y + (size_t)m * (size_t)p.n + n0 +
+                                                           WCOLS * wn + 8 * u));
+    }
   }
 }
 
