@@ -540,8 +540,9 @@ def prefill(args, fp8bs, dev) -> int:
     the fused call (cast + GEMM, two kernels) and the GEMM on pre-quantized
     activations, each as a captured graph of calls over a rotating weight
     pool, plus torch.nn.functional.linear with bf16 weights (hipBLASLt) on the
-    same shape. One JSON line per (shape, m), with TFLOP/s = 2 m n k / time
-    against the dense FP8 peak."""
+    same shape, and the library's FP8 GEMM with one scale per tensor
+    (torch._scaled_mm) on the same codes. One JSON line per (shape, m), with
+    TFLOP/s = 2 m n k / time against the dense FP8 peak."""
     import torch
 
     from workloads import WORKLOADS
@@ -599,6 +600,18 @@ def prefill(args, fp8bs, dev) -> int:
             t_qt = timed(lambda i: fp8bs.gemm_q_tiles(xq, xs, tiles[i % P], pool[i % P][1], out=y,
                                                       workspace=work), steps)
             t_lib = timed(lambda i: torch.nn.functional.linear(x, wbf), steps)
+            # the vendor library's FP8 GEMM on the same codes with one scale
+            # per tensor (hipBLASLt through torch._scaled_mm): not the
+            # block-scaled product, a reference for the FP8 matrix path alone
+            one = torch.ones((), dtype=torch.float32, device=dev)
+            xf8 = xq.view(torch.float8_e4m3fn)
+            t_f8 = None
+            try:
+                t_f8 = timed(lambda i: torch._scaled_mm(
+                    xf8, pool[i % P][0].view(torch.float8_e4m3fn).t(), scale_a=one, scale_b=one,
+                    out_dtype=torch.bfloat16), steps)
+            except (RuntimeError, TypeError):
+                pass
             cfg = fp8bs.select_config(m, n, k)
             print(json.dumps({
                 "mode": "prefill", "shape": name, "m": m, "n": n, "k": k,
@@ -608,6 +621,8 @@ def prefill(args, fp8bs, dev) -> int:
                 "pct_of_fp8_peak_gemm_q": round(100 * flop / (t_q * 1e6) / MFMA_FP8_PEAK_TFLOPS, 2),
                 "us_gemm_q_tiles": round(t_qt, 2), "TFLOPs_gemm_q_tiles": round(flop / (t_qt * 1e6), 1),
                 "bf16_library_us": round(t_lib, 2), "bf16_library_TFLOPs": round(flop / (t_lib * 1e6), 1),
+                "fp8_per_tensor_library_us": round(t_f8, 2) if t_f8 else None,
+                "fp8_per_tensor_library_TFLOPs": round(flop / (t_f8 * 1e6), 1) if t_f8 else None,
                 "timing": f"captured graph of {steps} calls over a {P}-weight pool, best of 3 replays"}),
                 flush=True)
             del x, xq, xs, y, work
