@@ -654,6 +654,9 @@ def main() -> int:
     ap.add_argument("--prefill-m", default="128,512,2048,8192", help="m values of --prefill")
     ap.add_argument("--prefill-shapes", default="square,mlp_up,mlp_down",
                     help="weight shapes of --prefill")
+    ap.add_argument("--config", default="",
+                    help="explicit GEMM configuration 'path,tiles_n,waves_n,waves_k,depth[,split_k[,reduce]]' "
+                         "for the GEMM line instead of the table's (analysis runs)")
     ap.add_argument("--weight-layout", default="tiles", choices=("tiles", "rows"),
                     help="weight codes for the GEMM and step-mix modes: the tile layout "
                          "(fp8bs_pack_weight, rearranged once before timing) or row-major")
@@ -751,6 +754,15 @@ def main() -> int:
     cfg = fp8bs.tiles_select_config(m, n, k) if tiles else fp8bs.select_config(m, n, k)
     gemm = fp8bs.gemm_tiles if tiles else fp8bs.gemm
     ws_bytes = fp8bs.workspace_bytes(m, n, k)
+    if args.config:
+        # an explicit kernel configuration instead of the table's (analysis runs)
+        from fp8_block_scaled_fp8bs_amd import GemmConfig
+        cfg = GemmConfig(*[int(v) for v in args.config.split(",")],
+                         weight_layout=fp8bs.LAYOUT_TILES if tiles else fp8bs.LAYOUT_ROWS)
+        ws_bytes = fp8bs.config_workspace_bytes(cfg, m, n, k)
+
+        def gemm(x_, wq_, wsc_, out, workspace):
+            return fp8bs.gemm_ex(cfg, wq_, wsc_, x=x_, out=out, workspace=workspace)
     workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
     print(f"# pool {pool_n} weights ({pool_n * code_bytes / 2**30:.2f} GiB), config {cfg}",
@@ -900,7 +912,8 @@ def main() -> int:
             "kernel": {"path": PATH_NAMES.get(cfg.path, str(cfg.path)), "tiles_n": cfg.tiles_n,
                        "waves_n": cfg.waves_n, "waves_k": cfg.waves_k, "depth": cfg.depth,
                        "split_k": cfg.split_k,
-                       "launches_per_gemm": 2 if cfg.split_k > 1 and cfg.reduce == 0 else 1},
+                       "launches_per_gemm": 2 if cfg.split_k > 1 and cfg.reduce == 0 else 1,
+                       "explicit": bool(args.config)},
             "weight_layout": layout,
             "timing": (f"hip graph replay, K steps timed with {timing_note}" if graph_ms is not None
                        else "stream launches"),
