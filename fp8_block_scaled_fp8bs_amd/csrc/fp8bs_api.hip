@@ -222,6 +222,28 @@ bool pfw_config(const fp8bs_gemm_config& c) {
   return c.path == FP8BS_PATH_PREFILL && (c.tiles_n == PF_WIDE || c.tiles_n == PF_WIDE_1D);
 }
 
+// 1-D schedule of the wide prefill kernel (tiles_n PF_WIDE_1D): whole
+// 256 x 256 tiles in complete rounds of kTableCUs workgroups; the tiles left
+// over run as two 128-column halves each when those fit in half a round,
+// else as whole tiles in a last, partly filled round.
+struct PfwPlan {
+  int64_t full, units;
+};
+PfwPlan pfw_plan(int waves_m, int64_t m, int64_t n) {
+  const int64_t tm = pfw_tile_m(waves_m);
+  const int64_t tiles = ((n + PFW_TILE_N - 1) / PFW_TILE_N) * ((m + tm - 1) / tm);
+  PfwPlan q;
+  q.full = tiles / kTableCUs * kTableCUs;
+  const int64_t rem = tiles - q.full;
+  if (rem > 0 && 2 * rem <= kTableCUs) {
+    q.units = q.full + 2 * rem;
+  } else {
+    q.full = tiles;
+    q.units = tiles;
+  }
+  return q;
+}
+
 // Output columns per workgroup of a grid configuration (the row-range
 // path divides n by the compute-unit count at launch instead).
 int config_rows(const fp8bs_gemm_config& c) {
@@ -393,7 +415,9 @@ bool select_config(int64_t m, int64_t n, int64_t k, fp8bs_gemm_config* out, bool
     // fewer (MLP up m = 128: 80 against 71 us).
     const int64_t wtiles = ((n + PFW_TILE_N - 1) / PFW_TILE_N) * ((m + 255) / 256);
     if (wtiles >= 150) {
-      *out = make_cfg(FP8BS_PATH_PREFILL, PF_WIDE_1D, 2, 4, 2, 1);
+      // (the grid schedule where the 1-D grid would pass 2^31 workgroups)
+      const bool one_d = pfw_plan(4, m, n).units <= INT32_MAX;
+      *out = make_cfg(FP8BS_PATH_PREFILL, one_d ? PF_WIDE_1D : PF_WIDE, 2, 4, 2, 1);
       out->weight_layout = layout;
       return true;
     }
@@ -510,28 +534,6 @@ size_t cfg_partial_bytes(const fp8bs_gemm_config& c, int64_t m, int64_t n) {
 // are written to the workspace first.
 size_t prefill_x_bytes(int64_t m, int64_t k) {
   return (size_t)((m * k + 255) / 256 * 256) + (size_t)((m * (k / BLK) * 4 + 15) / 16 * 16);
-}
-
-// 1-D schedule of the wide prefill kernel (tiles_n PF_WIDE_1D): whole
-// 256 x 256 tiles in complete rounds of kTableCUs workgroups; the tiles left
-// over run as two 128-column halves each when those fit in half a round,
-// else as whole tiles in a last, partly filled round.
-struct PfwPlan {
-  int64_t full, units;
-};
-PfwPlan pfw_plan(int waves_m, int64_t m, int64_t n) {
-  const int64_t tm = pfw_tile_m(waves_m);
-  const int64_t tiles = ((n + PFW_TILE_N - 1) / PFW_TILE_N) * ((m + tm - 1) / tm);
-  PfwPlan q;
-  q.full = tiles / kTableCUs * kTableCUs;
-  const int64_t rem = tiles - q.full;
-  if (rem > 0 && 2 * rem <= kTableCUs) {
-    q.units = q.full + 2 * rem;
-  } else {
-    q.full = tiles;
-    q.units = tiles;
-  }
-  return q;
 }
 
 // Prefill workspace: the cast activations (fused call), then the split
@@ -651,8 +653,10 @@ fp8bs_status gemm_impl(bool fused, const void* x_bf16, const uint8_t* x_fp8,
   if (c.split_k < 1 || c.split_k > 64 || c.split_k > kbn) return FP8BS_ERR_CONFIG;
   if (c.path == FP8BS_PATH_PREFILL ? c.reduce != FP8BS_REDUCE_KERNEL : m > kMaxDecodeM)
     return FP8BS_ERR_CONFIG;
-  // the 1-D schedule runs every tile over the whole K range
-  if (c.path == FP8BS_PATH_PREFILL && c.tiles_n == PF_WIDE_1D && c.split_k != 1)
+  // the 1-D schedule runs every tile over the whole K range, one workgroup
+  // per whole or half tile on a one-dimensional grid
+  if (c.path == FP8BS_PATH_PREFILL && c.tiles_n == PF_WIDE_1D &&
+      (c.split_k != 1 || pfw_plan(c.waves_k, m, n).units > INT32_MAX))
     return FP8BS_ERR_CONFIG;
   // row-range paths: split only on MFMA_ROWS, with the reduce kernel
   if (is_row_range(c.path) &&

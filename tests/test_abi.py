@@ -329,3 +329,26 @@ def test_tile_layout_config_rules(lib):
     c = GemmConfig(2, 2, 2, 4, 4, weight_layout=fp8bs.LAYOUT_TILES)._c()  # no DOT tile build
     r = lib.fp8bs_gemm_ex(P, None, None, 1, P, P, 512, 1024, P, None, 0, ctypes.byref(c), None)
     assert r == E_CFG
+
+
+def test_prefill_wide_configs_checked_before_any_launch(lib):
+    """The wide prefill kernel's 1-D schedule (tiles_n 4) takes no K split,
+    and it launches one workgroup per whole or half 256 x 256 tile on a
+    one-dimensional grid, so a shape with more than 2^31 - 1 such
+    workgroups is a configuration error for it; the table picks the grid
+    schedule (tiles_n 3) there instead. All of this is decided before any
+    device call."""
+    import fp8_block_scaled_fp8bs_amd as fp8bs
+    c = fp8bs._Config(5, 4, 2, 4, 2, 2, 0, 0, 0)             # 1-D schedule with a K split
+    assert lib.fp8bs_gemm_ex(None, P, P, 4096, P, P, 5120, 5120, P, None, 0, ctypes.byref(c),
+                             None) == E_CFG
+    m, n = 1 << 20, (1 << 31) - 128                           # 4096 x 8,388,608 whole tiles
+    c = fp8bs._Config(5, 4, 2, 4, 2, 1, 0, 0, 0)
+    assert lib.fp8bs_gemm_ex(None, P, P, m, P, P, n, 128, P, None, 0, ctypes.byref(c),
+                             None) == E_CFG
+    cfg = fp8bs.select_config(m, n, 128)
+    assert (cfg.path, cfg.tiles_n, cfg.split_k) == (fp8bs.PATH_PREFILL, 3, 1)
+    cfg = fp8bs.select_config(8192, 5120, 5120)
+    assert (cfg.path, cfg.tiles_n, cfg.waves_n, cfg.waves_k, cfg.split_k) == (fp8bs.PATH_PREFILL, 4, 2, 4, 1)
+    cfg = fp8bs.select_config(1024, 5120, 5120)               # 80 tiles: the 128 x 128 kernel
+    assert (cfg.path, cfg.tiles_n) == (fp8bs.PATH_PREFILL, 1)
