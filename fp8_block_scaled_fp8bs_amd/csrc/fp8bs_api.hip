@@ -408,16 +408,30 @@ bool select_config(int64_t m, int64_t n, int64_t k, fp8bs_gemm_config* out, bool
   if (swiglu && n % (2 * BLK)) return false;
   if (m > kMaxDecodeM && n > 0 && k > 0) {
     // prefill sizes with at least 150 256 x 256 output tiles (m n >= about
-    // 9.8 M): the wide kernel (8 waves, 64 x 128 outputs each) on the 1-D
+    // 9.8 M): the wide kernel (8 waves, 16 JM x 128 outputs each) on the 1-D
     // schedule. Measured on MI355X at m = 128 .. 8192 on the square, MLP-up
-    // and MLP-down weights: faster from 160 tiles up (square m = 2048:
-    // 76 against 84 us; m = 8192: 217 against 260 us), slower at 136 and
-    // fewer (MLP up m = 128: 80 against 71 us).
+    // and MLP-down weights: faster than the 128 x 128 kernel from 160 tiles
+    // up (square m = 2048: 70 against 84 us; m = 8192: 214 against 260 us),
+    // slower at 136 and fewer (MLP up m = 128: 80 against 71 us). Between
+    // 256-row (JM = 4) and 192-row (JM = 3) tiles, the one with fewer rounds
+    // of 256 workgroups, a 192-row tile counted as 0.8 of a 256-row one and
+    // a round of half tiles as 0.6 of a round (the measured ratios): 192 rows
+    // at square and MLP-down m = 2048 (70 against 74 us, 208 against
+    // 226 us), 256 rows at m = 8192 and on MLP up.
     const int64_t wtiles = ((n + PFW_TILE_N - 1) / PFW_TILE_N) * ((m + 255) / 256);
     if (wtiles >= 150) {
+      auto cost = [&](int jm) {
+        const int64_t tm = pfw_tile_m(jm);
+        const int64_t tiles = ((n + PFW_TILE_N - 1) / PFW_TILE_N) * ((m + tm - 1) / tm);
+        const int64_t full = tiles / kTableCUs * kTableCUs, rem = tiles - full;
+        double r = (double)(full / kTableCUs);
+        if (rem > 0) r += 2 * rem <= kTableCUs ? 0.6 : 1.0;
+        return jm == 3 ? 0.8 * r : r;
+      };
+      const int jm = cost(3) < cost(4) ? 3 : 4;
       // (the grid schedule where the 1-D grid would pass 2^31 workgroups)
-      const bool one_d = pfw_plan(4, m, n).units <= INT32_MAX;
-      *out = make_cfg(FP8BS_PATH_PREFILL, one_d ? PF_WIDE_1D : PF_WIDE, 2, 4, 2, 1);
+      const bool one_d = pfw_plan(jm, m, n).units <= INT32_MAX;
+      *out = make_cfg(FP8BS_PATH_PREFILL, one_d ? PF_WIDE_1D : PF_WIDE, 2, jm, 2, 1);
       out->weight_layout = layout;
       return true;
     }
@@ -745,7 +759,7 @@ fp8bs_status gemm_impl(bool fused, const void* x_bf16, const uint8_t* x_fp8,
       const int64_t tm = pfw_tile_m(c.waves_k);
       grid = dim3((unsigned)((n + PFW_TILE_N - 1) / PFW_TILE_N), (unsigned)((m + tm - 1) / tm),
                   (unsigned)c.split_k);
-      block = dim3(64 * c.waves_n * c.waves_k);
+      block = dim3(512);  // 8 waves; waves_k gives the rows per wave (16 waves_k)
       if (c.tiles_n == PF_WIDE_1D) {
         const PfwPlan q = pfw_plan(c.waves_k, m, n);
         grid = dim3((unsigned)q.units);

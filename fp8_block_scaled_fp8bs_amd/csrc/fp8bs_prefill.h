@@ -499,39 +499,41 @@ __global__ __launch_bounds__(128 * WN, WN == 2 ? 2 : 1) void gemm_prefill_dma_ke
 
 // Wide wave tiles. In the kernel above each wave owns 64 x 64 outputs, so per
 // K block it reads 16 KB of operands out of LDS for 2 MFLOP, and a 128 x 128
-// workgroup tile fetches 32 KB from L2 per 4 MFLOP. Here each wave owns a
-// 64 (m) x 128 (n) part -- 4 activation by 8 weight subtiles, one whole
-// weight block row, so the weight scale is one value per wave and block --
-// and the workgroup, WM waves along m by 2 along n, a (64 WM) x 256 tile:
-// with WM = 4, 8 waves on 256 x 256 read 24 KB of LDS per 4 MFLOP and fetch
-// 64 KB per 16 MFLOP, half the L2 traffic per product of the 128 x 128 tile.
-// One workgroup per compute unit (the two stages take 130 KB of LDS). A
-// workgroup can also take a half tile, (64 WM) x 128, with 64 x 64 per wave
-// (the last tile of an odd number of 128-column blocks, and the tail of the
-// one-dimensional schedule below). The stages are filled by direct loads as
-// in gemm_prefill_dma_kernel: every wave issues the same number per stage
-// (the activation scales, WM loads of 256 bytes, are loaded by waves w and
-// w + WM alike, which write the same bytes). Per block, a wave reads its 4
-// activation operands, then for each weight subtile one operand and 4
-// MFMAs, and rescales each subtile's products into the fp32 accumulators one
-// subtile later; the wait and barrier that publish the next block come after
-// the block's last operand read, so the last MFMAs run while the waves meet.
+// workgroup tile fetches 32 KB from L2 per 4 MFLOP. Here 8 waves, 4 along m
+// by 2 along n, own a 256-column tile; each wave owns 16 JM rows (JM = 4 or
+// 3 activation subtiles) by 128 columns (8 weight subtiles, one whole weight
+// block row, so the weight scale is one value per wave and block). With
+// JM = 4, 256 x 256 tiles read 24 KB of LDS per 4 MFLOP and fetch 64 KB per
+// 16 MFLOP, half the L2 traffic per product of the 128 x 128 tile; JM = 3
+// (192-row tiles) makes 4/3 as many tiles, for shapes where 256-row tiles
+// leave compute units idle. One workgroup per compute unit (two stages take
+// up to 130 KB of LDS). A workgroup can also take a half tile, 128 columns
+// with 16 JM x 64 per wave (the last tile of an odd number of 128-column
+// blocks, and the tail of the one-dimensional schedule below). The stages
+// are filled by direct loads as in gemm_prefill_dma_kernel, issued by one
+// loader wave per SIMD. Per block, a wave reads its activation operands,
+// then for each weight subtile one operand and JM MFMAs, and rescales each
+// subtile's products into the fp32 accumulators one subtile later; the wait
+// and barrier that publish the next block come after the block's last
+// operand read, so the last MFMAs run while the waves meet.
 constexpr int PFW_TILE_N = 256;  // output columns of a whole tile
 constexpr int PF_WIDE = 3;       // tiles_n of a configuration: this kernel, grid schedule
 constexpr int PF_WIDE_1D = 4;    // tiles_n of a configuration: this kernel, 1-D schedule
-__host__ __device__ constexpr int pfw_tile_m(int wm) { return 64 * wm; }
-__host__ __device__ constexpr int pfw_stage_bytes(int wm) {
-  return PFW_TILE_N * BLK + pfw_tile_m(wm) * BLK + pfw_tile_m(wm) * 4;
+// JM: activation subtiles (16 rows) per wave, 4 or 3; 4 waves along m, so
+// a tile has 64 JM rows (256 or 192).
+__host__ __device__ constexpr int pfw_tile_m(int jm) { return 64 * jm; }
+__host__ __device__ constexpr int pfw_stage_bytes(int jm) {
+  return PFW_TILE_N * BLK + pfw_tile_m(jm) * BLK + pfw_tile_m(jm) * 4;
 }
-__host__ __device__ constexpr int pfw_lds_bytes(int wm, int stages) {
-  return stages * pfw_stage_bytes(wm);
+__host__ __device__ constexpr int pfw_lds_bytes(int jm, int stages) {
+  return stages * pfw_stage_bytes(jm);
 }
 // Waves that issue the stage loads (one per SIMD), and the loads each issues
 // per stage with NT weight subtiles per wave (8: whole tile, 4: half tile):
 // 4 NT / 4 weight pieces of 1 KB, the activation pieces, one scale piece.
 constexpr int PFW_LOADERS = 4;
-__host__ __device__ constexpr int pfw_per_stage(int wm, int nt) {
-  return 4 * nt / PFW_LOADERS + pfw_tile_m(wm) * BLK / 1024 / PFW_LOADERS + 1;
+__host__ __device__ constexpr int pfw_per_stage(int jm, int nt) {
+  return 4 * nt / PFW_LOADERS + pfw_tile_m(jm) * BLK / 1024 / PFW_LOADERS + 1;
 }
 
 // Tile q of the grouped order -> (n tile, m tile): groups of up to 8 m tiles,
@@ -548,7 +550,7 @@ __device__ __forceinline__ void pfw_tile_xy(int q, int tiles_n, int tiles_m, int
 
 // Work of a workgroup: output columns n0 .. n0 + 255 (half: n0 .. n0 + 127),
 // rows m0 .., K blocks kb0 .. kb1 - 1.
-// Grid schedule (p.pf_1d == 0): grid (ceil(n / 256), ceil(m / (64 WM)),
+// Grid schedule (p.pf_1d == 0): grid (ceil(n / 256), ceil(m / (64 JM)),
 // split), the tile order of pf_tile_order, split z of K; a tile of one
 // 128-column block is a half tile.
 // 1-D schedule (p.pf_1d == 1): p.pf_full whole tiles, which fill complete
@@ -603,15 +605,17 @@ __device__ __forceinline__ void pf_static_for(F& f) {
 }
 
 // One unit (whole tile, NT = 8, or half tile, NT = 4) of the kernel below.
-template <int WM, int S, bool PK, int NT, bool LOADER>
+template <int JM, int S, bool PK, int NT, bool LOADER>
 __device__ __forceinline__ void pfw_unit(const GemmParams& p, uint8_t* lds_all, const PfwWork& work) {
-  constexpr int STAGE = pfw_stage_bytes(WM);
-  constexpr int TM = pfw_tile_m(WM);
+  constexpr int STAGE = pfw_stage_bytes(JM);
+  constexpr int TM = pfw_tile_m(JM);
+  constexpr int WR = 16 * JM;               // activation rows of a wave
   constexpr int LW = PFW_LOADERS;
   constexpr int WQ = 4 * NT / LW;           // weight pieces (1 KB) per loader and stage
   constexpr int XQ = TM * BLK / 1024 / LW;  // activation pieces per loader and stage
-  constexpr int PER = pfw_per_stage(WM, NT);
-  static_assert(PER == WQ + XQ + 1 && TM * 4 == 256 * LW, "one scale piece per loader");
+  constexpr int PER = pfw_per_stage(JM, NT);
+  static_assert(PER == WQ + XQ + 1 && TM * BLK % (1024 * LW) == 0, "equal loads per loader");
+  static_assert(TM * 4 == 256 * JM && JM <= LW, "at most one 256-byte scale piece per loader");
   constexpr int WCOLS = 16 * NT;         // output columns of a wave
   constexpr int XOFF = PFW_TILE_N * BLK;  // activation rows within a stage
   constexpr int SOFF = XOFF + TM * BLK;   // activation scales within a stage
@@ -627,7 +631,8 @@ __device__ __forceinline__ void pfw_unit(const GemmParams& p, uint8_t* lds_all, 
 
   // Loader wave w < LW copies pieces q = w + LW i of the stage's weight rows
   // (1 KB: rows 8q .. 8q+7, or half q % 2 of 2 KB tile q / 2) and of its
-  // activation rows, and scale piece w (rows 64 w ..). Every piece q a
+  // activation rows, and scale piece w (rows 64 w ..; with JM = 3 pieces,
+  // loader 3 loads piece 2 again, the same bytes). Every piece q a
   // loader takes has q % 2 = w % 2, so one lane offset serves all of them:
   // row 8q + lane / 8, 16-byte segment (lane % 8) ^ (lane / 8) ^ (q % 2)
   // (the swizzle of pf_swz); the rest of each weight offset is uniform and
@@ -636,7 +641,8 @@ __device__ __forceinline__ void pfw_unit(const GemmParams& p, uint8_t* lds_all, 
   const uint32_t xseg = 16u * (uint32_t)((lane & 7) ^ (lane >> 3) ^ (wave & 1));
   const uint32_t wlo = PK ? 16u * (uint32_t)lane : (uint32_t)(lane >> 3) * (uint32_t)p.k + xseg;
   const int xlim = p.m - 1 - m0;  // last activation row of the tile
-  const int sr = 64 * wave + lane;
+  const int sq = wave < JM ? wave : JM - 1;  // scale piece of this loader
+  const int sr = 64 * sq + lane;
   const uint32_t so = (uint32_t)(sr <= xlim ? sr : xlim) * (uint32_t)p.kbn * 4u;
   const uint8_t* wbase = PK ? p.wq + (size_t)(n0 >> 4) * (size_t)p.kbn * 2048u
                             : p.wq + (size_t)n0 * (size_t)p.k;
@@ -673,28 +679,28 @@ __device__ __forceinline__ void pfw_unit(const GemmParams& p, uint8_t* lds_all, 
         const uint32_t off = (uint32_t)(r <= xlim ? r : xlim) * (uint32_t)p.k + xseg;
         dma16(st + (uint32_t)XOFF + (uint32_t)q * 1024u, xb, off);
       }
-      dma4(st + (uint32_t)SOFF + (uint32_t)wave * 256u, sbase + kb, so);
+      dma4(st + (uint32_t)SOFF + (uint32_t)sq * 256u, sbase + kb, so);
     }
   };
 
-  f32x4 acc[NT][4];
+  f32x4 acc[NT][JM];
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < JM; ++j) acc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // The activation operands and the scale products of block kb, from its stage.
-  i32x8 bop[4];
-  float sc[4];
+  i32x8 bop[JM];
+  float sc[JM];
   auto read_x = [&](const uint8_t* st) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bop[j] = pf_swz_operand(st + XOFF, 64 * wm + 16 * j + l16, g);
+    for (int j = 0; j < JM; ++j) bop[j] = pf_swz_operand(st + XOFF, WR * wm + 16 * j + l16, g);
   };
   auto read_sc = [&](int kb, const uint8_t* st) {
     const float* sl = reinterpret_cast<const float*>(st + SOFF);
     const float sw = load_invariant(wsrow, (size_t)kb);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) sc[j] = sl[64 * wm + 16 * j + l16] * sw;
+    for (int j = 0; j < JM; ++j) sc[j] = sl[WR * wm + 16 * j + l16] * sw;
   };
 
   // S - 1 stages in flight (block kb0 + S - 1 is loaded during block kb0),
@@ -721,19 +727,19 @@ __device__ __forceinline__ void pfw_unit(const GemmParams& p, uint8_t* lds_all, 
     constexpr int SP = (ST + S - 1) % S;
     const uint8_t* wl = lds_all + ST * STAGE;
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    f32x4 pb[2][4];
+    f32x4 pb[2][JM];
     auto sub = [&](auto tc) {
       constexpr int T = decltype(tc)::value;
       if constexpr (T == 0) issue(kb + S - 1, SP);
       const i32x8 aop = PK ? pf_tile_operand(wl, NT * wn + T, lane)
                            : pf_swz_operand(wl, WCOLS * wn + 16 * T + l16, g);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < JM; ++j)
         pb[T & 1][j] =
             __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop[j], z, 0, 0, 0, 0, 0, 0);
       if constexpr (T > 0) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < JM; ++j)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             acc[T - 1][j][i] = __builtin_fmaf(pb[(T - 1) & 1][j][i], sc[j], acc[T - 1][j][i]);
@@ -744,7 +750,7 @@ __device__ __forceinline__ void pfw_unit(const GemmParams& p, uint8_t* lds_all, 
     const uint8_t* next = lds_all + ((ST + 1) % S) * STAGE;
     read_x(next);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < JM; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         acc[NT - 1][j][i] = __builtin_fmaf(pb[(NT - 1) & 1][j][i], sc[j], acc[NT - 1][j][i]);
@@ -761,8 +767,8 @@ __device__ __forceinline__ void pfw_unit(const GemmParams& p, uint8_t* lds_all, 
 
   if (p.out == OUT_PARTIAL) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int m = m0 + 64 * wm + 16 * j + l16;
+    for (int j = 0; j < JM; ++j) {
+      const int m = m0 + WR * wm + 16 * j + l16;
       if (m < p.m) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
@@ -774,7 +780,7 @@ __device__ __forceinline__ void pfw_unit(const GemmParams& p, uint8_t* lds_all, 
     }
     return;
   }
-  // bf16 output: each wave stages its 64 x WCOLS part in its own LDS
+  // bf16 output: each wave stages its WR x WCOLS part in its own LDS
   // (row r: 2 WCOLS bytes in U = 2 NT 16-byte units, unit u at
   // u ^ (r mod U), so both the 8-byte writes of 16 rows and the 16-byte
   // reads of whole rows spread over the banks), then writes whole row
@@ -782,9 +788,9 @@ __device__ __forceinline__ void pfw_unit(const GemmParams& p, uint8_t* lds_all, 
   // 32-byte pieces of 16 rows.
   constexpr int U = 2 * NT;       // 16-byte units per staged row
   constexpr int RPI = 64 / U;     // rows per store instruction
-  uint8_t* ob = lds_all + wave * (64 * 16 * U);
+  uint8_t* ob = lds_all + wave * (WR * 16 * U);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < JM; ++j) {
     const int r = 16 * j + l16;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -798,9 +804,9 @@ __device__ __forceinline__ void pfw_unit(const GemmParams& p, uint8_t* lds_all, 
   // complete in order)
   const int u = lane % U;
 #pragma unroll
-  for (int i = 0; i < 64 / RPI; ++i) {
+  for (int i = 0; i < WR / RPI; ++i) {
     const int r = RPI * i + lane / U;
-    const int m = m0 + 64 * wm + r;
+    const int m = m0 + WR * wm + r;
     const uint4 v = *reinterpret_cast<const uint4*>(ob + r * 16 * U + 16 * (u ^ (r % U)));
     if (m < p.m) {
       typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -811,26 +817,27 @@ __device__ __forceinline__ void pfw_unit(const GemmParams& p, uint8_t* lds_all, 
   }
 }
 
-// pfw_lds_bytes(WM, S) of dynamic LDS; 128 WM threads; grid as pfw_work.
-template <int WM, int S, bool PK = false>
-__global__ __launch_bounds__(128 * WM, 1) void gemm_prefill_wide_kernel(GemmParams p) {
-  static_assert(WM == 4, "8 waves: 4 along m, 2 along n");
-  static_assert(2 * WM * 16384 <= pfw_lds_bytes(WM, S), "output staging fits in the stages");
-  static_assert(S >= 2 && (S - 1) * pfw_per_stage(WM, 8) <= 63, "vmcnt range");
+// pfw_lds_bytes(JM, S) of dynamic LDS; 512 threads (8 waves: 4 along m,
+// 2 along n); grid as pfw_work.
+template <int JM, int S, bool PK = false>
+__global__ __launch_bounds__(512, 1) void gemm_prefill_wide_kernel(GemmParams p) {
+  static_assert(JM == 3 || JM == 4, "48 or 64 activation rows per wave");
+  static_assert(8 * 16 * JM * 256 <= pfw_lds_bytes(JM, S), "output staging fits in the stages");
+  static_assert(S >= 2 && (S - 1) * pfw_per_stage(JM, 8) <= 63, "vmcnt range");
   extern __shared__ __align__(16) uint8_t lds_all[];
-  const PfwWork work = pfw_work<pfw_tile_m(WM)>(p);
+  const PfwWork work = pfw_work<pfw_tile_m(JM)>(p);
   if (work.n0 >= p.n) return;  // the empty second half of a one-block tile
   const bool loader = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) < PFW_LOADERS;
   if (work.half) {
     if (loader)
-      pfw_unit<WM, S, PK, 4, true>(p, lds_all, work);
+      pfw_unit<JM, S, PK, 4, true>(p, lds_all, work);
     else
-      pfw_unit<WM, S, PK, 4, false>(p, lds_all, work);
+      pfw_unit<JM, S, PK, 4, false>(p, lds_all, work);
   } else {
     if (loader)
-      pfw_unit<WM, S, PK, 8, true>(p, lds_all, work);
+      pfw_unit<JM, S, PK, 8, true>(p, lds_all, work);
     else
-      pfw_unit<WM, S, PK, 8, false>(p, lds_all, work);
+      pfw_unit<JM, S, PK, 8, false>(p, lds_all, work);
   }
 }
 

@@ -187,11 +187,11 @@ enum { FP8BS_LAYOUT_ROWS = 0, FP8BS_LAYOUT_TILES = 1 };
  *             block ahead, depth 2..4 = a ring of LDS stages filled by
  *             direct loads, refilled when the next block starts (tiles_n
  *             1) or once every wave holds a block's operands (tiles_n 2);
- *             with tiles_n 3 or 4, waves_n 2, waves_k 4 and depth 2, the
- *             wide kernel: 8 waves own 256 x 256 output tiles (64 x 128
- *             each), on a grid of tiles with K split over split_k
- *             workgroups (tiles_n 3), or on the 1-D schedule (tiles_n 4,
- *             split_k 1): whole tiles in complete rounds of 256
+ *             with tiles_n 3 or 4, waves_n 2, waves_k 4 or 3 and depth 2,
+ *             the wide kernel: 8 waves own (64 waves_k) x 256 output tiles
+ *             (16 waves_k x 128 each), on a grid of tiles with K split over
+ *             split_k workgroups (tiles_n 3), or on the 1-D schedule
+ *             (tiles_n 4, split_k 1): whole tiles in complete rounds of 256
  *             workgroups, the tiles left over as 128-column halves; or
  *             MFMA_ROWS_REG (the work split of MFMA_ROWS with each wave's
  *             activation operands held in registers instead of LDS, so m up

@@ -86,7 +86,7 @@ def test_prefill_every_variant(fp8bs, variant, m, n, k, split):
     assert np.array_equal(host_bits(y), host_bits(y2))
 
 
-WIDE = [(4, 2)]  # (waves along m, LDS stages) of the wide-wave-tile kernels
+WIDE = [(4, 2), (3, 2)]  # (activation subtiles per wave, LDS stages) of the wide-wave-tile kernels
 
 
 @pytest.mark.parametrize("layout", ["rows", "tiles"])
@@ -95,8 +95,9 @@ WIDE = [(4, 2)]  # (waves along m, LDS stages) of the wide-wave-tile kernels
                                          (33, 1024, 128, 1), (520, 256, 2560, 2),
                                          (1000, 2176, 640, 1), (257, 128, 256, 1)])
 def test_prefill_wide_wave_tiles(fp8bs, layout, wk, depth, m, n, k, split):
-    """The kernels with 64 x 128 outputs per wave (256 x 256 output tiles,
-    8 waves, grid schedule): ragged m tails, an odd number of 128-column
+    """The kernels with 64 x 128 or 48 x 128 outputs per wave (256 x 256 or
+    192 x 256 output tiles, 8 waves, grid schedule): ragged m tails, an odd
+    number of 128-column
     blocks (the last tile one block wide), split and unsplit, one K block
     (fewer blocks than stages), both weight layouts. Full output against the
     oracle, and the same bits as the 128 x 128 direct-load kernel in the same
@@ -124,24 +125,26 @@ def test_prefill_wide_wave_tiles(fp8bs, layout, wk, depth, m, n, k, split):
     assert np.array_equal(host_bits(y), host_bits(y_q)), "fused cast differs"
 
 
+@pytest.mark.parametrize("jm", [4, 3])
 @pytest.mark.parametrize("layout", ["rows", "tiles"])
 @pytest.mark.parametrize("m,n,k", [(2100, 8320, 384), (4096, 4352, 256), (2100, 12800, 256),
                                    (300, 640, 1280), (33, 128, 256)])
-def test_prefill_wide_1d_schedule(fp8bs, layout, m, n, k):
-    """The 1-D schedule of the wide kernel: whole 256 x 256 tiles in complete
-    rounds of 256 workgroups, the tiles left over as two 128-column halves
-    when those fit in half a round. 2100 x 8320: 33 x 9 = 297 tiles, 41 left
-    over as 82 halves (the last tile column one 128-column block wide, so
-    one half of its tiles is empty; a ragged m tail); 4096 x 4352: 272 tiles,
-    16 left over; 2100 x 12800: 450 tiles, 194 left over (too many: a last
-    round of whole tiles); 300 x 640: 6 tiles, all halves; 33 x 128: one
-    half. Full output against the oracle and the bits of the unsplit
+def test_prefill_wide_1d_schedule(fp8bs, jm, layout, m, n, k):
+    """The 1-D schedule of the wide kernel: whole tiles (256 or 192 rows by
+    256 columns) in complete rounds of 256 workgroups, the tiles left over as
+    two 128-column halves when those fit in half a round. With 256-row tiles:
+    2100 x 8320: 33 x 9 = 297 tiles, 41 left over as 82 halves (the last tile
+    column one 128-column block wide, so one half of its tiles is empty; a
+    ragged m tail); 4096 x 4352: 272 tiles, 16 left over; 2100 x 12800: 450
+    tiles, 194 left over (too many: a last round of whole tiles); 300 x 640:
+    6 tiles, all halves; 33 x 128: one half (192-row tiles: 363, 374, 550, 6
+    and 1 tiles). Full output against the oracle and the bits of the unsplit
     128 x 128 kernel (every tile, whole or half, runs the whole K range with
     the same products rescaled in the same order); the bits repeat over
     graph replays."""
     import dataclasses
     from fp8_block_scaled_fp8bs_amd import GemmConfig
-    cfg = GemmConfig(fp8bs.PATH_PREFILL, 4, 2, 4, 2, 1)
+    cfg = GemmConfig(fp8bs.PATH_PREFILL, 4, 2, jm, 2, 1)
     announce("prefill wide 1-D", cfg, layout, m, n, k)
     x_bits, wq, ws, wq_ref, ws_ref = _problem(fp8bs, m, n, k, 7700 + m + n + k)
     x = dev_bf16(x_bits)
