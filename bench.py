@@ -862,17 +862,18 @@ def main() -> int:
     # GEMM: a graph of K launches over the same rotating pool behind a lead
     # graph. One workgroup of 512 threads per compute unit (or two), each
     # reading a contiguous range with non-temporal 16-byte loads, 2 x depth
-    # in flight per lane. The best configuration is the ceiling.
+    # in flight per lane; or one workgroup of 4 waves per compute unit
+    # requesting its range straight into LDS. The best one is the ceiling.
     sink = torch.zeros(4, dtype=torch.int32, device=dev)
     ceiling = {}
     if not args.eager_only:
-        for blocks, depth in ((256, 4), (256, 8), (256, 16), (512, 4)):
+        for blocks, depth in ((256, 4), (256, 8), (256, 16), (512, 4), (256, 0)):
             def rd(i, blocks=blocks, depth=depth):
                 fp8bs.diag_stream(pool[i % pool_n][0], sink, blocks=blocks, depth=depth)
             ms_r, _ = timed_graph(rd, args.steps)
             us_r = ms_r * 1e3
-            ceiling[f"{blocks}x512_depth{depth}"] = {"us": round(us_r, 3),
-                                                     "GBps": round(code_bytes / (us_r * 1e3), 1)}
+            name = f"{blocks}x256_lds" if depth == 0 else f"{blocks}x512_depth{depth}"
+            ceiling[name] = {"us": round(us_r, 3), "GBps": round(code_bytes / (us_r * 1e3), 1)}
     best = max(ceiling.values(), key=lambda v: v["GBps"]) if ceiling else None
 
     # --- library reference: the same product in bf16 through torch (hipBLASLt)

@@ -453,7 +453,8 @@ def diag_read(t: torch.Tensor, sink: torch.Tensor, blocks: int = 0, stream=None)
 
 def diag_stream(t: torch.Tensor, sink: torch.Tensor, blocks: int = 256, depth: int = 8,
                 stream=None, nbytes: int | None = None) -> None:
-    """Streaming-read ceiling kernel over the first nbytes (default: all) of t."""
+    """Streaming-read ceiling kernel over the first nbytes (default: all) of t
+    (depth 0: direct-to-LDS loads by 4 waves per workgroup)."""
     nb = t.numel() * t.element_size() if nbytes is None else int(nbytes)
     _check(load().fp8bs_diag_stream(t.data_ptr(), nb, sink.data_ptr(), blocks, depth,
                                     _stream(stream)))

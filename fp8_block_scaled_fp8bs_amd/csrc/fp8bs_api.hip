@@ -1155,7 +1155,8 @@ fp8bs_status fp8bs_diag_read(const void* src, size_t bytes, void* sink, int32_t 
 
 fp8bs_status fp8bs_diag_stream(const void* src, size_t bytes, void* sink, int32_t blocks,
                                int32_t depth, void* stream) {
-  if (bytes % 16 || blocks < 1 || (depth != 4 && depth != 8 && depth != 16)) return FP8BS_ERR_SHAPE;
+  if (bytes % 16 || blocks < 1 || (depth != 0 && depth != 4 && depth != 8 && depth != 16))
+    return FP8BS_ERR_SHAPE;
   if (bytes == 0) return FP8BS_OK;
   const int64_t per = ((int64_t)bytes / 16 + blocks - 1) / blocks * 16;
   if (per >= ((int64_t)1 << 31) - (int64_t)3 * 512 * 16 * 16) return FP8BS_ERR_SHAPE;
@@ -1166,6 +1167,12 @@ fp8bs_status fp8bs_diag_stream(const void* src, size_t bytes, void* sink, int32_
   const uint8_t* s8 = static_cast<const uint8_t*>(src);
   int64_t nb = (int64_t)bytes, pr = per;
   uint32_t* sk = static_cast<uint32_t*>(sink);
+  if (depth == 0) {
+    void* largs[] = {&s8, &nb, &pr};
+    g_counts[CNT_DIAG]++;
+    return launch(reinterpret_cast<const void*>(diag_stream_lds_kernel), dim3((unsigned)blocks),
+                  dim3(256), 0, stream, largs);
+  }
   void* args[] = {&s8, &nb, &pr, &sk};
   const void* fn = depth == 4 ? reinterpret_cast<const void*>(diag_stream_kernel<4>)
                    : depth == 8 ? reinterpret_cast<const void*>(diag_stream_kernel<8>)

@@ -438,9 +438,12 @@ fp8bs_status fp8bs_diag_read(const void* src, size_t bytes, void* sink, int32_t 
 /* Streaming-read ceiling over `bytes` bytes (multiple of 16, 16-byte
  * aligned): `blocks` workgroups of 512 threads each read one contiguous
  * range of about bytes/blocks with non-temporal 16-byte loads, 2 * depth
- * loads per lane in flight (depth 4, 8 or 16). The plain read a weight
- * stream could reach at best at this size; sink as for fp8bs_diag_read.
- * bytes/blocks must stay below about 2^31.                                  */
+ * loads per lane in flight (depth 4, 8 or 16); or (depth 0) workgroups of
+ * 4 waves request the range's 1 KB pieces straight into LDS, unpaced
+ * (non-temporal direct-to-LDS loads, one workgroup per compute unit). The
+ * plain read a weight stream could reach at best at this size; sink as for
+ * fp8bs_diag_read (unused with depth 0). bytes/blocks must stay below about
+ * 2^31.                                                                     */
 fp8bs_status fp8bs_diag_stream(const void* src, size_t bytes, void* sink, int32_t blocks,
                                int32_t depth, void* stream);
 
