@@ -517,8 +517,10 @@ __global__ __launch_bounds__(128 * WN, WN == 2 ? 2 : 1) void gemm_prefill_dma_ke
 // and barrier that publish the next block come after the block's last
 // operand read, so the last MFMAs run while the waves meet.
 constexpr int PFW_TILE_N = 256;  // output columns of a whole tile
+constexpr int PFW_NARROW_N = 160;  // output columns of a narrow tile (5 weight subtiles per wave)
 constexpr int PF_WIDE = 3;       // tiles_n of a configuration: this kernel, grid schedule
 constexpr int PF_WIDE_1D = 4;    // tiles_n of a configuration: this kernel, 1-D schedule
+constexpr int PF_WIDE_160 = 5;   // tiles_n of a configuration: narrow tiles, 1-D schedule
 // JM: activation subtiles (16 rows) per wave, 4 or 3; 4 waves along m, so
 // a tile has 64 JM rows (256 or 192).
 __host__ __device__ constexpr int pfw_tile_m(int jm) { return 64 * jm; }
@@ -595,6 +597,24 @@ __device__ __forceinline__ PfwWork pfw_work(const GemmParams& p) {
   return w;
 }
 
+// Work of a workgroup on narrow tiles (n a multiple of 160): whole tiles
+// only, one per workgroup of the 1-D grid, in the grouped order with each
+// XCD taking a contiguous eighth of it (as pfw_work's whole tiles).
+template <int TM>
+__device__ __forceinline__ PfwWork pfw_work_narrow(const GemmParams& p) {
+  PfwWork w;
+  int bx, by;
+  const int tiles_n = p.n / PFW_NARROW_N, tiles_m = (p.m + TM - 1) / TM;
+  const int b = blockIdx.x, full = p.pf_full;
+  pfw_tile_xy((full & 7) == 0 ? (b & 7) * (full >> 3) + (b >> 3) : b, tiles_n, tiles_m, bx, by);
+  w.n0 = bx * PFW_NARROW_N;
+  w.m0 = by * TM;
+  w.kb0 = 0;
+  w.kb1 = p.kbn;
+  w.half = false;
+  return w;
+}
+
 // f(integral_constant<I>) for I = I0 .. N-1, in order.
 template <int I, int N, typename F>
 __device__ __forceinline__ void pf_static_for(F& f) {
@@ -604,7 +624,8 @@ __device__ __forceinline__ void pf_static_for(F& f) {
   }
 }
 
-// One unit (whole tile, NT = 8, or half tile, NT = 4) of the kernel below.
+// One unit (whole tile, NT = 8; half tile, NT = 4; narrow tile, NT = 5) of
+// the kernel below.
 template <int JM, int S, bool PK, int NT, bool LOADER>
 __device__ __forceinline__ void pfw_unit(const GemmParams& p, uint8_t* lds_all, const PfwWork& work) {
   constexpr int STAGE = pfw_stage_bytes(JM);
@@ -625,8 +646,14 @@ __device__ __forceinline__ void pfw_unit(const GemmParams& p, uint8_t* lds_all, 
   const int n0 = work.n0, m0 = work.m0;
   const int l16 = lane & 15, g = lane >> 4;
   const int kb0 = work.kb0, last = work.kb1 - 1;
-  // a whole tile holds two weight blocks, one per wave column; a half tile one
-  const float* wsrow = p.ws + (size_t)(n0 / BLK + (NT == 8 ? wn : 0)) * (size_t)p.kbn;
+  // a whole tile holds two weight blocks, one per wave column; a half tile
+  // one; a narrow tile's wave column (80 columns from any multiple of 16)
+  // lies in one block or straddles two (nb0, nb1: the block of its first
+  // and of its last column)
+  const int nbw = NT == 5 ? (n0 + WCOLS * wn) / BLK : n0 / BLK + (NT == 8 ? wn : 0);
+  const float* wsrow = p.ws + (size_t)nbw * (size_t)p.kbn;
+  const int nbw1 = NT == 5 ? (n0 + WCOLS * wn + WCOLS - 1) / BLK : nbw;
+  const float* wsrow1 = p.ws + (size_t)nbw1 * (size_t)p.kbn;
   const uint32_t lds0 = lds_addr(lds_all);
 
   // Loader wave w < LW copies pieces q = w + LW i of the stage's weight rows
@@ -689,18 +716,38 @@ __device__ __forceinline__ void pfw_unit(const GemmParams& p, uint8_t* lds_all, 
 #pragma unroll
     for (int j = 0; j < JM; ++j) acc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // The activation operands and the scale products of block kb, from its stage.
+  // The activation operands and the scale products of block kb, from its
+  // stage. Narrow tiles keep the activation scales and both weight scales
+  // of the wave column, and form each subtile's products where it is
+  // rescaled (the same fp32 product sa * sw).
   i32x8 bop[JM];
   float sc[JM];
+  float sw0 = 0.0f, sw1 = 0.0f;
   auto read_x = [&](const uint8_t* st) {
 #pragma unroll
     for (int j = 0; j < JM; ++j) bop[j] = pf_swz_operand(st + XOFF, WR * wm + 16 * j + l16, g);
   };
   auto read_sc = [&](int kb, const uint8_t* st) {
     const float* sl = reinterpret_cast<const float*>(st + SOFF);
-    const float sw = load_invariant(wsrow, (size_t)kb);
+    if constexpr (NT == 5) {
+      sw0 = load_invariant(wsrow, (size_t)kb);
+      sw1 = load_invariant(wsrow1, (size_t)kb);
 #pragma unroll
-    for (int j = 0; j < JM; ++j) sc[j] = sl[WR * wm + 16 * j + l16] * sw;
+      for (int j = 0; j < JM; ++j) sc[j] = sl[WR * wm + 16 * j + l16];
+    } else {
+      const float sw = load_invariant(wsrow, (size_t)kb);
+#pragma unroll
+      for (int j = 0; j < JM; ++j) sc[j] = sl[WR * wm + 16 * j + l16] * sw;
+    }
+  };
+  // the scale product of subtile T and activation subtile j
+  auto scale = [&](int T, int j) {
+    if constexpr (NT == 5) {
+      const bool first = (n0 + WCOLS * wn + 16 * T) / BLK == nbw;  // wave-uniform
+      return sc[j] * (first ? sw0 : sw1);
+    } else {
+      return sc[j];
+    }
   };
 
   // S - 1 stages in flight (block kb0 + S - 1 is loaded during block kb0),
@@ -739,10 +786,12 @@ __device__ __forceinline__ void pfw_unit(const GemmParams& p, uint8_t* lds_all, 
             __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop[j], z, 0, 0, 0, 0, 0, 0);
       if constexpr (T > 0) {
 #pragma unroll
-        for (int j = 0; j < JM; ++j)
+        for (int j = 0; j < JM; ++j) {
+          const float sj = scale(T - 1, j);
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            acc[T - 1][j][i] = __builtin_fmaf(pb[(T - 1) & 1][j][i], sc[j], acc[T - 1][j][i]);
+            acc[T - 1][j][i] = __builtin_fmaf(pb[(T - 1) & 1][j][i], sj, acc[T - 1][j][i]);
+        }
       }
     };
     pf_static_for<0, NT>(sub);
@@ -750,10 +799,12 @@ __device__ __forceinline__ void pfw_unit(const GemmParams& p, uint8_t* lds_all, 
     const uint8_t* next = lds_all + ((ST + 1) % S) * STAGE;
     read_x(next);
 #pragma unroll
-    for (int j = 0; j < JM; ++j)
+    for (int j = 0; j < JM; ++j) {
+      const float sj = scale(NT - 1, j);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        acc[NT - 1][j][i] = __builtin_fmaf(pb[(NT - 1) & 1][j][i], sc[j], acc[NT - 1][j][i]);
+        acc[NT - 1][j][i] = __builtin_fmaf(pb[(NT - 1) & 1][j][i], sj, acc[NT - 1][j][i]);
+    }
     read_sc(kb + 1 < last ? kb + 1 : last, next);
   };
 
@@ -782,12 +833,18 @@ __device__ __forceinline__ void pfw_unit(const GemmParams& p, uint8_t* lds_all, 
   }
   // bf16 output: each wave stages its WR x WCOLS part in its own LDS
   // (row r: 2 WCOLS bytes in U = 2 NT 16-byte units, unit u at
-  // u ^ (r mod U), so both the 8-byte writes of 16 rows and the 16-byte
-  // reads of whole rows spread over the banks), then writes whole row
-  // segments of 2 WCOLS bytes, 1 KB per store instruction, instead of
-  // 32-byte pieces of 16 rows.
-  constexpr int U = 2 * NT;       // 16-byte units per staged row
-  constexpr int RPI = 64 / U;     // rows per store instruction
+  // u ^ (r mod U), or (u + r) mod U when U is not a power of two, so both
+  // the 8-byte writes of 16 rows and the 16-byte reads of whole rows spread
+  // over the banks), then writes whole row segments of 2 WCOLS bytes, 1 KB
+  // per store instruction (lane l of instruction i: unit 64 i + l of the
+  // wave's WR U units, row by row), instead of 32-byte pieces of 16 rows.
+  constexpr int U = 2 * NT;  // 16-byte units per staged row
+  auto slot = [](int u, int r) {
+    if constexpr ((U & (U - 1)) == 0)
+      return u ^ (r % U);
+    else
+      return (u + r) % U;
+  };
   uint8_t* ob = lds_all + wave * (WR * 16 * U);
 #pragma unroll
   for (int j = 0; j < JM; ++j) {
@@ -795,39 +852,50 @@ __device__ __forceinline__ void pfw_unit(const GemmParams& p, uint8_t* lds_all, 
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int u = 2 * t + (g >> 1);
-      *reinterpret_cast<uint2*>(ob + r * 16 * U + 16 * (u ^ (r % U)) + 8 * (g & 1)) =
+      *reinterpret_cast<uint2*>(ob + r * 16 * U + 16 * slot(u, r) + 8 * (g & 1)) =
           make_uint2(pack_bf16x2(acc[t][j][0], acc[t][j][1]),
                      pack_bf16x2(acc[t][j][2], acc[t][j][3]));
     }
   }
   // the wave reads back only what it wrote itself (LDS accesses of one wave
   // complete in order)
-  const int u = lane % U;
 #pragma unroll
-  for (int i = 0; i < WR / RPI; ++i) {
-    const int r = RPI * i + lane / U;
+  for (int i = 0; i < (WR * U + 63) / 64; ++i) {
+    const int f = 64 * i + lane;
+    const int r = f / U, u = f - (f / U) * U;
     const int m = m0 + WR * wm + r;
-    const uint4 v = *reinterpret_cast<const uint4*>(ob + r * 16 * U + 16 * (u ^ (r % U)));
-    if (m < p.m) {
-      typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-      __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w},
-                                  reinterpret_cast<u32x4*>(p.y + (size_t)m * (size_t)p.n + n0 +
-                                                           WCOLS * wn + 8 * u));
+    if (f < WR * U) {
+      const uint4 v = *reinterpret_cast<const uint4*>(ob + r * 16 * U + 16 * slot(u, r));
+      if (m < p.m) {
+        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+        __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w},
+                                    reinterpret_cast<u32x4*>(p.y + (size_t)m * (size_t)p.n + n0 +
+                                                             WCOLS * wn + 8 * u));
+      }
     }
   }
 }
 
 // pfw_lds_bytes(JM, S) of dynamic LDS; 512 threads (8 waves: 4 along m,
-// 2 along n); grid as pfw_work.
-template <int JM, int S, bool PK = false>
+// 2 along n); grid as pfw_work, or (TW = 160, narrow tiles) pfw_work_narrow.
+template <int JM, int S, bool PK = false, int TW = PFW_TILE_N>
 __global__ __launch_bounds__(512, 1) void gemm_prefill_wide_kernel(GemmParams p) {
   static_assert(JM == 3 || JM == 4, "48 or 64 activation rows per wave");
+  static_assert(TW == PFW_TILE_N || TW == PFW_NARROW_N, "256- or 160-column tiles");
   static_assert(8 * 16 * JM * 256 <= pfw_lds_bytes(JM, S), "output staging fits in the stages");
   static_assert(S >= 2 && (S - 1) * pfw_per_stage(JM, 8) <= 63, "vmcnt range");
   extern __shared__ __align__(16) uint8_t lds_all[];
+  const bool loader = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) < PFW_LOADERS;
+  if constexpr (TW == PFW_NARROW_N) {
+    const PfwWork work = pfw_work_narrow<pfw_tile_m(JM)>(p);
+    if (loader)
+      pfw_unit<JM, S, PK, 5, true>(p, lds_all, work);
+    else
+      pfw_unit<JM, S, PK, 5, false>(p, lds_all, work);
+    return;
+  }
   const PfwWork work = pfw_work<pfw_tile_m(JM)>(p);
   if (work.n0 >= p.n) return;  // the empty second half of a one-block tile
-  const bool loader = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) < PFW_LOADERS;
   if (work.half) {
     if (loader)
       pfw_unit<JM, S, PK, 4, true>(p, lds_all, work);

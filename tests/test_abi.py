@@ -350,5 +350,26 @@ def test_prefill_wide_configs_checked_before_any_launch(lib):
     assert (cfg.path, cfg.tiles_n, cfg.split_k) == (fp8bs.PATH_PREFILL, 3, 1)
     cfg = fp8bs.select_config(8192, 5120, 5120)
     assert (cfg.path, cfg.tiles_n, cfg.waves_n, cfg.waves_k, cfg.split_k) == (fp8bs.PATH_PREFILL, 4, 2, 4, 1)
-    cfg = fp8bs.select_config(1024, 5120, 5120)               # 80 tiles: the 128 x 128 kernel
+    cfg = fp8bs.select_config(1024, 4096, 4096)               # 64 tiles: the 128 x 128 kernel
     assert (cfg.path, cfg.tiles_n) == (fp8bs.PATH_PREFILL, 1)
+
+
+def test_prefill_narrow_tiles_table_and_limits(lib):
+    """Narrow (64 JM) x 160 tiles: the table takes them where n is a multiple
+    of 640 and they make one round of 192 to 256 workgroups (256-row tiles
+    first); elsewhere it keeps the wide or the 128 x 128 kernel. A narrow
+    configuration on n not a multiple of 160, or with a K split, is a
+    configuration error before any device call."""
+    import fp8_block_scaled_fp8bs_amd as fp8bs
+    want = {(2048, 5120, 5120): (5, 4), (2048, 5120, 17408): (5, 4), (1024, 5120, 5120): (5, 3),
+            (1536, 5120, 5120): (5, 4), (4096, 5120, 5120): (4, 4), (8192, 5120, 17408): (4, 4),
+            (2048, 34816, 5120): (4, 4), (512, 5120, 5120): (1, 2)}
+    for (m, n, k), (tn, wk) in want.items():
+        for sel in (fp8bs.select_config, fp8bs.tiles_select_config):
+            cfg = sel(m, n, k)
+            assert cfg.path == fp8bs.PATH_PREFILL and cfg.split_k == 1 or tn == 1, (m, n, k, cfg)
+            assert (cfg.tiles_n, cfg.waves_k) == (tn, wk), (m, n, k, cfg)
+    for n, split in ((5248, 1), (5120, 2)):
+        c = fp8bs._Config(5, 5, 2, 4, 2, split, 0, 0, 0)
+        assert lib.fp8bs_gemm_ex(None, P, P, 2048, P, P, n, 5120, P, None, 0, ctypes.byref(c),
+                                 None) == E_CFG

@@ -181,6 +181,76 @@ def test_prefill_wide_1d_schedule(fp8bs, jm, layout, m, n, k):
         assert np.array_equal(host_bits(out), yb), f"replay {rep_i}"
 
 
+@pytest.mark.parametrize("jm", [4, 3])
+@pytest.mark.parametrize("layout", ["rows", "tiles"])
+@pytest.mark.parametrize("m,n,k", [(300, 640, 1280), (2100, 1280, 384), (33, 640, 256),
+                                   (700, 5120, 256), (520, 1920, 640)])
+def test_prefill_wide_narrow_tiles(fp8bs, jm, layout, m, n, k):
+    """The wide kernel on 160-column tiles (5 weight subtiles per wave; n a
+    multiple of 160 and of 128), every tile a unit of the 1-D grid. A wave's
+    80 columns start at any multiple of 16 and straddle a 128-column scale
+    block in some tiles (columns 80-159, 240-319, ...), so each subtile takes
+    its own weight scale. Shapes with 256-row tiles: 8, 72 and 96 tiles (the
+    per-XCD order), 4 and 36 tiles (the plain order), ragged m tails. Full
+    output against the oracle, the bits of the unsplit 128 x 128 kernel, the
+    fused cast against quantize-then-multiply, and graph replays."""
+    import dataclasses
+    from fp8_block_scaled_fp8bs_amd import GemmConfig
+    cfg = GemmConfig(fp8bs.PATH_PREFILL, 5, 2, jm, 2, 1)
+    announce("prefill narrow tiles", cfg, layout, m, n, k)
+    x_bits, wq, ws, wq_ref, ws_ref = _problem(fp8bs, m, n, k, 7900 + m + n + k)
+    x = dev_bf16(x_bits)
+    w = wq
+    if layout == "tiles":
+        cfg = dataclasses.replace(cfg, weight_layout=fp8bs.LAYOUT_TILES)
+        w = fp8bs.pack_weight(wq)
+    y = fp8bs.gemm_ex(cfg, w, ws, x=x)
+    y1 = fp8bs.gemm_ex(GemmConfig(fp8bs.PATH_PREFILL, 1, 2, 2, 2, 1), wq, ws, x=x)
+    xq, xs = fp8bs.quantize_act(x)
+    yq = fp8bs.gemm_ex(cfg, w, ws, x_q=xq, x_s=xs)
+    torch.cuda.synchronize()
+    yb = host_bits(y)
+    xq_ref, xs_ref = oracle.quantize_act_ref(x_bits)
+    rep = oracle.tolerance_report(yb, oracle.gemm_ref(xq_ref, xs_ref, wq_ref, ws_ref), **TOL)
+    assert rep["finite"] and rep["n_bad"] == 0, rep
+    assert np.array_equal(yb, host_bits(y1)), "differs from the 128 x 128 kernel"
+    assert np.array_equal(yb, host_bits(yq)), "fused cast differs"
+    out = torch.empty_like(y)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fp8bs.gemm_ex(cfg, w, ws, x_q=xq, x_s=xs, out=out, stream=s)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fp8bs.gemm_ex(cfg, w, ws, x_q=xq, x_s=xs, out=out)
+    for rep_i in range(3):
+        out.fill_(0)
+        fp8bs.gemm_ex(cfg, w, ws, x_q=xq, x_s=xs)  # eager work between replays
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host_bits(out), yb), f"replay {rep_i}"
+
+
+def test_prefill_narrow_tiles_rejected_off_shape(fp8bs):
+    """Narrow tiles need n to be a multiple of 160 and run unsplit: other
+    configurations are errors before any launch."""
+    from fp8_block_scaled_fp8bs_amd import Fp8bsError, GemmConfig
+    before = fp8bs.launch_count("gemm_mfma")
+    x_bits, wq, ws, _, _ = _problem(fp8bs, 64, 256, 512, 7801)
+    for cfg in (GemmConfig(fp8bs.PATH_PREFILL, 5, 2, 4, 2, 1), GemmConfig(fp8bs.PATH_PREFILL, 5, 2, 3, 2, 2)):
+        with pytest.raises(Fp8bsError) as e:
+            fp8bs.gemm_ex(cfg, wq, ws, x=dev_bf16(x_bits))
+        assert e.value.status == 7
+    x_bits, wq, ws, _, _ = _problem(fp8bs, 64, 640, 512, 7802)
+    with pytest.raises(Fp8bsError) as e:
+        fp8bs.gemm_ex(GemmConfig(fp8bs.PATH_PREFILL, 5, 2, 4, 2, 2), wq, ws, x=dev_bf16(x_bits))
+    assert e.value.status == 7
+    torch.cuda.synchronize()
+    assert fp8bs.launch_count("gemm_mfma") == before
+
+
 def test_prefill_wide_1d_rejects_split(fp8bs):
     """The 1-D schedule runs every tile over the whole K range: a K split in
     its configuration is a configuration error."""
