@@ -192,7 +192,9 @@ enum { FP8BS_LAYOUT_ROWS = 0, FP8BS_LAYOUT_TILES = 1 };
  *             (16 waves_k x 128 each), on a grid of tiles with K split over
  *             split_k workgroups (tiles_n 3), or on the 1-D schedule
  *             (tiles_n 4, split_k 1): whole tiles in complete rounds of 256
- *             workgroups, the tiles left over as 128-column halves; or
+ *             workgroups, the tiles left over as 128-column halves; with
+ *             tiles_n 5 (split_k 1, n a multiple of 160) the same kernel on
+ *             narrow (64 waves_k) x 160 tiles, one workgroup per tile; or
  *             MFMA_ROWS_REG (the work split of MFMA_ROWS with each wave's
  *             activation operands held in registers instead of LDS, so m up
  *             to 32 runs unsplit at any K the registers hold: depth is the
