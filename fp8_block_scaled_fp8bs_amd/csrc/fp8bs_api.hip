@@ -444,6 +444,33 @@ bool select_config(int64_t m, int64_t n, int64_t k, fp8bs_gemm_config* out, bool
     // narrow tiles against 192 x 256 tiles); MLP down m = 1024 148.2 against
     // 152.0 us, m = 2048 204.6 against 212.8 us; at m = 4096 (not one round)
     // the two tie, at m = 8192 narrow tiles take 17% longer.
+    // Deep K (k >= 12288) with too few wide tiles to occupy the compute
+    // units: the wide kernel on the grid schedule with K split over s
+    // workgroups, s the largest that keeps tiles x s within one round of
+    // kTableCUs workgroups, when that round is at least three quarters full
+    // and each split keeps at least 8 K blocks (256-row tiles first); the
+    // fp32 partials are summed by the reduce kernel. Measured on MI355X on
+    // MLP down (17408 -> 5120): m = 1024 110 against 148 us (80 tiles,
+    // split 3), m = 512 74 against 88 us (40 tiles, split 6), m = 256 52
+    // against 64 us, m = 128 41 against 44 us (20 tiles, split 12); at
+    // m = 64 the 128 x 128 kernel stays (34 against 38 us: three quarters
+    // of a 256-row tile would be padding).
+    const int64_t kbn_p = k / BLK;
+    if (kbn_p >= 96 && m > 64) {
+      for (int jm = 4; jm >= 3; --jm) {
+        const int64_t tm = pfw_tile_m(jm);
+        const int64_t tiles = ((n + PFW_TILE_N - 1) / PFW_TILE_N) * ((m + tm - 1) / tm);
+        if (tiles >= kTableCUs) break;
+        int64_t sp = kTableCUs / tiles;
+        sp = sp < kbn_p / 8 ? sp : kbn_p / 8;
+        sp = sp < 64 ? sp : 64;
+        if (sp >= 2 && 4 * tiles * sp >= 3 * kTableCUs) {
+          *out = make_cfg(FP8BS_PATH_PREFILL, PF_WIDE, 2, jm, 2, (int)sp);
+          out->weight_layout = layout;
+          return true;
+        }
+      }
+    }
     if (n % (5 * BLK) == 0) {
       for (int njm = 4; njm >= 3; --njm) {
         const int64_t t = pfw_plan_narrow(njm, m, n).units;

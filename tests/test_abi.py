@@ -369,6 +369,14 @@ def test_prefill_narrow_tiles_table_and_limits(lib):
             cfg = sel(m, n, k)
             assert cfg.path == fp8bs.PATH_PREFILL and cfg.split_k == 1 or tn == 1, (m, n, k, cfg)
             assert (cfg.tiles_n, cfg.waves_k) == (tn, wk), (m, n, k, cfg)
+    # deep K (k >= 12288, m > 64): the wide kernel's grid schedule with K
+    # split so that tiles x split fill one round of 256 workgroups
+    deep = {(1024, 5120, 17408): (3, 4, 3), (512, 5120, 17408): (3, 4, 6),
+            (128, 5120, 17408): (3, 4, 12), (64, 5120, 17408): (1, 2, 7)}
+    for (m, n, k), want_cfg in deep.items():
+        for sel in (fp8bs.select_config, fp8bs.tiles_select_config):
+            cfg = sel(m, n, k)
+            assert (cfg.tiles_n, cfg.waves_k, cfg.split_k) == want_cfg, (m, n, k, cfg)
     for n, split in ((5248, 1), (5120, 2)):
         c = fp8bs._Config(5, 5, 2, 4, 2, split, 0, 0, 0)
         assert lib.fp8bs_gemm_ex(None, P, P, 2048, P, P, n, 5120, P, None, 0, ctypes.byref(c),

@@ -93,7 +93,8 @@ WIDE = [(4, 2), (3, 2)]  # (activation subtiles per wave, LDS stages) of the wid
 @pytest.mark.parametrize("wk,depth", WIDE)
 @pytest.mark.parametrize("m,n,k,split", [(300, 512, 1280, 1), (129, 768, 2048, 3), (64, 384, 384, 1),
                                          (33, 1024, 128, 1), (520, 256, 2560, 2),
-                                         (1000, 2176, 640, 1), (257, 128, 256, 1)])
+                                         (1000, 2176, 640, 1), (257, 128, 256, 1),
+                                         (130, 256, 12288, 12)])
 def test_prefill_wide_wave_tiles(fp8bs, layout, wk, depth, m, n, k, split):
     """The kernels with 64 x 128 or 48 x 128 outputs per wave (256 x 256 or
     192 x 256 output tiles, 8 waves, grid schedule): ragged m tails, an odd
@@ -329,6 +330,39 @@ def test_prefill_full_size_sampled_rows(fp8bs):
     xq_ref, xs_ref = oracle.quantize_act_ref(x_bits[rows])
     ref = oracle.gemm_ref(xq_ref, xs_ref, wq_ref, ws_ref)
     rep = oracle.tolerance_report(yb[rows], ref, **TOL)
+    assert rep["finite"] and rep["n_bad"] == 0, rep
+
+
+@pytest.mark.parametrize("m", [1024, 128])
+def test_prefill_deep_k_split_sampled_rows(fp8bs, m):
+    """The MLP-down weight (17408 -> 5120, the seeded workload weight) at
+    m = 1024 and 128, where the table splits K of the wide kernel over 3 and
+    12 workgroups: sampled full output rows, including the first and last,
+    against the oracle; the same bits as the unsplit 1-D schedule would not
+    hold (the split partials are summed in split order), so the check is
+    the tolerance and run-to-run identity."""
+    wl = WORKLOADS["mlp_down"]
+    cfg = fp8bs.tiles_select_config(m, wl.n, wl.k)
+    announce("prefill deep K", m, wl.n, wl.k, cfg)
+    assert (cfg.path, cfg.tiles_n, cfg.split_k) == (fp8bs.PATH_PREFILL, 3, 3 if m == 1024 else 12)
+    w_bits = wl.weight()
+    x_bits = act_bf16(wl.x_seed, wl.col_seed, m, wl.k, wl.n_outlier, wl.outlier_factor)
+    wq, ws = fp8bs.quantize_weight(dev_bf16(w_bits))
+    wt = fp8bs.pack_weight(wq)
+    x = dev_bf16(x_bits)
+    y = fp8bs.gemm_tiles(x, wt, ws)
+    y2 = fp8bs.gemm_tiles(x, wt, ws)
+    yr = fp8bs.gemm(x, wq, ws)
+    torch.cuda.synchronize()
+    yb = host_bits(y)
+    assert np.array_equal(yb, host_bits(y2)), "run-to-run bits differ"
+    assert np.array_equal(yb, host_bits(yr)), "row-major call differs"
+    wq_ref, ws_ref = oracle.quantize_weight_ref(w_bits)
+    assert np.array_equal(wq.cpu().numpy(), wq_ref)
+    rows = np.unique(np.concatenate([[0, 1, min(255, m - 2), min(256, m - 1), m - 1],
+                                     np.random.default_rng(6).choice(m, 11, replace=False)]))
+    xq_ref, xs_ref = oracle.quantize_act_ref(x_bits[rows])
+    rep = oracle.tolerance_report(yb[rows], oracle.gemm_ref(xq_ref, xs_ref, wq_ref, ws_ref), **TOL)
     assert rep["finite"] and rep["n_bad"] == 0, rep
 
 
