@@ -363,7 +363,8 @@ def test_prefill_narrow_tiles_table_and_limits(lib):
     import fp8_block_scaled_fp8bs_amd as fp8bs
     want = {(2048, 5120, 5120): (5, 4), (2048, 5120, 17408): (5, 4), (1024, 5120, 5120): (5, 3),
             (1536, 5120, 5120): (5, 4), (4096, 5120, 5120): (4, 4), (8192, 5120, 17408): (4, 4),
-            (2048, 34816, 5120): (4, 4), (512, 5120, 5120): (1, 2)}
+            (2048, 34816, 5120): (4, 4), (512, 5120, 5120): (1, 2),
+            (256, 34816, 5120): (4, 4), (128, 34816, 5120): (1, 2)}
     for (m, n, k), (tn, wk) in want.items():
         for sel in (fp8bs.select_config, fp8bs.tiles_select_config):
             cfg = sel(m, n, k)
