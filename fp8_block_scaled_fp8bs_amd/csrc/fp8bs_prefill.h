@@ -648,7 +648,7 @@ __device__ __forceinline__ void pfw_unit(const GemmParams& p, uint8_t* lds_all, 
   const int kb0 = work.kb0, last = work.kb1 - 1;
   // a whole tile holds two weight blocks, one per wave column; a half tile
   // one; a narrow tile's wave column (80 columns from any multiple of 16)
-  // lies in one block or straddles two (nb0, nb1: the block of its first
+  // lies in one block or straddles two (nbw, nbw1: the block of its first
   // and of its last column)
   const int nbw = NT == 5 ? (n0 + WCOLS * wn) / BLK : n0 / BLK + (NT == 8 ? wn : 0);
   const float* wsrow = p.ws + (size_t)nbw * (size_t)p.kbn;
