@@ -23,7 +23,7 @@ __all__ = [
     "swiglu_quant", "gemm_swiglu", "gemm_swiglu_ex", "swiglu_select_config",
     "swiglu_workspace_bytes",
     "encode_e4m3", "launch_count", "build_info", "diag_read", "diag_copy", "diag_stream",
-    "streamk_plan_check", "PATH_MFMA_STREAMK", "diag_timestamp", "diag_timestamp_hz",
+    "streamk_plan_check", "PATH_MFMA_STREAMK", "PATH_MFMA_ROWS_DMA", "diag_timestamp", "diag_timestamp_hz",
     "hip_runtime_mappings", "PATH_MFMA", "PATH_DOT", "REDUCE_KERNEL",
     "REDUCE_LAST_ARRIVER", "EPILOGUE_SEPARATE", "EPILOGUE_IN_GEMM", "LAYOUT_ROWS",
     "LAYOUT_TILES", "COUNTER",
@@ -36,6 +36,7 @@ _LIB = None
 PATH_AUTO, PATH_MFMA, PATH_DOT, PATH_MFMA_ROWS, PATH_MFMA_STREAM, PATH_PREFILL = 0, 1, 2, 3, 4, 5
 PATH_MFMA_ROWS_REG = 6
 PATH_MFMA_STREAMK = 7
+PATH_MFMA_ROWS_DMA = 8
 REDUCE_KERNEL, REDUCE_LAST_ARRIVER = 0, 1
 EPILOGUE_SEPARATE, EPILOGUE_IN_GEMM = 0, 1
 LAYOUT_ROWS, LAYOUT_TILES = 0, 1

@@ -165,7 +165,7 @@ constexpr int kTableCUs = 256;
 // Row-range paths: one workgroup per compute unit, n split over them.
 inline bool is_row_range(int path) {
   return path == FP8BS_PATH_MFMA_ROWS || path == FP8BS_PATH_MFMA_STREAM ||
-         path == FP8BS_PATH_MFMA_ROWS_REG;
+         path == FP8BS_PATH_MFMA_ROWS_REG || path == FP8BS_PATH_MFMA_ROWS_DMA;
 }
 
 // The streaming kernel addresses activations with 32-bit buffer offsets
@@ -186,6 +186,9 @@ const KernelEntry* find_kernel(const fp8bs_gemm_config& c, int m, bool fused,
   if (c.path == FP8BS_PATH_MFMA || c.path == FP8BS_PATH_MFMA_ROWS ||
       c.path == FP8BS_PATH_MFMA_ROWS_REG) {
     mt = m <= 16 ? 1 : 2;
+  } else if (c.path == FP8BS_PATH_MFMA_ROWS_DMA) {
+    if (m > 16 || swiglu) return nullptr;
+    mt = 1;
   } else if (c.path == FP8BS_PATH_MFMA_STREAMK) {
     if (swiglu) return nullptr;  // the epilogue runs in a second kernel
     mt = m <= 16 ? 1 : 2;
@@ -274,6 +277,14 @@ int config_rows(const fp8bs_gemm_config& c) {
 // on MI355X: tile-aligned ranges are needed on long ranges (972 rows of the
 // vocabulary layer: 211 against 240-290 us at m = 16-32); on 136-row
 // ranges the unaligned split is 1-2.5% faster than the aligned one.
+// The row-range kernel with the weight stream through LDS copies whole 2 KB
+// tiles: its ranges start on 16-row tiles.
+int rows_per_workgroup_tiles16(int64_t n, int num_cu) {
+  const int64_t cu = num_cu > 0 ? num_cu : 1;
+  const int64_t r = (n + cu - 1) / cu;
+  return (int)((r + 15) / 16 * 16);
+}
+
 int rows_per_workgroup(int64_t n, int num_cu, int layout = FP8BS_LAYOUT_ROWS) {
   const int64_t cu = num_cu > 0 ? num_cu : 1;
   const int64_t r = (n + cu - 1) / cu;
@@ -292,6 +303,8 @@ size_t config_lds_bytes(const fp8bs_gemm_config& c, int m, int64_t n, int kbn, i
   const int mt = m <= 16 ? 1 : 2;
   if (c.path == FP8BS_PATH_MFMA_STREAMK)
     return (size_t)lds_streamk_bytes(c.split_k > 0 ? kbn / c.split_k : kbn, m, c.waves_k, mt);
+  if (c.path == FP8BS_PATH_MFMA_ROWS_DMA)
+    return (size_t)rd_lds_bytes(rows_per_workgroup_tiles16(n, num_cu), kbn, m, c.depth);
   if (is_row_range(c.path)) {
     // weight scales of the row range first, then the kernel's own layout,
     // then (SwiGLU epilogue) the staged outputs
@@ -362,6 +375,7 @@ constexpr int RW = FP8BS_PATH_MFMA_ROWS;
 constexpr int ST = FP8BS_PATH_MFMA_STREAM;
 constexpr int RR = FP8BS_PATH_MFMA_ROWS_REG;
 constexpr int SK = FP8BS_PATH_MFMA_STREAMK;
+constexpr int RD = FP8BS_PATH_MFMA_ROWS_DMA;
 
 // Configurations the SwiGLU call accepts. With the separate epilogue:
 // everything but the last-arriver reduce (the split sum carries the
@@ -414,6 +428,10 @@ bool candidate_fits(const Candidate& cd, int64_t m, int64_t n, int kbn, fp8bs_ge
 // kernels on long row ranges do not, so this table takes the grid kernels
 // wherever they win; candidates without a tile-layout kernel are passed
 // over. Prefill sizes take the direct-load kernel in either layout.
+// Vocabulary-wide shapes at m = 9-16 on tile-layout weights take the
+// row-range kernel with the weight stream through LDS (3 stages): 248320 x
+// 5120 at m = 9 / 12 / 16: 190.0 / 194.6 / 201.0 us against 197.9 / 202.7 /
+// 207.9 us for the row-range kernel.
 // Deep K (MLP down, 17408 -> 5120) from m = 5 splits K over 5 or 6
 // workgroups per 128-column group (200 or 240 workgroups): tile layout
 // m = 8 18.5 against 19.2 us with 4, m = 16 19.5 against 21.4 us, m = 32
@@ -592,7 +610,7 @@ bool select_config(int64_t m, int64_t n, int64_t k, fp8bs_gemm_config* out, bool
        {{{MF, 1, 2, 4, 2, 1, RK}, {MF, 1, 1, 8, 5, 1, RK}}, 2},
        {{{MF, 1, 2, 4, 2, 1, RK}, {MF, 1, 2, 4, 5, 1, RK}}, 2},
        {{{MF, 1, 8, 1, 5, 1, RK}, {MF, 1, 2, 4, 5, 1, RK}}, 2},
-       {{{RW, 1, 1, 8, 3, 1, RK}, {MF, 1, 8, 1, 5, 1, RK}}, 2},
+       {{{RD, 1, 1, 8, 3, 1, RK}, {RW, 1, 1, 8, 3, 1, RK}, {MF, 1, 8, 1, 5, 1, RK}}, 3},
        {{{RW, 1, 1, 8, 3, 1, RK}, {RR, 1, 1, 8, 5, 1, RK}, {MF, 1, 8, 1, 5, 2, RK}}, 3}}};
   const int shape = nbn >= 512 ? 3 : (nbn >= 200 ? 2 : (kbn > 48 ? 1 : 0));
   const int mc = m == 1 ? 0 : (m == 2 ? 1 : (m <= 4 ? 2 : (m <= 8 ? 3 : (m <= 16 ? 4 : 5))));
@@ -748,6 +766,9 @@ fp8bs_status gemm_impl(bool fused, const void* x_bf16, const uint8_t* x_fp8,
     return FP8BS_ERR_CONFIG;
   if (c.path == FP8BS_PATH_MFMA_STREAM && !stream_offsets_fit(m, k)) return FP8BS_ERR_CONFIG;
   if (c.path == FP8BS_PATH_MFMA_ROWS_REG && !rows_reg_fits(c, kbn)) return FP8BS_ERR_CONFIG;
+  if (c.path == FP8BS_PATH_MFMA_ROWS_DMA &&
+      (c.weight_layout != FP8BS_LAYOUT_TILES || c.split_k != 1 || c.tiles_n != 1 || m > 16))
+    return FP8BS_ERR_CONFIG;
   const bool streamk = c.path == FP8BS_PATH_MFMA_STREAMK;
   if (streamk && (!streamk_fits(c, m, n, k) || c.reduce != FP8BS_REDUCE_KERNEL))
     return FP8BS_ERR_CONFIG;
@@ -810,7 +831,8 @@ fp8bs_status gemm_impl(bool fused, const void* x_bf16, const uint8_t* x_fp8,
   void* args[] = {&p};
   dim3 grid((unsigned)(n / rows), (unsigned)c.split_k);
   if (is_row_range(c.path)) {
-    p.rows_per_wg = rows_per_workgroup(n, kTableCUs, c.weight_layout);
+    p.rows_per_wg = c.path == FP8BS_PATH_MFMA_ROWS_DMA ? rows_per_workgroup_tiles16(n, kTableCUs)
+                                                      : rows_per_workgroup(n, kTableCUs, c.weight_layout);
     grid = dim3((unsigned)((n + p.rows_per_wg - 1) / p.rows_per_wg), (unsigned)c.split_k);
   }
   // the SwiGLU epilogue arrives on each (side, 128-column block) pair of a
@@ -819,6 +841,7 @@ fp8bs_status gemm_impl(bool fused, const void* x_bf16, const uint8_t* x_fp8,
                      SWIGLU_MAX_ARRIVALS)
     return FP8BS_ERR_CONFIG;
   dim3 block(64 * (is_row_range(c.path) ? 1 : c.waves_n) * c.waves_k);
+  if (c.path == FP8BS_PATH_MFMA_ROWS_DMA) block = dim3(64 * (RD_WK + RD_LOADERS));
   if (streamk) {
     grid = dim3((unsigned)kTableCUs);
     block = dim3(64 * (c.waves_k + 1));

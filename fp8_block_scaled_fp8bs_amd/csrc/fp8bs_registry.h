@@ -5,6 +5,7 @@
 #include <vector>
 
 #include "fp8bs_gemm.h"
+#include "fp8bs_rows_dma.h"
 #include "fp8bs_streamk.h"
 
 namespace fp8bs {
@@ -12,7 +13,8 @@ namespace fp8bs {
 struct KernelEntry {
   int path;    // 1 = MFMA grid, 2 = DOT grid, 3 = MFMA row range (one workgroup per CU),
                // 4 = MFMA streaming row range, 5 = prefill-size tiled MFMA GEMM,
-               // 6 = MFMA row range with register-resident activations, 7 = stream-K
+               // 6 = MFMA row range with register-resident activations, 7 = stream-K,
+               // 8 = MFMA row range with the weight stream through LDS
   int mt;      // MFMA: 16-row activation tiles (1: m <= 16, 2: m <= 32); DOT: max m
   int tn;      // MFMA: 16-row weight tiles per wave; DOT: 8-row groups per wave
   int wn, wk, d;
@@ -44,6 +46,12 @@ struct KernelRegistrar {
   {1, 2, TN, WN, WK, D, 1, gemm_mfma_kernel<2, TN, WN, WK, D, true, true>, 0, 1},        \
   {1, 1, TN, WN, WK, D, 0, gemm_mfma_kernel<1, TN, WN, WK, D, false, true>, 0, 1},       \
   {1, 2, TN, WN, WK, D, 0, gemm_mfma_kernel<2, TN, WN, WK, D, false, true>, 0, 1},
+
+// Row-range kernel with the weight stream through LDS (tile layout, m <= 16):
+// the config's depth field holds the ring's stages.
+#define FP8BS_ROWS_DMA_ENTRY(S)                                          \
+  {8, 1, 1, 1, RD_WK, S, 1, gemm_rows_dma_kernel<S, true>, 0, 1},        \
+  {8, 1, 1, 1, RD_WK, S, 0, gemm_rows_dma_kernel<S, false>, 0, 1},
 
 #define FP8BS_DOT_ENTRY(RT, WN, WK, D)                                    \
   {2, 1, RT, WN, WK, D, 1, gemm_dot_kernel<1, RT, WN, WK, D, true>},      \

@@ -163,7 +163,8 @@ enum {
   FP8BS_PATH_MFMA_STREAM = 4,
   FP8BS_PATH_PREFILL = 5,
   FP8BS_PATH_MFMA_ROWS_REG = 6,
-  FP8BS_PATH_MFMA_STREAMK = 7
+  FP8BS_PATH_MFMA_STREAMK = 7,
+  FP8BS_PATH_MFMA_ROWS_DMA = 8
 };
 enum { FP8BS_REDUCE_KERNEL = 0, FP8BS_REDUCE_LAST_ARRIVER = 1 };
 enum { FP8BS_EPILOGUE_SEPARATE = 0, FP8BS_EPILOGUE_IN_GEMM = 1 };
@@ -215,7 +216,13 @@ enum { FP8BS_LAYOUT_ROWS = 0, FP8BS_LAYOUT_TILES = 1 };
  *             cut where needed; 2 = whole tiles only (split_k must be 1),
  *             the workgroups' tile counts differing by at most one, no
  *             workspace; needs n*k < 2^31 and m <= 32).
- *             Paths 1-4, 6 and 7 take m <= 32.
+ *             MFMA_ROWS_DMA (tile-layout weights, m <= 16: the work split
+ *             of MFMA_ROWS with 8 waves along K on 16-row-aligned ranges,
+ *             the weight tiles streamed into a ring of `depth` LDS stages of
+ *             16 KB (3 or 6) by four more waves that only issue direct
+ *             loads; waves_k must be 8, tiles_n, waves_n and split_k 1; the
+ *             staged activations and the ring must fit in the LDS).
+ *             Paths 1-4 and 6-8 take m <= 32.
  *   tiles_n   MFMA: 16-row tiles per wave (1, 2, 4); DOT: 8-row groups per wave (1, 2, 4)
  *   waves_n   waves side by side along N in one workgroup (1, 2, 4)
  *   waves_k   waves splitting a workgroup's K range (1, 2, 4, 8); their

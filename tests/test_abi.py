@@ -291,7 +291,7 @@ def test_tile_layout_config_rules(lib):
             t = fp8bs.tiles_select_config(m, n, k)
             r = fp8bs.select_config(m, n, k)
             assert t.weight_layout == fp8bs.LAYOUT_TILES and r.weight_layout == fp8bs.LAYOUT_ROWS
-            assert t.path in (fp8bs.PATH_MFMA, 3, 4, 6)
+            assert t.path in (fp8bs.PATH_MFMA, 3, 4, 6, fp8bs.PATH_MFMA_ROWS_DMA)
             assert t == fp8bs.tiles_select_config(m, n, k)
             assert 1 <= t.split_k <= k // 128
             if t.path == fp8bs.PATH_MFMA:
@@ -352,6 +352,22 @@ def test_prefill_wide_configs_checked_before_any_launch(lib):
     assert (cfg.path, cfg.tiles_n, cfg.waves_n, cfg.waves_k, cfg.split_k) == (fp8bs.PATH_PREFILL, 4, 2, 4, 1)
     cfg = fp8bs.select_config(1024, 4096, 4096)               # 64 tiles: the 128 x 128 kernel
     assert (cfg.path, cfg.tiles_n) == (fp8bs.PATH_PREFILL, 1)
+
+
+def test_vocab_rows_dma_table(lib):
+    """The vocabulary layer at m = 9-16 on tile-layout weights takes the
+    row-range kernel with the weight stream through LDS (3 stages); at
+    m = 1-8, on row-major weights and where the LDS cannot hold the
+    activations beside the ring, it does not."""
+    import fp8_block_scaled_fp8bs_amd as fp8bs
+    for m in (9, 12, 16):
+        c = fp8bs.tiles_select_config(m, 248320, 5120)
+        assert (c.path, c.waves_k, c.depth, c.split_k) == (fp8bs.PATH_MFMA_ROWS_DMA, 8, 3, 1), (m, c)
+        assert fp8bs.select_config(m, 248320, 5120).path != fp8bs.PATH_MFMA_ROWS_DMA
+    for m in (1, 4, 8, 17, 32):
+        assert fp8bs.tiles_select_config(m, 248320, 5120).path != fp8bs.PATH_MFMA_ROWS_DMA
+    # 16 rows of a K = 8192 range: 118 KB of staged activations leave no room for the ring
+    assert fp8bs.tiles_select_config(16, 131072, 8192).path != fp8bs.PATH_MFMA_ROWS_DMA
 
 
 def test_prefill_narrow_tiles_table_and_limits(lib):
