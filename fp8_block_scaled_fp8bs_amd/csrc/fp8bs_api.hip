@@ -277,14 +277,6 @@ int config_rows(const fp8bs_gemm_config& c) {
 // on MI355X: tile-aligned ranges are needed on long ranges (972 rows of the
 // vocabulary layer: 211 against 240-290 us at m = 16-32); on 136-row
 // ranges the unaligned split is 1-2.5% faster than the aligned one.
-// The row-range kernel with the weight stream through LDS copies whole 2 KB
-// tiles: its ranges start on 16-row tiles.
-int rows_per_workgroup_tiles16(int64_t n, int num_cu) {
-  const int64_t cu = num_cu > 0 ? num_cu : 1;
-  const int64_t r = (n + cu - 1) / cu;
-  return (int)((r + 15) / 16 * 16);
-}
-
 int rows_per_workgroup(int64_t n, int num_cu, int layout = FP8BS_LAYOUT_ROWS) {
   const int64_t cu = num_cu > 0 ? num_cu : 1;
   const int64_t r = (n + cu - 1) / cu;
@@ -304,7 +296,7 @@ size_t config_lds_bytes(const fp8bs_gemm_config& c, int m, int64_t n, int kbn, i
   if (c.path == FP8BS_PATH_MFMA_STREAMK)
     return (size_t)lds_streamk_bytes(c.split_k > 0 ? kbn / c.split_k : kbn, m, c.waves_k, mt);
   if (c.path == FP8BS_PATH_MFMA_ROWS_DMA)
-    return (size_t)rd_lds_bytes(rows_per_workgroup_tiles16(n, num_cu), kbn, m, c.depth);
+    return (size_t)rd_lds_bytes(rows_per_workgroup(n, num_cu, FP8BS_LAYOUT_TILES), kbn, m, c.depth);
   if (is_row_range(c.path)) {
     // weight scales of the row range first, then the kernel's own layout,
     // then (SwiGLU epilogue) the staged outputs
@@ -831,8 +823,7 @@ fp8bs_status gemm_impl(bool fused, const void* x_bf16, const uint8_t* x_fp8,
   void* args[] = {&p};
   dim3 grid((unsigned)(n / rows), (unsigned)c.split_k);
   if (is_row_range(c.path)) {
-    p.rows_per_wg = c.path == FP8BS_PATH_MFMA_ROWS_DMA ? rows_per_workgroup_tiles16(n, kTableCUs)
-                                                      : rows_per_workgroup(n, kTableCUs, c.weight_layout);
+    p.rows_per_wg = rows_per_workgroup(n, kTableCUs, c.weight_layout);
     grid = dim3((unsigned)((n + p.rows_per_wg - 1) / p.rows_per_wg), (unsigned)c.split_k);
   }
   // the SwiGLU epilogue arrives on each (side, 128-column block) pair of a

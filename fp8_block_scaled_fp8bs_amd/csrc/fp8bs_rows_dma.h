@@ -2,7 +2,7 @@
 // weights, m <= 16).
 //
 // The work split is the row-range kernel's: one workgroup per compute unit
-// owns a contiguous range of output columns (a multiple of 16) over the
+// owns a contiguous range of output columns (a multiple of 4) over the
 // whole K range; 8 compute waves take the K blocks of each 16-row tile in
 // turn (wave w: blocks w, w + 8, ...) and their fp32 partials are summed in
 // wave order. The difference is how the weight tiles arrive. Four more
@@ -17,6 +17,13 @@
 // publishes the next step's stage and frees the one just read; at the end of
 // each tile the partials cross through LDS at the same barrier and wave 0
 // adds them and writes the outputs.
+//
+// The workgroup works through the 16-row tiles of the tile layout that
+// overlap its range. Where a range starts or ends inside a tile, the loader
+// lanes of rows outside it read the nearest row inside it instead (each
+// lane gives its own address; those lanes' bytes lie on the same lines as
+// rows of the range, so they cost no extra memory traffic), and only rows
+// inside the range are written.
 //
 // The products, their per-block rescale and both summation orders are those
 // of the row-range kernel with 8 waves along K, so the outputs are the same
@@ -63,10 +70,10 @@ __device__ __forceinline__ void gemm_rows_dma_body(const GemmParams& p, uint8_t*
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int M = p.m;
   const int nblk = p.kbn;
-  const int r0 = blockIdx.x * p.rows_per_wg;  // a multiple of 16
+  const int r0 = blockIdx.x * p.rows_per_wg;  // a multiple of 4
   const int r1 = r0 + p.rows_per_wg < p.n ? r0 + p.rows_per_wg : p.n;
-  const int nrows = r1 - r0;
-  const int ntile = (nrows + 15) >> 4;
+  const int tb = r0 >> 4;                     // first tile overlapping the range
+  const int ntile = ((r1 - 1) >> 4) - tb + 1;
   const int spt = (nblk + RD_WK - 1) / RD_WK;  // steps per tile
   const int nsteps = ntile * spt;
   const int nbf = r0 / BLK, nbr = (r1 - 1) / BLK - nbf + 1;
@@ -81,21 +88,26 @@ __device__ __forceinline__ void gemm_rows_dma_body(const GemmParams& p, uint8_t*
     // step, both 1 KB halves. Steps past the last reload the last step's
     // bytes into the stage they would use (freed, and never read again), so
     // every step issues the same number of loads and one wait count holds.
+    // Lane 16 q + r holds row r of the tile (quarter q); a row outside the
+    // range is replaced by the range's nearest row of the same tile.
     const int l = wave - RD_WK;
     const uint32_t ring0 = (uint32_t)reinterpret_cast<uintptr_t>(ring);
-    const uint8_t* tiles = p.wq + (size_t)(r0 >> 4) * (size_t)p.kbn * 2048u;
+    const uint8_t* tiles = p.wq + (size_t)tb * (size_t)p.kbn * 2048u;
     auto issue = [&](int i) {
       const uint32_t st = ring0 + (uint32_t)((i % S) * RD_STEP);
       const int ic = i < nsteps ? i : nsteps - 1;
       const int t = ic / spt, g = ic - t * spt;
+      int r = 16 * (tb + t) + (lane & 15);
+      r = r < r0 ? r0 : (r >= r1 ? r1 - 1 : r);
+      const uint32_t lo = (uint32_t)((lane & 48) + (r & 15)) * 16u;
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         const int w = 2 * l + s2;
         int kb = RD_WK * g + w;
         kb = kb < nblk ? kb : nblk - 1;
         const uint8_t* src = tiles + ((size_t)t * (size_t)p.kbn + (size_t)kb) * 2048u;
-        rd_dma16(st + (uint32_t)w * 2048u, src, (uint32_t)lane * 16u);
-        rd_dma16(st + (uint32_t)w * 2048u + 1024u, src + 1024, (uint32_t)lane * 16u);
+        rd_dma16(st + (uint32_t)w * 2048u, src, lo);
+        rd_dma16(st + (uint32_t)w * 2048u + 1024u, src + 1024, lo);
       }
     };
     for (int i = 0; i < S - 1; ++i) issue(i);
@@ -144,9 +156,9 @@ __device__ __forceinline__ void gemm_rows_dma_body(const GemmParams& p, uint8_t*
         sa = act_s[kb * M + l16];
       }
       // this lane's four output rows lie in one 128-row scale block; lanes
-      // past the range read a valid entry
-      int nbl = (r0 + 16 * t + 4 * g16) / BLK - nbf;
-      nbl = nbl < nbr ? nbl : nbr - 1;
+      // outside the range read a valid entry
+      int nbl = (16 * (tb + t) + 4 * g16) / BLK - nbf;
+      nbl = nbl < 0 ? 0 : (nbl < nbr ? nbl : nbr - 1);
       const float sw = wsl[nbl * nblk + kb];
       const f32x4 z = {0.f, 0.f, 0.f, 0.f};
       const f32x4 pb = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(aop, bop, z, 0, 0, 0, 0, 0, 0);
@@ -161,9 +173,10 @@ __device__ __forceinline__ void gemm_rows_dma_body(const GemmParams& p, uint8_t*
     if (tile_end) {
       if (w == 0) {
         for (int ww = 1; ww < RD_WK; ++ww) acc += rt[(ww - 1) * 64 + lane];
-        const int rl = 16 * t + 4 * g16;  // first of this lane's four rows
-        if (row_ok && rl < nrows) {
-          uint2* dst = reinterpret_cast<uint2*>(p.y + (size_t)l16 * (size_t)p.n + r0 + rl);
+        // this lane's four rows (r0 and r1 are multiples of 4: all in or out)
+        const int rg = 16 * (tb + t) + 4 * g16;
+        if (row_ok && rg >= r0 && rg < r1) {
+          uint2* dst = reinterpret_cast<uint2*>(p.y + (size_t)l16 * (size_t)p.n + rg);
           *dst = make_uint2(pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]));
         }
       }
@@ -173,7 +186,7 @@ __device__ __forceinline__ void gemm_rows_dma_body(const GemmParams& p, uint8_t*
 }
 
 // rd_lds_bytes(rows_per_wg, k / 128, m, S) of dynamic LDS; 768 threads (8
-// compute and 4 loader waves); grid: one workgroup per 16-aligned row range.
+// compute and 4 loader waves); grid: one workgroup per row range.
 template <int S, bool FUSED>
 __global__ __launch_bounds__(64 * (RD_WK + RD_LOADERS), 1) void gemm_rows_dma_kernel(GemmParams p) {
   constexpr int NT = 64 * RD_WK;

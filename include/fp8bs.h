@@ -217,7 +217,7 @@ enum { FP8BS_LAYOUT_ROWS = 0, FP8BS_LAYOUT_TILES = 1 };
  *             the workgroups' tile counts differing by at most one, no
  *             workspace; needs n*k < 2^31 and m <= 32).
  *             MFMA_ROWS_DMA (tile-layout weights, m <= 16: the work split
- *             of MFMA_ROWS with 8 waves along K on 16-row-aligned ranges,
+ *             of MFMA_ROWS with 8 waves along K,
  *             the weight tiles streamed into a ring of `depth` LDS stages of
  *             16 KB (3 or 6) by four more waves that only issue direct
  *             loads; waves_k must be 8, tiles_n, waves_n and split_k 1; the

@@ -5,7 +5,9 @@
   the same codes;
 - K ranges of one partial step (3 blocks: five compute waves idle), of a
   full and a partial step (13 blocks), of whole steps (40 blocks), and the
-  full MLP-up weight (34816 x 5120: 144-row ranges, the last one shorter);
+  full MLP-up weight (34816 x 5120: 136-row ranges, every one starting or
+  ending inside a 16-row tile; the small problems: 8- or 4-row ranges, half
+  or a quarter of a tile);
 - rings of 3 and 6 stages; m from 1 to 16, where the LDS holds the
   activations beside the ring (others rejected before any launch);
 - the same bits as the row-range kernel with 8 waves along K, whose
@@ -44,11 +46,20 @@ def rows_cfg(fp8bs):
     return GemmConfig(fp8bs.PATH_MFMA_ROWS, 1, 1, 8, 3, 1, weight_layout=fp8bs.LAYOUT_TILES)
 
 
+def range_rows(n):
+    """Rows per workgroup of the row-range kernels on tile-layout weights:
+    n over 256 units rounded up to 16 rows, unless that leaves more than 2%
+    of the units idle; then to 4 rows."""
+    r = -(-n // 256)
+    r16 = -(-r // 16) * 16
+    return r16 if 50 * -(-n // r16) >= 49 * 256 else -(-r // 4) * 4
+
+
 def lds_fits(n, k, m, stages):
     """Whether the workgroup's LDS (160 KB) holds the range's weight scales,
     the staged activations (148 bytes per row and block, rounded to 16), two
     partial-exchange areas and the ring of 16 KB stages."""
-    rows = -(-(-(-n // 256)) // 16) * 16
+    rows = range_rows(n)
     nblk = k // 128
     ws = ((rows // 128 + 2) * nblk * 4 + 15) // 16 * 16
     act = (nblk * m * 148 + 15) // 16 * 16
