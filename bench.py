@@ -738,9 +738,11 @@ def main() -> int:
     layout = "tiles" if tiles else "rows"
 
     def prepared(w):
-        # quantized once; in the tile layout, rearranged once (neither is timed)
+        # quantized once; in the tile layout, rearranged once (neither is
+        # timed). The other layout's codes are kept for the comparison line.
         wq, wsc = fp8bs.quantize_weight(w)
-        return (fp8bs.pack_weight(wq), wsc) if tiles else (wq, wsc)
+        wt = fp8bs.pack_weight(wq)
+        return (wt, wsc, wq) if tiles else (wq, wsc, wt)
 
     pool = [prepared(w0)]
     del w0
@@ -771,7 +773,7 @@ def main() -> int:
     calls = [0]
 
     def step(i):
-        wq, wsc = pool[i % pool_n]
+        wq, wsc, _ = pool[i % pool_n]
         gemm(x, wq, wsc, out=y, workspace=workspace)
         calls[0] += 1
 
@@ -876,6 +878,42 @@ def main() -> int:
             ceiling[name] = {"us": round(us_r, 3), "GBps": round(code_bytes / (us_r * 1e3), 1)}
     best = max(ceiling.values(), key=lambda v: v["GBps"]) if ceiling else None
 
+    # --- the other weight layout: the same weights and activations through
+    # the other call (row-major fp8bs_gemm, or fp8bs_gemm_tiles), with its own
+    # table configuration, timed exactly like the GEMM steps
+    other = None
+    if not args.eager_only and not args.config:
+        o_tiles = not tiles
+        o_gemm = fp8bs.gemm_tiles if o_tiles else fp8bs.gemm
+        o_cfg = fp8bs.tiles_select_config(m, n, k) if o_tiles else fp8bs.select_config(m, n, k)
+        o_before = fp8bs.launch_count("gemm_mfma") + fp8bs.launch_count("gemm_dot")
+        o_calls = [0]
+        o_work = torch.empty(max(fp8bs.config_workspace_bytes(o_cfg, m, n, k), 16),
+                             dtype=torch.uint8, device=dev)
+
+        def o_step(i):
+            _, wsc, wo = pool[i % pool_n]
+            o_gemm(x, wo, wsc, out=y, workspace=o_work)
+            o_calls[0] += 1
+
+        o_ms, _ = timed_graph(o_step, args.steps)
+        o_launches = fp8bs.launch_count("gemm_mfma") + fp8bs.launch_count("gemm_dot") - o_before
+        if o_launches != o_calls[0]:
+            print(f"kernel launch count {o_launches} != expected {o_calls[0]} (other layout)",
+                  file=sys.stderr)
+            return 1
+        o_us = o_ms * 1e3
+        o_gbps = alg_bytes / (o_us * 1e3)
+        other = {"weight_layout": "tiles" if o_tiles else "rows",
+                 "call": "fp8bs_gemm_tiles" if o_tiles else "fp8bs_gemm",
+                 "us_per_gemm": round(o_us, 3), "GBps": round(o_gbps, 1),
+                 "pct_of_8TBps": round(100 * o_gbps / HBM_PEAK_GBPS, 2),
+                 "kernel": {"path": PATH_NAMES.get(o_cfg.path, str(o_cfg.path)),
+                            "tiles_n": o_cfg.tiles_n, "waves_n": o_cfg.waves_n,
+                            "waves_k": o_cfg.waves_k, "depth": o_cfg.depth,
+                            "split_k": o_cfg.split_k},
+                 "timing": "the same weights and activations, timed exactly like the GEMM steps"}
+
     # --- library reference: the same product in bf16 through torch (hipBLASLt)
     lib_ref = None if args.no_library_ref else library_reference(args, x, n, k, gen, dev, stream)
 
@@ -923,6 +961,7 @@ def main() -> int:
         "pct_of_8TBps": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "eager_us_per_gemm": round(eager_ms * 1e3, 3),
         "replay_spread": spread,
+        "other_layout": other,
         "stream_read_ceiling": ({"bytes": code_bytes, "best_us": best["us"], "best_GBps": best["GBps"],
                                  "gemm_frac_of_ceiling": round(best["us"] / us, 4),
                                  "configs": ceiling,
