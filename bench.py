@@ -476,10 +476,12 @@ def _pct(v: list, q: float) -> float:
     return v[min(len(v) - 1, max(0, int(round(q * (len(v) - 1)))))]
 
 
-def summarize_trace(root: str, last: int) -> int:
+def summarize_trace(root: str, last: int, by_grid: bool = False) -> int:
     """Print a markdown summary of a rocprofv3 --kernel-trace CSV directory:
     per kernel, all dispatches (calls, mean, min, max) and the last `last`
-    dispatches (median, p10, p90), in ns."""
+    dispatches (median, p10, p90), in ns. by_grid: one row per kernel and
+    grid size (work-items in x, y, z), which separates shapes that share a
+    kernel."""
     import csv
     files = _find_csv(root, "kernel_trace.csv")
     if not files:
@@ -492,16 +494,19 @@ def summarize_trace(root: str, last: int) -> int:
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
     by = {}
     for r in rows:
-        by.setdefault(r["Kernel_Name"], []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        key = r["Kernel_Name"]
+        if by_grid:
+            key = f"{key[:90]} grid {r['Grid_Size_X']}x{r['Grid_Size_Y']}x{r['Grid_Size_Z']}"
+        by.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
     print("| kernel | calls | mean ns | min ns | max ns |")
     print("|---|---|---|---|---|")
     for k, v in sorted(by.items(), key=lambda kv: -sum(kv[1])):
-        print(f"| `{k[:110]}` | {len(v)} | {sum(v) / len(v):.0f} | {min(v)} | {max(v)} |")
+        print(f"| `{k[:130]}` | {len(v)} | {sum(v) / len(v):.0f} | {min(v)} | {max(v)} |")
     print()
     for k, v in by.items():
         if "fp8bs::" in k and ("gemm" in k or "splitk" in k or "swiglu" in k or "diag_stream" in k):
             t = v[-last:]
-            print(f"- `{k[:110]}`: last {len(t)} dispatches: median {_pct(t, 0.5):.0f} ns, "
+            print(f"- `{k[:130]}`: last {len(t)} dispatches: median {_pct(t, 0.5):.0f} ns, "
                   f"p10 {_pct(t, 0.1):.0f} ns, p90 {_pct(t, 0.9):.0f} ns, mean {sum(t) / len(t):.0f} ns")
     return 0
 
@@ -673,10 +678,12 @@ def main() -> int:
     ap.add_argument("--counter", default="FETCH_SIZE")
     ap.add_argument("--last", type=int, default=200,
                     help="dispatches per kernel counted as the timed ones in --summarize-trace")
+    ap.add_argument("--by-grid", action="store_true",
+                    help="--summarize-trace: one row per kernel and grid size")
     args = ap.parse_args()
 
     if args.summarize_trace:
-        return summarize_trace(args.summarize_trace, args.last)
+        return summarize_trace(args.summarize_trace, args.last, args.by_grid)
     if args.summarize_pmc:
         return summarize_pmc(args.summarize_pmc, args.counter)
 
