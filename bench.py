@@ -229,6 +229,115 @@ def step_mix(args, fp8bs, dev) -> int:
     return 0
 
 
+# One GPU's share of each shape when the GEMM is split over 8 GPUs: whole
+# 128-row weight blocks per GPU (column split; the largest share), or whole
+# K blocks (row split of MLP down, whose partials would meet in a rank-order
+# sum). (name, description, n, k, full shape it comes from)
+SHARD_SHAPES = (
+    ("vocab_col8", "vocabulary layer, one GPU's column share of 8: 243 of 1,940 block rows",
+     31104, 5120, "vocab"),
+    ("mlp_up_col8", "MLP up/gate, one GPU's column share of 8: 34 of 272 block rows", 4352, 5120,
+     "mlp_up"),
+    ("mlp_down_row8", "MLP down, one GPU's K share of 8: 17 of 136 K blocks", 5120, 2176,
+     "mlp_down"),
+    ("square_col8", "square projection, one GPU's column share of 8: 5 of 40 block rows", 640,
+     5120, "square"),
+)
+
+
+def shards(args, fp8bs, dev) -> int:
+    """The GEMM at one GPU's share of each shape under an 8-way split (the
+    per-GPU kernel of the sharded path; nothing here runs on more than one
+    GPU): the table's configuration on tile-layout weights over a rotating
+    pool of at least --pool-gib GiB, K calls captured in one graph, the
+    median of 5 replays. One JSON line per (shape, m), with the algorithmic
+    GB/s of the share and, beside it, the time of the full shape divided by
+    8 (what a perfect split would give per GPU)."""
+    import torch
+
+    from workloads import WORKLOADS
+
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, steps):
+        for i in range(2):
+            fn(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                for i in range(steps):
+                    fn(i)
+        stream.wait_stream(cap)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t = []
+        for _ in range(5):
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t.append(e0.elapsed_time(e1) * 1e3 / steps)
+        return sorted(t)[2]
+
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1700)
+    ms = [int(v) for v in args.shard_m.split(",")]
+    for name, descr, n, k, full in SHARD_SHAPES:
+        count = max(1, math.ceil(args.pool_gib * (1 << 30) / (n * k)))
+        pool = []
+        for _ in range(count):
+            w = (torch.randn((n, k), generator=gen, device=dev, dtype=torch.float32) * 0.02).to(torch.bfloat16)
+            wq, wsc = fp8bs.quantize_weight(w)
+            pool.append((fp8bs.pack_weight(wq), wsc))
+            del w, wq
+        fw = WORKLOADS[full]
+        fcount = max(1, math.ceil(args.pool_gib * (1 << 30) / (fw.n * fw.k)))
+        fpool = []
+        for _ in range(fcount):
+            w = (torch.randn((fw.n, fw.k), generator=gen, device=dev, dtype=torch.float32) * 0.02).to(torch.bfloat16)
+            wq, wsc = fp8bs.quantize_weight(w)
+            fpool.append((fp8bs.pack_weight(wq), wsc))
+            del w, wq
+        torch.cuda.synchronize()
+        for m in ms:
+            x = torch.randn((m, k), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+            fx = torch.randn((m, fw.k), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+            y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            fy = torch.empty((m, fw.n), dtype=torch.bfloat16, device=dev)
+            work = torch.empty(max(fp8bs.workspace_bytes(m, n, k), 16), dtype=torch.uint8, device=dev)
+            fwork = torch.empty(max(fp8bs.workspace_bytes(m, fw.n, fw.k), 16), dtype=torch.uint8,
+                                device=dev)
+            P, FP = len(pool), len(fpool)
+            steps = 200 if n * k < (1 << 28) else 40
+            us = timed(lambda i: fp8bs.gemm_tiles(x, pool[i % P][0], pool[i % P][1], out=y,
+                                                  workspace=work), steps)
+            us_full = timed(lambda i: fp8bs.gemm_tiles(fx, fpool[i % FP][0], fpool[i % FP][1],
+                                                       out=fy, workspace=fwork), steps)
+            cfg = fp8bs.tiles_select_config(m, n, k)
+            nbytes = n * k + 4 * (n // 128) * (k // 128) + 2 * m * k + 2 * m * n
+            gbps = nbytes / (us * 1e3)
+            print(json.dumps({
+                "mode": "shard", "shape": name, "of": full, "description": descr, "m": m, "n": n,
+                "k": k, "us": round(us, 3), "GBps": round(gbps, 1),
+                "pct_of_8TBps": round(100 * gbps / HBM_PEAK_GBPS, 2), "algorithmic_bytes": nbytes,
+                "full_shape_us": round(us_full, 3), "full_shape_us_over_8": round(us_full / 8, 3),
+                "share_vs_perfect_split": round(us_full / 8 / us, 3),
+                "kernel": {"path": PATH_NAMES.get(cfg.path, str(cfg.path)), "tiles_n": cfg.tiles_n,
+                           "waves_n": cfg.waves_n, "waves_k": cfg.waves_k, "depth": cfg.depth,
+                           "split_k": cfg.split_k},
+                "weight_layout": "tiles", "weight_pool": P,
+                "timing": f"graph of {steps} calls over the rotating pool, median of 5 replays"}),
+                flush=True)
+            del x, fx, y, fy, work, fwork
+        del pool, fpool
+        torch.cuda.empty_cache()
+    return 0
+
+
 def library_reference(args, x, n, k, gen, dev, stream) -> dict:
     """The same product with bf16 weights through torch.nn.functional.linear
     (hipBLASLt on ROCm), timed the same way as the kernel under test: a
@@ -654,6 +763,9 @@ def main() -> int:
                     help="decode-step mix: 256 GEMMs over the four shapes per step, at every M; "
                          "prints one JSON line per M")
     ap.add_argument("--step-m", default="1,2,4,8,16,32", help="M values of the step mix")
+    ap.add_argument("--shards", action="store_true",
+                    help="the GEMM at one GPU's share of each shape under an 8-way split")
+    ap.add_argument("--shard-m", default="1,8,16", help="M values of --shards")
     ap.add_argument("--prefill", action="store_true",
                     help="prefill sizes (m > 32) on the square and MLP shapes; one JSON line each")
     ap.add_argument("--prefill-m", default="128,512,2048,8192", help="m values of --prefill")
@@ -705,6 +817,8 @@ def main() -> int:
     torch.cuda.set_device(dev)
     fp8bs.load()
 
+    if args.shards:
+        return shards(args, fp8bs, dev)
     if args.step_mix:
         return step_mix(args, fp8bs, dev)
     if args.mlp_swiglu:

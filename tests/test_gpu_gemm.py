@@ -153,6 +153,69 @@ def test_vocab_parity_sampled_columns(fp8bs, vocab_weight, m):
     _assert_close(np.concatenate(gots, axis=1), np.concatenate(refs, axis=1), f"vocab m={m}")
 
 
+# One GPU's share of a shape under an 8-way split (the per-GPU kernel of the
+# sharded path, run here on one GPU): the vocabulary layer split on 128-row
+# block boundaries (ranks 0-3 hold 243 of the 1,940 block rows, ranks 4-7
+# hold 242), MLP down split along K (17 of the 136 K blocks per rank).
+VOCAB_SHARD_BLOCKS = [243] * 4 + [242] * 4
+DOWN_SHARD_KB = 17
+
+
+@pytest.mark.parametrize("rank", [0, 7])
+@pytest.mark.parametrize("m", [1, 8, 16])
+def test_vocab_column_shard(fp8bs, vocab_weight, rank, m):
+    """A rank's column share of the vocabulary weight is a contiguous slice of
+    its block rows with their own scales; the GEMM on it (row-major and tile
+    layout, each in the table's configuration for the share's shape) gives
+    the columns of the full product: sampled block rows, regenerated alone,
+    against the oracle."""
+    wl = WORKLOADS["vocab"]
+    b0 = sum(VOCAB_SHARD_BLOCKS[:rank])
+    b1 = b0 + VOCAB_SHARD_BLOCKS[rank]
+    wq, ws = vocab_weight
+    wsh, ssh = wq[b0 * 128:b1 * 128], ws[b0:b1]
+    n = (b1 - b0) * 128
+    announce("vocab shard", rank, "n", n, "m", m, "cfg", fp8bs.select_config(m, n, wl.k))
+    x_bits = act_bf16(wl.x_seed, wl.col_seed, 32, wl.k, wl.n_outlier, wl.outlier_factor)[:m]
+    x = dev_bf16(x_bits)
+    y = host_bits(fp8bs.gemm(x, wsh, ssh))
+    yt = host_bits(fp8bs.gemm_tiles(x, fp8bs.pack_weight(wsh), ssh))
+    xq, xs = oracle.quantize_act_ref(x_bits)
+    refs, gots, gots_t = [], [], []
+    for c in (b0, b0 + 1, (b0 + b1) // 2, b1 - 1):
+        rows = weight_rows_bf16(wl.w_seed, c, 128, wl.k)
+        qr, sr = oracle.quantize_weight_ref(rows)
+        refs.append(oracle.gemm_ref(xq, xs, qr, sr))
+        gots.append(y[:, (c - b0) * 128:(c - b0 + 1) * 128])
+        gots_t.append(yt[:, (c - b0) * 128:(c - b0 + 1) * 128])
+    ref = np.concatenate(refs, axis=1)
+    _assert_close(np.concatenate(gots, axis=1), ref, f"vocab shard {rank} m={m}")
+    _assert_close(np.concatenate(gots_t, axis=1), ref, f"vocab shard {rank} m={m} tiles")
+
+
+@pytest.mark.parametrize("rank", [0, 7])
+@pytest.mark.parametrize("m", [1, 8, 16])
+def test_mlp_down_k_shard(fp8bs, full_problems, rank, m):
+    """A rank's K share of MLP down: its weight columns hold whole 128x128
+    blocks and its activation columns whole 1x128 blocks, so its codes and
+    scales are those columns of the full quantization. The GEMM on the share
+    (row-major and tile layout, the table's configuration for 5120 x 2176)
+    against the oracle on the same slices, full output."""
+    pr = full_problems["mlp_down"]
+    k0, k1 = 128 * DOWN_SHARD_KB * rank, 128 * DOWN_SHARD_KB * (rank + 1)
+    b0, b1 = DOWN_SHARD_KB * rank, DOWN_SHARD_KB * (rank + 1)
+    wq = pr.wq[:, k0:k1].contiguous()
+    ws = pr.ws[:, b0:b1].contiguous()
+    x = pr.x[:m, k0:k1].contiguous()
+    announce("mlp_down shard", rank, "k", k1 - k0, "m", m, "cfg", fp8bs.select_config(m, 5120, k1 - k0))
+    y = host_bits(fp8bs.gemm(x, wq, ws))
+    yt = host_bits(fp8bs.gemm_tiles(x, fp8bs.pack_weight(wq), ws))
+    ref = oracle.gemm_ref(pr.xq_ref[:m, k0:k1], pr.xs_ref[:m, b0:b1], pr.wq_ref[:, k0:k1],
+                          pr.ws_ref[:, b0:b1])
+    _assert_close(y, ref, f"mlp_down shard {rank} m={m}")
+    _assert_close(yt, ref, f"mlp_down shard {rank} m={m} tiles")
+
+
 @pytest.mark.parametrize("m", [8, 16])
 def test_vocab_run_to_run_bit_identical(fp8bs, vocab_weight, m):
     """The 248,320-wide layer in the configuration each layout's table picks:
