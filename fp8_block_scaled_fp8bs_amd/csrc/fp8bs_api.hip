@@ -542,7 +542,7 @@ bool select_config(int64_t m, int64_t n, int64_t k, fp8bs_gemm_config* out, bool
   };
   // [shape class][m class]: m = 1, 2, 3-4, 5-8, 9-16, 17-32; each candidate
   // is {path, tiles_n, waves_n, waves_k, depth, split_k, reduce}
-  static const Cell table[4][6] = {
+  static const Cell table[5][6] = {
       // square-like: n < 25600, k <= 6144
       {{{{DT, 2, 2, 4, 4, 1, RK}, {MF, 1, 2, 4, 5, 1, RK}}, 2},
        {{{MF, 1, 2, 4, 5, 1, RK}}, 1},
@@ -570,12 +570,23 @@ bool select_config(int64_t m, int64_t n, int64_t k, fp8bs_gemm_config* out, bool
        {{{MF, 4, 1, 4, 2, 1, RK}, {MF, 1, 8, 1, 5, 1, RK}}, 2},
        {{{ST, 1, 1, 8, 6, 1, RK}, {RW, 2, 1, 8, 6, 1, RK}}, 2},
        {{{RW, 1, 1, 8, 3, 1, RK}, {RW, 2, 1, 8, 6, 1, RK}}, 2},
-       {{{RW, 2, 1, 8, 6, 1, RK}, {RR, 1, 1, 8, 5, 1, RK}, {MF, 1, 8, 1, 5, 2, RK}}, 3}}};
+       {{{RW, 2, 1, 8, 6, 1, RK}, {RR, 1, 1, 8, 5, 1, RK}, {MF, 1, 8, 1, 5, 2, RK}}, 3}},
+      // wide N in one round of 128-row workgroups: 200 <= n/128 <= 256 (one
+      // GPU's 8-way column share of the vocabulary layer, 31104 x 5120: 8
+      // waves along N, 128 output columns per workgroup, at most one per
+      // compute unit; at m = 3-24, 26.2-33.1 us against 27.4-37.2 us for the
+      // wide-N choices)
+      {{{{MF, 1, 1, 4, 5, 1, RK}, {MF, 1, 1, 8, 5, 1, RK}}, 2},
+       {{{MF, 1, 8, 1, 5, 1, RK}, {RW, 4, 1, 8, 4, 1, RK}}, 2},
+       {{{MF, 1, 8, 1, 5, 1, RK}, {RW, 1, 1, 8, 3, 1, RK}}, 2},
+       {{{MF, 1, 8, 1, 5, 1, RK}, {RW, 2, 1, 8, 6, 1, RK}}, 2},
+       {{{MF, 1, 8, 1, 5, 1, RK}, {RW, 4, 1, 8, 4, 1, RK}}, 2},
+       {{{MF, 1, 8, 1, 5, 1, RK}, {RW, 2, 1, 8, 6, 1, RK}, {RR, 1, 1, 8, 5, 1, RK}}, 3}}};
   static const Candidate fallback[] = {{MF, 1, 1, 4, 5, 1, RK}, {MF, 1, 1, 4, 5, 2, RK},
                                        {MF, 1, 1, 4, 5, 4, RK}, {MF, 1, 1, 4, 5, 8, RK},
                                        {MF, 1, 1, 4, 5, 16, RK}, {MF, 1, 1, 4, 5, 32, RK},
                                        {MF, 1, 1, 4, 5, 64, RK}};
-  static const Cell table_tiles[4][6] = {
+  static const Cell table_tiles[5][6] = {
       // square-like
       {{{{MF, 1, 2, 4, 5, 1, RK}}, 1},
        {{{MF, 1, 2, 4, 5, 1, RK}}, 1},
@@ -603,8 +614,23 @@ bool select_config(int64_t m, int64_t n, int64_t k, fp8bs_gemm_config* out, bool
        {{{MF, 1, 2, 4, 2, 1, RK}, {MF, 1, 2, 4, 5, 1, RK}}, 2},
        {{{MF, 1, 8, 1, 5, 1, RK}, {MF, 1, 2, 4, 5, 1, RK}}, 2},
        {{{RD, 1, 1, 8, 3, 1, RK}, {RW, 1, 1, 8, 3, 1, RK}, {MF, 1, 8, 1, 5, 1, RK}}, 3},
-       {{{RW, 1, 1, 8, 3, 1, RK}, {RR, 1, 1, 8, 5, 1, RK}, {MF, 1, 8, 1, 5, 2, RK}}, 3}}};
-  const int shape = nbn >= 512 ? 3 : (nbn >= 200 ? 2 : (kbn > 48 ? 1 : 0));
+       {{{RW, 1, 1, 8, 3, 1, RK}, {RR, 1, 1, 8, 5, 1, RK}, {MF, 1, 8, 1, 5, 2, RK}}, 3}},
+      // wide N in one round of 128-row workgroups (31104 x 5120 at m = 3-4:
+      // 24.7-25.3 us with 2 x 4 waves against 33.0-33.1; m = 5-24: 8 waves
+      // along N, 26.4-32.9 us against 34.0-42.4; m = 32: the same with K
+      // split in two, 39.4 against 43.5 us)
+      {{{{MF, 1, 2, 4, 5, 1, RK}, {MF, 1, 1, 4, 5, 1, RK}}, 2},
+       {{{MF, 1, 2, 4, 5, 1, RK}, {MF, 1, 8, 1, 5, 1, RK}}, 2},
+       {{{MF, 1, 2, 4, 5, 1, RK}, {MF, 1, 8, 1, 5, 1, RK}}, 2},
+       {{{MF, 1, 8, 1, 5, 1, RK}, {MF, 1, 2, 4, 5, 1, RK}}, 2},
+       {{{MF, 1, 8, 1, 5, 1, RK}, {RD, 1, 1, 8, 3, 1, RK}, {RW, 1, 1, 8, 3, 1, RK}}, 3},
+       {{{MF, 1, 8, 1, 5, 1, RK}, {MF, 1, 8, 1, 5, 2, RK}, {RW, 2, 1, 8, 6, 1, RK}}, 3}}};
+  // shape class: 3 vocabulary-wide, 2 wide N, 4 wide N whose 128-row blocks
+  // fill at most one round of compute units, 1 deep K, 0 square-like
+  const int shape = nbn >= 512 ? 3
+                    : nbn > kTableCUs ? 2
+                    : nbn >= 200 ? 4
+                    : (kbn > 48 ? 1 : 0);
   const int mc = m == 1 ? 0 : (m == 2 ? 1 : (m <= 4 ? 2 : (m <= 8 ? 3 : (m <= 16 ? 4 : 5))));
   const Cell& cell = layout == FP8BS_LAYOUT_ROWS ? table[shape][mc] : table_tiles[shape][mc];
   for (int i = 0; i < cell.n; ++i)

@@ -184,7 +184,7 @@ def test_config_table_is_a_pure_function_of_shape(lib):
     import fp8_block_scaled_fp8bs_amd as fp8bs
     shapes = [(m, n, k) for m in (1, 2, 3, 8, 16, 17, 32)
               for (n, k) in ((512, 1024), (5120, 5120), (34816, 5120), (5120, 17408),
-                             (248320, 5120), (128, 128))]
+                             (248320, 5120), (31104, 5120), (128, 128))]
     for s in shapes:
         a, b = fp8bs.select_config(*s), fp8bs.select_config(*s)
         assert a == b
@@ -286,7 +286,8 @@ def test_tile_layout_config_rules(lib):
     workspace query covers both layouts."""
     import fp8_block_scaled_fp8bs_amd as fp8bs
     from fp8_block_scaled_fp8bs_amd import GemmConfig
-    for (n, k) in ((512, 1024), (5120, 5120), (34816, 5120), (5120, 17408), (248320, 5120)):
+    for (n, k) in ((512, 1024), (5120, 5120), (34816, 5120), (5120, 17408), (248320, 5120),
+                   (31104, 5120)):
         for m in range(1, 33):
             t = fp8bs.tiles_select_config(m, n, k)
             r = fp8bs.select_config(m, n, k)
@@ -398,3 +399,24 @@ def test_prefill_narrow_tiles_table_and_limits(lib):
         c = fp8bs._Config(5, 5, 2, 4, 2, split, 0, 0, 0)
         assert lib.fp8bs_gemm_ex(None, P, P, 2048, P, P, n, 5120, P, None, 0, ctypes.byref(c),
                                  None) == E_CFG
+
+
+def test_one_round_wide_n_class(lib):
+    """Shapes whose 128-row weight blocks number 200 to 256 (one GPU's 8-way
+    column share of the vocabulary layer, 31104 x 5120) take the grid kernel
+    with 8 waves along N, one workgroup per block row, where it fits (K split
+    in two at m = 32 on tile-layout weights); wider shapes (MLP up, 272 block
+    rows) keep the wide-N choices."""
+    import fp8_block_scaled_fp8bs_amd as fp8bs
+    for m in (5, 8, 16, 24):
+        for t in (fp8bs.tiles_select_config(m, 31104, 5120), fp8bs.select_config(m, 31104, 5120)):
+            assert (t.path, t.tiles_n, t.waves_n, t.waves_k, t.depth, t.split_k) == \
+                (fp8bs.PATH_MFMA, 1, 8, 1, 5, 1), (m, t)
+    t = fp8bs.tiles_select_config(32, 31104, 5120)
+    assert (t.path, t.waves_n, t.waves_k, t.split_k) == (fp8bs.PATH_MFMA, 8, 1, 2), t
+    t = fp8bs.tiles_select_config(4, 31104, 5120)
+    assert (t.path, t.waves_n, t.waves_k, t.split_k) == (fp8bs.PATH_MFMA, 2, 4, 1), t
+    assert fp8bs.select_config(32, 31104, 5120).path != fp8bs.PATH_MFMA
+    for m in (8, 16):
+        assert fp8bs.tiles_select_config(m, 34816, 5120).path == 3
+        assert fp8bs.tiles_select_config(m, 32896, 5120).path == 3  # 257 block rows
