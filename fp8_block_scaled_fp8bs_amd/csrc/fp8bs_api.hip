@@ -401,8 +401,9 @@ bool candidate_fits(const Candidate& cd, int64_t m, int64_t n, int kbn, fp8bs_ge
 
 // The fixed configuration table. A pure function of (m, n, k): no timing,
 // no device state, so a shape always runs the same kernel and gives the
-// same bits. Shapes fall in four classes by their extents (square-like,
-// deep K, wide N, vocabulary-wide N) and six classes of m; each cell lists
+// same bits. Shapes fall in five classes by their extents (square-like,
+// deep K, wide N in one round of 128-row workgroups, wide N, vocabulary-wide
+// N) and six classes of m; each cell lists
 // candidates in order of preference, measured on MI355X with graph-replayed
 // launches over a rotating 1 GiB weight pool. The first candidate that fits
 // the shape (rows dividing n, split not above the number of K blocks,
@@ -557,7 +558,7 @@ bool select_config(int64_t m, int64_t n, int64_t k, fp8bs_gemm_config* out, bool
        {{{MF, 1, 8, 1, 5, 6, RK}, {MF, 1, 5, 2, 5, 4, RK}}, 2},
        {{{MF, 1, 8, 1, 5, 6, RK}, {MF, 1, 5, 2, 5, 4, RK}}, 2},
        {{{MF, 1, 8, 1, 5, 6, RK}, {MF, 2, 5, 1, 5, 8, RK}}, 2}},
-      // wide N: 25600 <= n < 65536
+      // wide N: 256 < n/128 < 512 (32768 < n < 65536)
       {{{{MF, 1, 1, 4, 5, 1, RK}, {MF, 1, 1, 8, 5, 1, RK}}, 2},
        {{{RW, 4, 1, 8, 4, 1, RK}, {RW, 1, 1, 8, 3, 1, RK}}, 2},
        {{{RW, 1, 1, 8, 3, 1, RK}, {RW, 2, 1, 8, 6, 1, RK}}, 2},
@@ -601,7 +602,7 @@ bool select_config(int64_t m, int64_t n, int64_t k, fp8bs_gemm_config* out, bool
        {{{MF, 1, 8, 1, 5, 5, RK}, {MF, 1, 8, 1, 5, 4, RK}}, 2},
        {{{MF, 1, 8, 1, 5, 6, RK}, {MF, 1, 8, 1, 5, 4, RK}}, 2},
        {{{MF, 1, 8, 1, 5, 6, RK}, {MF, 2, 5, 1, 5, 8, RK}}, 2}},
-      // wide N
+      // wide N (256 < n/128 < 512)
       {{{{MF, 1, 1, 4, 5, 1, RK}, {MF, 1, 1, 8, 5, 1, RK}}, 2},
        {{{MF, 1, 1, 8, 5, 1, RK}, {MF, 1, 1, 4, 5, 1, RK}}, 2},
        {{{RW, 1, 1, 8, 3, 1, RK}, {MF, 1, 1, 8, 5, 1, RK}}, 2},
