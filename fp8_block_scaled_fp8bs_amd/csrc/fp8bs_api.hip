@@ -595,9 +595,11 @@ bool select_config(int64_t m, int64_t n, int64_t k, fp8bs_gemm_config* out, bool
        {{{MF, 1, 2, 4, 5, 1, RK}, {MF, 1, 5, 1, 5, 4, RK}}, 2},
        {{{MF, 1, 8, 1, 5, 4, RK}, {MF, 1, 5, 1, 5, 4, RK}}, 2},
        {{{MF, 1, 8, 1, 5, 4, RK}, {MF, 1, 5, 2, 5, 4, RK}}, 2}},
-      // deep K
-      {{{{MF, 1, 5, 2, 2, 4, RK}, {MF, 1, 5, 1, 5, 4, RK}}, 2},
-       {{{MF, 1, 5, 1, 5, 4, RK}, {MF, 1, 5, 2, 2, 4, RK}}, 2},
+      // deep K (m = 1-2: no K split, so no second kernel; MLP down
+      // 17408 -> 5120 at m = 1 / 2: 16.2 / 16.8 us against 17.5 / 17.8 us
+      // with K split in four)
+      {{{{MF, 1, 2, 4, 5, 1, RK}, {MF, 1, 5, 2, 2, 4, RK}, {MF, 1, 5, 1, 5, 4, RK}}, 3},
+       {{{MF, 1, 2, 4, 5, 1, RK}, {MF, 1, 5, 1, 5, 4, RK}, {MF, 1, 5, 2, 2, 4, RK}}, 3},
        {{{MF, 1, 5, 1, 5, 4, RK}, {MF, 1, 5, 2, 2, 4, RK}}, 2},
        {{{MF, 1, 8, 1, 5, 5, RK}, {MF, 1, 8, 1, 5, 4, RK}}, 2},
        {{{MF, 1, 8, 1, 5, 6, RK}, {MF, 1, 8, 1, 5, 4, RK}}, 2},

@@ -420,3 +420,14 @@ def test_one_round_wide_n_class(lib):
     for m in (8, 16):
         assert fp8bs.tiles_select_config(m, 34816, 5120).path == 3
         assert fp8bs.tiles_select_config(m, 32896, 5120).path == 3  # 257 block rows
+
+
+def test_deep_k_small_m_tiles_unsplit(lib):
+    """On tile-layout weights the MLP-down shape (17408 -> 5120) at m = 1-2
+    takes the grid kernel without a K split (no reduce kernel); from m = 3 K
+    stays split."""
+    import fp8_block_scaled_fp8bs_amd as fp8bs
+    for m in (1, 2):
+        t = fp8bs.tiles_select_config(m, 5120, 17408)
+        assert (t.path, t.waves_n, t.waves_k, t.split_k) == (fp8bs.PATH_MFMA, 2, 4, 1), (m, t)
+    assert fp8bs.tiles_select_config(3, 5120, 17408).split_k > 1
