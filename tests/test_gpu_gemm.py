@@ -162,7 +162,7 @@ DOWN_SHARD_KB = 17
 
 
 @pytest.mark.parametrize("rank", [0, 7])
-@pytest.mark.parametrize("m", [1, 8, 16])
+@pytest.mark.parametrize("m", [1, 8, 16, 24, 32])
 def test_vocab_column_shard(fp8bs, vocab_weight, rank, m):
     """A rank's column share of the vocabulary weight is a contiguous slice of
     its block rows with their own scales; the GEMM on it (row-major and tile
