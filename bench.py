@@ -801,7 +801,7 @@ def main() -> int:
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(this build has no multi-GPU path).", file=sys.stderr)
+              "(the library runs on one GPU; --shards times one GPU's share of each shape).", file=sys.stderr)
         return 2
 
     import numpy as np
