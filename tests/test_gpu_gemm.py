@@ -216,6 +216,30 @@ def test_mlp_down_k_shard(fp8bs, full_problems, rank, m):
     _assert_close(yt, ref, f"mlp_down shard {rank} m={m} tiles")
 
 
+@pytest.mark.parametrize("name", ["mlp_up", "square"])
+@pytest.mark.parametrize("rank", [0, 7])
+@pytest.mark.parametrize("m", [1, 8, 16])
+def test_column_shard_full_output(fp8bs, full_problems, name, rank, m):
+    """A rank's column share of MLP up (34 of 272 block rows) or of the
+    square projection (5 of 40) under an 8-way split: a contiguous slice of
+    the weight's block rows with their scales, in each layout's table
+    configuration for the share's shape; full output against the oracle on
+    the same rows."""
+    pr = full_problems[name]
+    nb = pr.w_bits.shape[0] // 128 // 8
+    b0, b1 = nb * rank, nb * (rank + 1)
+    wq, ws = pr.wq[b0 * 128:b1 * 128], pr.ws[b0:b1]
+    k = pr.w_bits.shape[1]
+    announce("column shard", name, rank, "n", (b1 - b0) * 128, "m", m)
+    x = pr.x[:m].contiguous()
+    y = host_bits(fp8bs.gemm(x, wq, ws))
+    yt = host_bits(fp8bs.gemm_tiles(x, fp8bs.pack_weight(wq), ws))
+    ref = oracle.gemm_ref(pr.xq_ref[:m], pr.xs_ref[:m], pr.wq_ref[b0 * 128:b1 * 128],
+                          pr.ws_ref[b0:b1])
+    _assert_close(y, ref, f"{name} shard {rank} m={m} k={k}")
+    _assert_close(yt, ref, f"{name} shard {rank} m={m} tiles")
+
+
 @pytest.mark.parametrize("m", [8, 16])
 def test_vocab_run_to_run_bit_identical(fp8bs, vocab_weight, m):
     """The 248,320-wide layer in the configuration each layout's table picks:
